@@ -1,0 +1,133 @@
+"""Pins of the oracle's weight packer and dual-path GEMM: hand dot products,
+a permutation weight, the error bound of the review's §3.6, and the expected
+ordering SharQ < plain FP4 (review §5.3 and Table 5; qualitative only)."""
+import numpy as np
+import pytest
+
+from oracle import formats as F
+from oracle import sharq as O
+from conftest import read_golden
+from sparsity_sharq_prepare_amd import synth
+
+F32 = np.float32
+
+
+def worked_example_act():
+    x = np.full((1, 32), F32(0.2), dtype=F32)
+    x[0, 5] = 12.0
+    return O.prepare(x, None, fmt="mxfp4")
+
+
+def test_pack_weight_hand_column():
+    # column of 32 ones: amax 1 -> e = -2 (6 * 2^-2 = 1.5 >= 1 > 0.75), 1 / 0.25 = 4 -> code 6
+    w = np.ones((32, 1), F32)
+    wp = O.pack_weight(w, "mxfp4")
+    assert wp["scale_sp"].tolist() == [[125]]
+    assert wp["payload"].tolist() == [[0x66] * 16]
+    # alternating signs -> codes 6 / 0xE alternate, even k in the low nibble
+    w2 = np.array([[(-1.0) ** k] for k in range(32)], F32)
+    assert O.pack_weight(w2, "mxfp4")["payload"].tolist() == [[0xE6] * 16]
+    # the payload row d holds column d of W (K x D input)
+    w3 = np.zeros((32, 3), F32)
+    w3[4, 2] = 6.0
+    wp3 = O.pack_weight(w3, "mxfp4")
+    assert wp3["payload"][2, 2] == 0x07 and np.all(wp3["payload"][:2] == 0)
+
+
+def test_nvfp4_weight_views():
+    rng = np.random.default_rng(0)
+    w = (rng.standard_normal((64, 4)) * 0.02).astype(F32)
+    wp = O.pack_weight(w, "nvfp4")
+    assert wp["scale_sp"].shape == (4, 2) and wp["scale_dn"].shape == (4, 4)
+    assert np.array_equal(wp["scale_dn"][:, 0::2], wp["scale_sp"])
+    assert np.array_equal(wp["scale_dn"][:, 1::2], wp["scale_sp"])
+    assert np.array_equal(O.weight_dequant(wp, "sp"), O.weight_dequant(wp, "dn"))
+    assert wp["tensor_scale"][0] == F32(np.abs(w).max() / F32(2688))
+
+
+def test_hand_dot_products():
+    g = {r[0]: r[1:] for r in read_golden("worked_example_block.txt")}
+    act = worked_example_act()
+    ones = O.pack_weight(np.ones((32, 1), F32), "mxfp4")
+    Y, _ = O.sharq_linear(act, ones)
+    assert Y[0, 0] == float(g["y_ones"][0])
+    alt = O.pack_weight(np.array([[(-1.0) ** k] for k in range(32)], F32), "mxfp4")
+    Y2, _ = O.sharq_linear(act, alt)
+    assert Y2[0, 0] == float(g["y_alt"][0])
+
+
+def test_permutation_weight():
+    # W = permutation matrix -> W~ = W exactly and Y^[:, pi(k)] = x~_sp[:, k] + r~[:, k]
+    case = synth.random_case(8, 6, 256, 256)
+    act = O.prepare(case.x_f32(), case.gamma, 1e-6)
+    pi = np.random.default_rng(9).permutation(256)
+    W = np.zeros((256, 256), F32)
+    W[np.arange(256), pi] = 1.0
+    wp = O.pack_weight(W, "mxfp4")
+    Y, _ = O.sharq_linear(act, wp)
+    Xt, Rt = O.act_dequant(act)
+    assert np.array_equal(Y[:, pi], Xt + Rt)
+    # and x~_sp + r~ approximates y (quantization error only)
+    y = act["y"].astype(np.float64)
+    assert np.abs(Y[:, pi] - y).max() <= 0.25 * np.abs(y).max()
+
+
+def test_non_square_shapes_and_rows():
+    # a transposed operand would not even broadcast here; check against a
+    # direct per-element dot product
+    case = synth.random_case(12, 5, 128, 40)
+    act = O.prepare(case.x_f32(), case.gamma, 1e-6)
+    wp = O.pack_weight(case.w_f32(), "mxfp4")
+    Y, S = O.sharq_linear(act, wp)
+    assert Y.shape == (5, 40)
+    Xt, Rt = O.act_dequant(act)
+    Wt = O.weight_dequant(wp)
+    for t, d in [(0, 0), (4, 39), (2, 17)]:
+        ref = sum(Xt[t, k] * Wt[k, d] for k in range(128)) + sum(Rt[t, k] * Wt[k, d] for k in range(128))
+        assert abs(Y[t, d] - ref) <= 1e-12 * S[t, d]
+    Ys, Ss = O.sharq_linear_sampled(act, wp, [0, 4, 2], [0, 39, 17])
+    assert np.allclose(Ys, Y[[0, 4, 2], [0, 39, 17]], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_error_bound_review_3_6(fmt):
+    case = synth.random_case(21, 16, 256, 64, fmt=fmt)
+    act = O.prepare(case.x_f32(), case.gamma, 1e-6, fmt=fmt)
+    wp = O.pack_weight(case.w_f32(), fmt)
+    lhs, rhs = O.error_bound_terms(act, act, wp)
+    assert lhs <= rhs * (1 + 1e-9)
+    # error merge: y - (X~_sp + R~) = R - R~, with X~_sp the fp32 backbone the
+    # residual was formed against (NVFP4 dequantizes to fp32 before the subtraction)
+    _, Rt = O.act_dequant(act)
+    y, Xs, R = (act[k].astype(np.float64) for k in ("y", "Xt_sp", "R"))
+    assert np.allclose(y - (Xs + Rt), R - Rt, rtol=0, atol=1e-12)
+
+
+def test_grouped_linear_matches_per_expert():
+    rng = np.random.default_rng(4)
+    go, ri = synth.draw_routing(rng, 32, 4, 2)
+    case = synth.random_case(5, 32, 128, 24)
+    act = O.prepare(case.x_f32(), case.gamma, 1e-6)
+    ws = [O.pack_weight((rng.standard_normal((128, 24)) * 0.02).astype(F32)) for _ in range(4)]
+    Y, _ = O.grouped_linear(act, ws, go, ri)
+    for e in range(4):
+        a, b = go[e], go[e + 1]
+        sub = O.act_rows(act, ri[a:b])
+        Ye, _ = O.sharq_linear(sub, ws[e])
+        assert np.array_equal(Y[a:b], Ye)
+    assert sorted(ri.tolist()) == sorted(list(range(32)) * 2)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_sharq_beats_plain_fp4_on_outliers(fmt):
+    # review §3.6 / §5.3: isolating outliers in the backbone leaves a residual
+    # whose block scales are not outlier-dominated -> lower output error than
+    # plain FP4 of the same activations (ordering only; values are unpinned)
+    case = synth.random_case(30, 32, 1024, 64, fmt=fmt)
+    act = O.prepare(case.x_f32(), case.gamma, 1e-6, fmt=fmt)
+    wp = O.pack_weight(case.w_f32(), fmt)
+    W = O.weight_dequant(wp)
+    ref = act["y"].astype(np.float64) @ W
+    Y, _ = O.sharq_linear(act, wp)
+    plain = O.plain_quantized(act["y"], fmt) @ W
+    assert O.rel_frobenius(Y, ref) < 0.5 * O.rel_frobenius(plain, ref)
