@@ -304,10 +304,11 @@ def prepare(x: np.ndarray, gamma, eps: float = 1e-6, fmt: str = "mxfp4") -> dict
 # ----------------------------------------------------------------------------
 # weight packer: one payload, two scale views (review §3.5)
 # ----------------------------------------------------------------------------
-def pack_weight(w: np.ndarray, fmt: str = "mxfp4") -> dict:
+def pack_weight(w: np.ndarray, fmt: str = "mxfp4", tensor_amax=None) -> dict:
     """Quantize W (K x D, fp32 values) column by column, 32 K-values per block,
     into one shared payload (D x K/2) and the sparse (per 32) and dense (per 16,
-    each per-32 scale repeated twice) scale views."""
+    each per-32 scale repeated twice) scale views.  NVFP4: ``tensor_amax``
+    overrides amax|W| when only some columns of a larger weight are packed."""
     w = np.asarray(w, dtype=F32)
     Wt = np.ascontiguousarray(w.T)                      # D x K
     if fmt == "mxfp4":
@@ -316,7 +317,9 @@ def pack_weight(w: np.ndarray, fmt: str = "mxfp4") -> dict:
         return {"fmt": fmt, "payload": pack_nibbles(codes), "scale_sp": sp, "scale_dn": sp.copy(),
                 "tensor_scale": None, "codes": codes}
     if fmt == "nvfp4":
-        s_w = nv_tensor_scale(np.abs(w).max() if w.size else 0.0)
+        if tensor_amax is None:
+            tensor_amax = np.abs(w).max() if w.size else 0.0
+        s_w = nv_tensor_scale(tensor_amax)
         codes, sc = nv_quantize(Wt, NV_W_BLOCK, s_w)
         return {"fmt": fmt, "payload": pack_nibbles(codes), "scale_sp": sc,
                 "scale_dn": np.repeat(sc, 2, axis=-1), "tensor_scale": np.array([s_w], dtype=F32),

@@ -1,0 +1,137 @@
+// Device-side helpers shared by the SharQ kernels (gfx950 / CDNA4).
+//
+// Number formats follow the SharQ pages (xllm-io paper review §3.1 block
+// scales, §5.3 MXFP4 power-of-two scale; kasblo explainer: NVFP4 = 16 E2M1
+// values + one E4M3 scale), with these exact rules:
+//  - E2M1 rounding is to nearest, ties to the even code, saturating at 6, the
+//    sign copied from the input.  gfx950's v_cvt_scalef32_pk_fp4_f32 computes
+//    exactly this for x / 2^e (checked exhaustively against an integer
+//    reference over all fp32 inputs |x| <= 6 * 2^e on MI355X).
+//  - MXFP4 scale exponent: the smallest e with amax <= 6 * 2^e, in [-127, 127].
+//  - E4M3: OCP FP8 (bias 7, max 448), nearest, ties to even, saturating.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define SHARQ_DEV __device__ __forceinline__
+
+namespace sharq {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- E8M0 (MXFP4)
+// amax = 1.m * 2^(E-127) (biased E): amax <= 6 * 2^e  <=>  e >= E-129 (m <= 0.5)
+// or e >= E-128 (m > 0.5).  Zero and subnormal amax give e <= -128 -> -127.
+SHARQ_DEV int e8m0_exponent(float amax) {
+  uint32_t b = __float_as_uint(amax);
+  int e = (int)(b >> 23) - 129 + ((b & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+  return e < -127 ? -127 : e;
+}
+
+// 2^e as fp32 (e in [-127, 127]; 2^-127 is a subnormal, handled by v_ldexp).
+SHARQ_DEV float exp2i(int e) { return __builtin_amdgcn_ldexpf(1.0f, e); }
+
+// Two E2M1 codes of a / 2^e and b / 2^e (|.| <= 6 * 2^e) into byte `sel` of `old`:
+// a -> low nibble, b -> high nibble.
+template <int SEL>
+SHARQ_DEV uint32_t cvt_fp4x2(uint32_t old, float a, float b, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, SEL);
+}
+
+// Values of the two E2M1 codes in byte `SEL` of `word`, times scale (exact).
+template <int SEL>
+SHARQ_DEV v2f dq_fp4x2(uint32_t word, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, scale, SEL);
+}
+
+// ---------------------------------------------------------------- E4M3 (OCP)
+// Code of non-negative u: nearest finite value, ties to even, saturating at 448.
+SHARQ_DEV uint32_t e4m3_encode(float u) {
+  if (!(u < 448.0f)) return 0x7Eu;
+  if (u < 0.015625f) {                       // below 2^-6: subnormal grid m * 2^-9
+    float m = __builtin_rintf(u * 512.0f);   // exact scaling, ties to even
+    return (uint32_t)m;                      // 0..8 (8 == 0x08 == 2^-6)
+  }
+  uint32_t b = __float_as_uint(u);
+  b = b + 0x7FFFFu + ((b >> 20) & 1u);       // round mantissa to 3 bits, ties to even
+  uint32_t code = (b >> 20) - (120u << 3);   // rebias 127 -> 7
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+SHARQ_DEV float e4m3_decode(uint32_t code) {
+  uint32_t E = (code >> 3) & 15u, M = code & 7u;
+  if (E == 0) return __builtin_amdgcn_ldexpf((float)M, -9);
+  return __builtin_amdgcn_ldexpf((float)(8u + M), (int)E - 10);
+}
+
+// ---------------------------------------------------------------- E2M1 value
+SHARQ_DEV float e2m1_value(uint32_t code) {
+  // twice the magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 as nibbles of one word
+  const float v = 0.5f * (float)((0xC8643210u >> (4u * (code & 7u))) & 15u);
+  return (code & 8u) ? -v : v;
+}
+
+// ---------------------------------------------------------------- sqrt
+// Correctly rounded fp32 square root of v >= 0.  v_sqrt_f32 (what __fsqrt_rn
+// lowers to on gfx950) can be one ulp off; here the double-precision root is
+// rounded to fp32 and then checked against the exact squares of the two
+// neighbouring midpoints (a midpoint of adjacent floats has at most 26
+// significant bits, so its square is exact in fp64).
+SHARQ_DEV float sqrt_rn(float v) {
+  if (!(v > 0.0f) || v == __builtin_inff()) return __builtin_sqrtf(v);
+  const float s = (float)__builtin_sqrt((double)v);
+  const uint32_t b = __float_as_uint(s);
+  const float up = __uint_as_float(b + 1u), dn = __uint_as_float(b - 1u);
+  const double hi = 0.5 * ((double)s + (double)up), lo = 0.5 * ((double)s + (double)dn);
+  const double dv = (double)v;
+  if (hi * hi < dv) return up;
+  if (lo * lo > dv) return dn;
+  return s;
+}
+
+// ---------------------------------------------------------------- cross-lane
+SHARQ_DEV float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
+SHARQ_DEV uint32_t shfl_xor_u(uint32_t v, int m) { return (uint32_t)__shfl_xor((int)v, m, kWave); }
+
+// 4:8 in-pairs top-2 of four pair scores, ties to the lower pair: returns the
+// kept-pair bit mask (exactly two bits).  Pair p beats pair q (p < q) when
+// s_p >= s_q; a pair is kept when fewer than two pairs beat it.
+SHARQ_DEV uint32_t top2_pairs(float s0, float s1, float s2, float s3) {
+  const uint32_t c01 = s0 >= s1, c02 = s0 >= s2, c03 = s0 >= s3;
+  const uint32_t c12 = s1 >= s2, c13 = s1 >= s3, c23 = s2 >= s3;
+  const uint32_t r0 = 3u - c01 - c02 - c03;           // pairs beating pair 0
+  const uint32_t r1 = c01 + 2u - c12 - c13;
+  const uint32_t r2 = c02 + c12 + 1u - c23;
+  const uint32_t r3 = c03 + c13 + c23;
+  return (r0 < 2u) | ((r1 < 2u) << 1) | ((r2 < 2u) << 2) | ((r3 < 2u) << 3);
+}
+
+// kept mask (bits) -> metadata nibble i0 | i1 << 2 (i0 < i1)
+SHARQ_DEV uint32_t mask_to_nibble(uint32_t km) {
+  // km: 3->(0,1)=4, 5->(0,2)=8, 6->(1,2)=9, 9->(0,3)=12, 10->(1,3)=13, 12->(2,3)=14
+  const uint64_t lut = (4ull << 12) | (8ull << 20) | (9ull << 24) | (12ull << 36) | (13ull << 40) |
+                       (14ull << 48);
+  return (uint32_t)(lut >> (4u * km)) & 15u;
+}
+
+// Expand the two kept pair-bytes of one group (byte0, byte1 of `two`) into the
+// four pair slots given by the metadata nibble (zeros in dropped pairs).
+SHARQ_DEV uint32_t expand_group(uint32_t two, uint32_t nib) {
+  const uint32_t i0 = nib & 3u, i1 = nib >> 2;
+  return ((two & 0xFFu) << (8u * i0)) | (((two >> 8) & 0xFFu) << (8u * i1));
+}
+
+// activation row of output row r: row_index[r] clamped into [0, act_rows), or r
+SHARQ_DEV int64_t gather_row(const int32_t* row_index, int r, int act_rows) {
+  if (!row_index) return r;
+  const int v = row_index[r];
+  return v < 0 ? 0 : (v >= act_rows ? act_rows - 1 : v);
+}
+
+}  // namespace sharq

@@ -1,0 +1,43 @@
+// Host-side launchers of the SharQ kernels (internal to libsharq).  Each
+// launcher enqueues its kernels on `s` and returns the launch status; argument
+// validation happens before, in api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sharq {
+
+// Row gathers read row_index[r] from device memory; kernels clamp each index
+// into [0, act_rows) and grouped kernels clamp group offsets into [0, rows],
+// so malformed device tables cannot make a kernel access memory out of bounds.
+
+// largest K the register-resident prepare kernels handle
+int prepare_max_k();
+size_t prepare_nv_workspace(int T, int K);
+size_t pack_nv_workspace(int K, int D, int n_groups);
+
+hipError_t launch_prepare_mx(const void* X, bool bf16, int T, int K, int64_t ldx, const float* gamma, float eps,
+                             uint8_t* bb_codes, uint8_t* bb_meta, uint8_t* bb_scale, uint8_t* res_codes,
+                             uint8_t* res_scale, hipStream_t s);
+
+hipError_t launch_prepare_nv(const void* X, bool bf16, int T, int K, int64_t ldx, const float* gamma, float eps,
+                             uint8_t* bb_codes, uint8_t* bb_meta, uint8_t* bb_scale, uint8_t* res_codes,
+                             uint8_t* res_scale, float* tensor_scales, void* workspace, hipStream_t s);
+
+hipError_t launch_pack(const void* W, bool bf16, bool nv, int K, int D, int n_groups, int64_t ldw, int64_t gstride,
+                       uint8_t* payload, uint8_t* scale_sp, uint8_t* scale_dn, float* tscale, void* workspace,
+                       hipStream_t s);
+
+hipError_t launch_linear_mx(const uint8_t* bb_codes, const uint8_t* bb_meta, const uint8_t* bb_scale,
+                            const uint8_t* res_codes, const uint8_t* res_scale, const int32_t* row_index, int rows,
+                            int act_rows, int K, const uint8_t* payload, const uint8_t* wscale, int D, int n_groups,
+                            const int32_t* group_offsets, float* Y, int64_t ldy, hipStream_t s);
+
+hipError_t launch_linear_nv(const uint8_t* bb_codes, const uint8_t* bb_meta, const uint8_t* bb_scale,
+                            const uint8_t* res_codes, const uint8_t* res_scale, const float* a_ts,
+                            const int32_t* row_index, int rows, int act_rows, int K, const uint8_t* payload,
+                            const uint8_t* wscale, const float* w_ts, int D, float* Y, int64_t ldy, hipStream_t s);
+
+}  // namespace sharq

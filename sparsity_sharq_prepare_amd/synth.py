@@ -172,10 +172,15 @@ def _llama_like(name, fmt, T, K, D, spec, seed) -> LinearCase:
 DECODE_SHAPES = ((4096, 4096), (4096, 14336), (14336, 4096))
 
 
+def decode_case(i: int, seed: int = 0, T: int = 8) -> LinearCase:
+    """Llama-3.1-8B decode linear number i of DECODE_SHAPES (T=8), MXFP4, bf16."""
+    K, D = DECODE_SHAPES[i]
+    return _llama_like(f"decode_{K}x{D}", "mxfp4", T, K, D, LLAMA_OUTLIERS, seed)
+
+
 def decode_cases(seed: int = 0, T: int = 8):
-    """Llama-3.1-8B decode linears (T=8), MXFP4, bf16 storage."""
-    return [_llama_like(f"decode_{K}x{D}", "mxfp4", T, K, D, LLAMA_OUTLIERS, seed)
-            for K, D in DECODE_SHAPES]
+    """All three Llama-3.1-8B decode linears (T=8), MXFP4, bf16 storage."""
+    return [decode_case(i, seed, T) for i in range(len(DECODE_SHAPES))]
 
 
 def prefill_case(seed: int = 0, T: int = 4096, K: int = 4096, D: int = 14336) -> LinearCase:

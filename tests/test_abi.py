@@ -1,0 +1,132 @@
+"""The C-ABI library loads, exports every symbol include/sharq.h declares, and
+rejects bad arguments on the host before touching the GPU (no compute calls:
+every call here fails validation, so nothing is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparsity_sharq_prepare_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH), reason="libsharq.so not built")
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "sharq.h")).read()
+    return sorted(set(re.findall(r"^(?:sharq_status|const char \*)\s*(sharq_\w+)\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = header_functions()
+    assert set(names) == set(L.EXPORTS)
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert L.status_name(0) == "SHARQ_OK"
+    assert L.status_name(3) == "SHARQ_ERR_FORMAT_MISMATCH"
+
+
+def test_sizes():
+    # MXFP4 prep output = K/4 + K/16 + K/32 + K/2 + K/32 = 0.875 B per input element
+    sz = L.act_sizes(L.SHARQ_MXFP4, 8, 4096)
+    assert sz[:5] == [8 * 1024, 8 * 256, 8 * 128, 8 * 2048, 8 * 128] and sum(sz[:5]) == 0.875 * 8 * 4096
+    assert sz[5] == 0 and sz[6] == 0
+    nv = L.act_sizes(L.SHARQ_NVFP4_EMU, 8, 4096)
+    assert nv[4] == 8 * 256 and nv[5] == 8 and nv[6] > 8 * 4
+    w = L.weight_sizes(L.SHARQ_MXFP4, 4096, 14336, 1)
+    assert w[0] == 14336 * 2048 and w[1] == w[2] == 14336 * 128 and w[3] == 0
+    wn = L.weight_sizes(L.SHARQ_NVFP4_EMU, 3584, 18944, 2)
+    assert wn[2] == 2 * 18944 * 224 and wn[3] == 8
+
+
+@pytest.mark.parametrize("K", [0, 31, 48, -32])
+def test_sizes_reject_bad_k(K):
+    with pytest.raises(L.SharqError) as e:
+        L.act_sizes(L.SHARQ_MXFP4, 8, K)
+    assert e.value.status == L.SHARQ_ERR_UNSUPPORTED_SHAPE
+
+
+def _fake_act(fmt=0, T=8, K=256, base=0x10000):
+    return L.SharqAct(fmt, T, K, base, base + 0x1000, base + 0x2000, base + 0x3000, base + 0x4000,
+                      base + 0x5000 if fmt else None)
+
+
+def _fake_weight(fmt=0, K=256, D=64, G=1, base=0x20000):
+    return L.SharqWeight(fmt, K, D, G, base, base + 0x1000, base + 0x1000 if fmt == 0 else base + 0x2000,
+                         base + 0x3000 if fmt else None)
+
+
+def test_linear_validation_errors():
+    lib = L.lib()
+    Y = 0x30000
+    a, w = _fake_act(), _fake_weight()
+    # format mismatch
+    assert lib.sharq_linear(_fake_act(fmt=1), w, None, None, 8, Y, 64, None) == L.SHARQ_ERR_FORMAT_MISMATCH
+    # K mismatch
+    assert lib.sharq_linear(a, _fake_weight(K=512), None, None, 8, Y, 64, None) == L.SHARQ_ERR_FORMAT_MISMATCH
+    # K not a multiple of 128 for the GEMM
+    assert lib.sharq_linear(_fake_act(K=96), _fake_weight(K=96), None, None, 8, Y, 64, None) == \
+        L.SHARQ_ERR_UNSUPPORTED_SHAPE
+    # ldy < D, NULL Y, misaligned Y
+    assert lib.sharq_linear(a, w, None, None, 8, Y, 32, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert lib.sharq_linear(a, w, None, None, 8, None, 64, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert lib.sharq_linear(a, w, None, None, 8, Y + 4, 64, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    # more rows than T without a gather
+    assert lib.sharq_linear(a, w, None, None, 9, Y, 64, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    # grouped needs offsets; NVFP4 grouped is unsupported
+    assert lib.sharq_linear(a, _fake_weight(G=4), None, None, 8, Y, 64, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert lib.sharq_linear(_fake_act(fmt=1), _fake_weight(fmt=1, G=4), 0x40000, None, 8, Y, 64, None) == \
+        L.SHARQ_ERR_UNSUPPORTED_SHAPE
+    # null activation buffer
+    bad = _fake_act()
+    bad.res_codes = None
+    assert lib.sharq_linear(bad, w, None, None, 8, Y, 64, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert "NULL" in lib.sharq_last_error().decode()
+
+
+def test_prepare_validation_errors():
+    lib = L.lib()
+    X = 0x50000
+    out = _fake_act()
+    assert lib.sharq_prepare(None, 1, 8, 256, 256, None, 1e-6, out, None, 0, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert lib.sharq_prepare(X, 7, 8, 256, 256, None, 1e-6, out, None, 0, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert lib.sharq_prepare(X, 1, 8, 250, 256, None, 1e-6, _fake_act(K=250), None, 0, None) == \
+        L.SHARQ_ERR_UNSUPPORTED_SHAPE
+    # struct / call disagree
+    assert lib.sharq_prepare(X, 1, 9, 256, 256, None, 1e-6, out, None, 0, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    # ldx < K, unaligned rows, unaligned gamma, negative eps
+    assert lib.sharq_prepare(X, 1, 8, 256, 128, None, 1e-6, out, None, 0, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert lib.sharq_prepare(X, 1, 8, 256, 260, None, 1e-6, out, None, 0, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert lib.sharq_prepare(X, 1, 8, 256, 256, 0x60004, 1e-6, out, None, 0, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert lib.sharq_prepare(X, 1, 8, 256, 256, None, -1.0, out, None, 0, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    # K beyond the register-resident maximum
+    big = _fake_act(K=65536)
+    assert lib.sharq_prepare(X, 1, 8, 65536, 65536, None, 1e-6, big, None, 0, None) == L.SHARQ_ERR_UNSUPPORTED_SHAPE
+    # NVFP4 needs a workspace
+    nv = _fake_act(fmt=1)
+    assert lib.sharq_prepare(X, 1, 8, 256, 256, None, 1e-6, nv, None, 0, None) == L.SHARQ_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_pack_validation_errors():
+    lib = L.lib()
+    W = 0x70000
+    w = _fake_weight()
+    assert lib.sharq_pack_weight(None, 1, 256, 64, 1, 64, 0, w, None, 0, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert lib.sharq_pack_weight(W, 1, 256, 64, 1, 32, 0, w, None, 0, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert lib.sharq_pack_weight(W, 1, 512, 64, 1, 64, 0, w, None, 0, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert lib.sharq_pack_weight(W, 1, 100, 64, 1, 64, 0, _fake_weight(K=100), None, 0, None) == \
+        L.SHARQ_ERR_UNSUPPORTED_SHAPE
+    g = _fake_weight(G=2)
+    assert lib.sharq_pack_weight(W, 1, 256, 64, 2, 64, 100, g, None, 0, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    nv = _fake_weight(fmt=1)
+    assert lib.sharq_pack_weight(W, 1, 256, 64, 1, 64, 0, nv, None, 0, None) == L.SHARQ_ERR_WORKSPACE_TOO_SMALL
+    nv_alias = _fake_weight(fmt=1)
+    nv_alias.scale_dn = nv_alias.scale_sp
+    assert lib.sharq_pack_weight(W, 1, 256, 64, 1, 64, 0, nv_alias, 0x80000, 1 << 20, None) == \
+        L.SHARQ_ERR_INVALID_ARGUMENT

@@ -1,0 +1,261 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle on
+the same seeded inputs.  Codes, scales, metadata and tensor scales must be
+bit-exact; fp32 GEMM outputs must lie within 1e-5 * sum_k |x~_k w~_k| of the
+fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import sharq as O
+from sparsity_sharq_prepare_amd import ops, synth
+
+from gpu_util import (assert_gemm_close, compare_act, compare_weight, dev_gamma, dev_w, dev_x, run_case,
+                      sample_pairs)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+
+
+def oracle_prepare(case, fmt=None, eps=1e-6):
+    return O.prepare(case.x_f32(), case.gamma, eps, fmt or case.fmt)
+
+
+# ------------------------------------------------------------------ prepare
+def test_prepare_tiny_config():
+    case = synth.tiny_case()
+    act = ops.prepare(dev_x(case), dev_gamma(case.gamma), 1e-6, "mxfp4")
+    compare_act(act, oracle_prepare(case))
+
+
+PREP_SHAPES = [  # (T, K, dtype, gamma): spans 64/128/256 threads per row, 1..16 chunks, ragged T
+    (37, 256, "bf16", True), (5, 768, "bf16", True), (3, 32, "f32", True), (64, 4096, "bf16", False),
+    (17, 14336, "bf16", True), (9, 18944, "bf16", True), (33, 2048, "f32", True), (2, 3584, "bf16", True),
+    (1, 96, "bf16", True), (300, 512, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("T,K,dtype,gamma", PREP_SHAPES)
+def test_prepare_shapes(T, K, dtype, gamma, fmt):
+    case = synth.random_case(T * 7 + K, T, K, 8, fmt=fmt, dtype=dtype, gamma=gamma)
+    act = ops.prepare(dev_x(case), dev_gamma(case.gamma), 1e-6, fmt)
+    compare_act(act, oracle_prepare(case))
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_prepare_edge_rows(fmt):
+    # zero row, worked-example row (one 12 among 0.2s), signed zeros, tiny and
+    # large magnitudes, exact ties between pairs
+    K = 64
+    x = np.zeros((6, K), np.float32)
+    x[1, :] = 0.2
+    x[1, 5] = 12.0
+    x[2, ::2] = -0.0
+    x[2, 1::2] = 1e-30
+    x[3, :] = np.float32(3.0e30) * np.cos(np.arange(K))
+    x[4, :] = np.tile(np.array([1, -1, 1, -1, 2, 2, -2, -2], np.float32), K // 8)
+    x[5, :] = np.float32(1e-38) * np.arange(K)
+    case = synth.LinearCase("edge", fmt, "f32", 6, K, 8, x, None, np.zeros((K, 8), np.float32))
+    act = ops.prepare(dev_x(case), None, 1e-6, fmt)
+    compare_act(act, O.prepare(x, None, 1e-6, fmt))
+    g = np.ones(K, np.float32)
+    act = ops.prepare(dev_x(case), dev_gamma(g), 1e-6, fmt)
+    compare_act(act, O.prepare(x, g, 1e-6, fmt))
+
+
+DECODE_IDS = [f"{K}x{D}" for K, D in synth.DECODE_SHAPES]
+NVFP4_IDS = [f"{K}x{D}" for K, D in synth.NVFP4_SHAPES]
+
+
+@pytest.mark.parametrize("i", range(3), ids=DECODE_IDS)
+def test_prepare_decode_full(i):
+    case = synth.decode_case(i)
+    act = ops.prepare(dev_x(case), dev_gamma(case.gamma), 1e-6, "mxfp4")
+    compare_act(act, oracle_prepare(case))
+
+
+def test_prepare_prefill_full_and_deterministic():
+    case = synth.prefill_case(D=256)          # the activation of the 4096 x 4096 x 14336 prefill
+    X, g = dev_x(case), dev_gamma(case.gamma)
+    a1 = ops.prepare(X, g, 1e-6, "mxfp4")
+    s2 = torch.cuda.Stream()
+    with torch.cuda.stream(s2):
+        a2 = ops.prepare(X, g, 1e-6, "mxfp4", stream=s2)
+    s2.synchronize()
+    compare_act(a1, oracle_prepare(case))
+    for k in ("bb_codes", "bb_meta", "bb_scale", "res_codes", "res_scale"):
+        assert torch.equal(getattr(a1, k), getattr(a2, k)), k
+
+
+# ------------------------------------------------------------------ packer
+PACK_SHAPES = [(256, 256, "f32"), (256, 100, "bf16"), (160, 70, "bf16"), (4096, 4096, "bf16"), (96, 513, "f32")]
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("K,D,dtype", PACK_SHAPES)
+def test_pack_shapes(K, D, dtype, fmt):
+    case = synth.random_case(K + D, 1, K, D, fmt=fmt, dtype=dtype)
+    w = ops.pack_weight(dev_w(case.w, dtype), fmt)
+    compare_weight(w, O.pack_weight(case.w_f32(), fmt))
+
+
+def test_pack_grouped_and_full_decode_weight():
+    case = synth.decode_cases()[1]             # 4096 x 14336
+    w = ops.pack_weight(dev_w(case.w, "bf16"), "mxfp4")
+    compare_weight(w, O.pack_weight(case.w_f32(), "mxfp4"))
+    rng = np.random.default_rng(3)
+    W = synth.f32_to_bf16_bits(rng.standard_normal((3, 256, 96)).astype(np.float32) * 0.02)
+    for fmt in ("mxfp4", "nvfp4"):
+        wg = ops.pack_weight(dev_w(W, "bf16"), fmt)
+        for e in range(3):
+            compare_weight(wg, O.pack_weight(synth.bf16_bits_to_f32(W[e]), fmt), group=e)
+
+
+# ------------------------------------------------------------------ dual GEMM
+def test_linear_tiny_config():
+    case = synth.tiny_case()
+    act, w, Y = run_case(case)
+    compare_act(act, oracle_prepare(case))
+    Yr, S = O.sharq_linear(oracle_prepare(case), O.pack_weight(case.w_f32()))
+    assert_gemm_close(Y.cpu().numpy(), Yr, S)
+
+
+LINEAR_SHAPES = [  # skinny (T <= 64) and tile paths, ragged rows and columns
+    (1, 512, 200), (8, 512, 200), (13, 256, 64), (64, 384, 130), (65, 512, 300), (300, 512, 520),
+    (256, 1024, 256), (700, 128, 40),
+]
+
+
+@pytest.mark.parametrize("T,K,D", LINEAR_SHAPES)
+def test_linear_shapes(T, K, D):
+    case = synth.random_case(T + 3 * K + D, T, K, D)
+    act, w, Y = run_case(case)
+    ref = oracle_prepare(case)
+    compare_act(act, ref)
+    Yr, S = O.sharq_linear(ref, O.pack_weight(case.w_f32()))
+    assert_gemm_close(Y.cpu().numpy(), Yr, S)
+
+
+@pytest.mark.parametrize("T", [8, 200])
+def test_linear_row_gather(T):
+    case = synth.random_case(99 + T, T, 256, 96)
+    act = ops.prepare(dev_x(case), dev_gamma(case.gamma), 1e-6)
+    w = ops.pack_weight(dev_w(case.w, "bf16"))
+    rows = np.random.default_rng(T).integers(0, T, T + 5).astype(np.int32)
+    Y = ops.linear(act, w, row_index=torch.from_numpy(rows).cuda())
+    Yr, S = O.sharq_linear(oracle_prepare(case), O.pack_weight(case.w_f32()), rows=rows)
+    assert_gemm_close(Y.cpu().numpy(), Yr, S)
+
+
+@pytest.mark.parametrize("i", range(3), ids=DECODE_IDS)
+def test_linear_decode_full_sampled(i):
+    case = synth.decode_case(i)
+    act, w, Y = run_case(case)
+    ref = oracle_prepare(case)
+    compare_act(act, ref)
+    r, c = sample_pairs(case.T, case.D, 3000, seed=case.K)
+    Yr, S = O.sharq_linear_sampled(ref, O.pack_weight(case.w_f32()), r, c)
+    assert_gemm_close(Y.cpu().numpy()[r, c], Yr, S)
+
+
+def test_linear_prefill_full_sampled_and_deterministic():
+    case = synth.prefill_case()
+    act, w, Y = run_case(case)
+    Y2 = ops.linear(act, w)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2)
+    ref = oracle_prepare(case)
+    r, c = sample_pairs(case.T, case.D, 3000, seed=1)
+    cols = np.unique(c)
+    wref = O.weight_cols(O.pack_weight(case.w_f32()[:, cols]), slice(None))
+    ci = np.searchsorted(cols, c)
+    Yr, S = O.sharq_linear_sampled(ref, wref, r, ci)
+    assert_gemm_close(Y.cpu().numpy()[r, c], Yr, S)
+
+
+# ------------------------------------------------------------------ NVFP4 (emulated)
+@pytest.mark.parametrize("T,K,D", [(16, 256, 64), (130, 512, 200), (64, 3584, 300)])
+def test_nvfp4_linear_shapes(T, K, D):
+    case = synth.random_case(T + K + D + 1, T, K, D, fmt="nvfp4", spec=synth.QWEN_OUTLIERS)
+    act, w, Y = run_case(case)
+    ref = oracle_prepare(case)
+    compare_act(act, ref)
+    wref = O.pack_weight(case.w_f32(), "nvfp4")
+    compare_weight(w, wref)
+    Yr, S = O.sharq_linear(ref, wref)
+    assert_gemm_close(Y.cpu().numpy(), Yr, S)
+
+
+@pytest.mark.parametrize("i", range(2), ids=NVFP4_IDS)
+def test_nvfp4_full_sampled(i):
+    case = synth.nvfp4_cases(shapes=[synth.NVFP4_SHAPES[i]])[0]
+    act, w, Y = run_case(case)
+    ref = oracle_prepare(case)
+    compare_act(act, ref)
+    r, c = sample_pairs(case.T, case.D, 2000, seed=2)
+    cols = np.unique(c)
+    Wf = case.w_f32()
+    # the tensor scale belongs to the whole weight: pack the sampled columns under it
+    wsub = O.pack_weight(np.ascontiguousarray(Wf[:, cols]), "nvfp4", tensor_amax=np.abs(Wf).max())
+    assert np.array_equal(w.tensor_scale.cpu().numpy(), wsub["tensor_scale"])
+    compare_weight_cols(w, wsub, cols)
+    Yr, S = O.sharq_linear_sampled(ref, wsub, r, np.searchsorted(cols, c))
+    assert_gemm_close(Y.cpu().numpy()[r, c], Yr, S)
+
+
+def compare_weight_cols(w, ref, cols):
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(cols).cuda()
+    for k in ("payload", "scale_sp", "scale_dn"):
+        got = getattr(w, k)[0].index_select(0, idx).cpu().numpy()
+        assert np.array_equal(got, ref[k]), k
+
+
+# ------------------------------------------------------------------ grouped (MoE)
+def test_grouped_small():
+    rng = np.random.default_rng(8)
+    E, T, K, D = 8, 64, 256, 160
+    go, ri = synth.draw_routing(rng, T, E, 2)
+    case = synth.random_case(8, T, K, 1)
+    W = synth.f32_to_bf16_bits(rng.standard_normal((E, K, D)).astype(np.float32) * 0.02)
+    act = ops.prepare(dev_x(case), dev_gamma(case.gamma), 1e-6)
+    w = ops.pack_weight(dev_w(W, "bf16"))
+    Y = ops.linear(act, w, group_offsets=torch.from_numpy(go).cuda(), row_index=torch.from_numpy(ri).cuda())
+    ref = oracle_prepare(case)
+    wps = [O.pack_weight(synth.bf16_bits_to_f32(W[e])) for e in range(E)]
+    Yr, S = O.grouped_linear(ref, wps, go, ri)
+    assert_gemm_close(Y.cpu().numpy(), Yr, S)
+
+
+@pytest.mark.parametrize("proj", ["up", "down"])
+def test_grouped_moe_full_sampled(proj):
+    mc = synth.moe_case(proj)
+    X = torch.from_numpy(mc.x.view(np.int16)).view(torch.bfloat16).cuda()
+    act = ops.prepare(X, dev_gamma(mc.gamma), 1e-6)
+    w = ops.pack_weight(torch.from_numpy(mc.w.view(np.int16)).view(torch.bfloat16).cuda())
+    go = torch.from_numpy(mc.group_offsets).cuda()
+    ri = None if mc.row_index is None else torch.from_numpy(mc.row_index).cuda()
+    Y = ops.linear(act, w, group_offsets=go, row_index=ri, total_rows=mc.total_rows)
+    torch.cuda.synchronize()
+    xa = mc.x_f32()
+    ref = O.prepare(xa, mc.gamma, 1e-6)
+    compare_act(act, ref)
+    # sample outputs in a handful of experts; pack only those experts in the oracle
+    rng = np.random.default_rng(5)
+    experts = rng.choice(mc.n_experts, 6, replace=False)
+    Yg = Y.cpu().numpy()
+    for e in experts:
+        a, b = int(mc.group_offsets[e]), int(mc.group_offsets[e + 1])
+        wref = O.pack_weight(synth.bf16_bits_to_f32(mc.w[e]))
+        compare_weight(w, wref, group=int(e))
+        r = rng.integers(a, b, 200)
+        c = rng.integers(0, mc.D, 200)
+        rows = None if mc.row_index is None else mc.row_index
+        Yr, S = O.sharq_linear_sampled(ref, wref, r, c, rows=rows)
+        assert_gemm_close(Yg[r, c], Yr, S)
