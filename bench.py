@@ -1,0 +1,394 @@
+"""Benchmark of the SharQ linear-layer hot path on one MI355X.
+
+Default workload (one JSON line on stdout): the Llama-3.1-8B decode linears,
+MXFP4, T = 8 tokens, shapes (K, D) = (4096, 4096), (4096, 14336),
+(14336, 4096).  One step = the whole per-forward hot path over one batch:
+for each of the three linears, the fused prepare (RMSNorm, 4:8 in-pairs mask,
+FP4 backbone + residual) and the dual-path FP4 GEMM.  Weight packing is the
+offline step and is timed separately (``pack_us``).
+
+Inputs are resident in HBM before timing starts; the packed weights rotate
+through ``--copies`` distinct buffers (default 8, about 570 MB) so the 256 MB
+Infinity Cache cannot serve them between steps.
+
+``--workload prefill|nvfp4|moe`` measures the other shapes (4096 x 4096 x
+14336 prefill; emulated NVFP4 at T = 2048; grouped MoE up+down) for the
+profiles; they are not the headline line.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = "SharQ linear TFLOPS-eff + tokens/s at Llama-3.1-8B shapes; % HBM/MFMA peak"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="decode", choices=["decode", "prefill", "nvfp4", "moe"])
+    p.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = enough for > 512 MB)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+# ----------------------------------------------------------------------------
+# workloads
+# ----------------------------------------------------------------------------
+class Job:
+    """One SharQ linear of the step: inputs, preallocated outputs, weight copies."""
+
+    def __init__(self, name, fmt, X, gamma, weights, T, K, D, rows=None, group_offsets=None, row_index=None):
+        from sparsity_sharq_prepare_amd import ops
+        import torch
+        # activation copies rotate with the weight copies (same data, distinct buffers)
+        self.Xs = [X] + [X.clone() for _ in range(len(weights) - 1)]
+        self.X = X
+        self.name, self.fmt, self.gamma, self.weights = name, fmt, gamma, weights
+        self.T, self.K, self.D = T, K, D
+        self.rows = rows if rows is not None else T
+        self.group_offsets, self.row_index = group_offsets, row_index
+        self.act = ops.empty_act(fmt, X.shape[0], K, X.device)
+        self.Y = torch.empty((self.rows, D), dtype=torch.float32, device=X.device)
+        self.groups = weights[0].n_groups
+
+    # algorithmic work (SURVEY-defined units)
+    def gemm_flops_nominal(self):
+        return 2.0 * self.rows * self.K * self.D
+
+    def gemm_flops_alg(self):            # backbone counted at its nonzeros: 3 T K D
+        return 3.0 * self.rows * self.K * self.D
+
+    def gemm_flops_issued(self):         # zero-filled backbone on dense MFMA: 4 T K D
+        return 4.0 * self.rows * self.K * self.D
+
+    def gemm_bytes(self):
+        w = self.groups * self.D * self.K * (0.5 + 1.0 / 32)
+        a = self.X.shape[0] * self.K * 0.875
+        return w + a + 4.0 * self.rows * self.D
+
+    def prep_bytes(self):
+        xb = self.X.element_size()
+        out = 0.875 if self.fmt == "mxfp4" else 0.90625
+        return self.X.shape[0] * self.K * (xb + out) + 4.0 * self.K
+
+
+def _dev(a, bf16=True):
+    import numpy as np
+    import torch
+    if bf16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def build_jobs(workload: str, copies: int):
+    import numpy as np
+    import torch
+    from sparsity_sharq_prepare_amd import ops, synth
+
+    jobs, cases, pack_times = [], [], []
+
+    def pack_copies(W, fmt, n):
+        out = []
+        for i in range(n):
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            out.append(ops.pack_weight(W, fmt))
+            ev1.record()
+            torch.cuda.synchronize()
+            pack_times.append((ev0.elapsed_time(ev1) * 1e3, W.numel()))
+        return out
+
+    def n_copies(bytes_one):
+        return copies or max(2, min(64, int(np.ceil(600e6 / bytes_one))))
+
+    if workload == "decode":
+        trio_bytes = sum(K * D * 0.53125 for K, D in synth.DECODE_SHAPES)
+        n = n_copies(trio_bytes)
+        for i in range(3):
+            c = synth.decode_case(i)
+            W = _dev(c.w)
+            jobs.append(Job(c.name, "mxfp4", _dev(c.x), _dev(c.gamma, False), pack_copies(W, "mxfp4", n),
+                            c.T, c.K, c.D))
+            del W
+            cases.append(c)
+    elif workload == "prefill":
+        c = synth.prefill_case()
+        W = _dev(c.w)
+        jobs.append(Job(c.name, "mxfp4", _dev(c.x), _dev(c.gamma, False),
+                        pack_copies(W, "mxfp4", n_copies(c.K * c.D * 0.53125)), c.T, c.K, c.D))
+        cases.append(c)
+    elif workload == "nvfp4":
+        for c in synth.nvfp4_cases():
+            W = _dev(c.w)
+            jobs.append(Job(c.name, "nvfp4", _dev(c.x), _dev(c.gamma, False),
+                            pack_copies(W, "nvfp4", n_copies(c.K * c.D * 0.53125)), c.T, c.K, c.D))
+            cases.append(c)
+    elif workload == "moe":
+        for proj in ("up", "down"):
+            mc = synth.moe_case(proj)
+            W = _dev(mc.w)
+            go = torch.from_numpy(mc.group_offsets).cuda()
+            ri = None if mc.row_index is None else torch.from_numpy(mc.row_index).cuda()
+            jobs.append(Job(mc.name, "mxfp4", _dev(mc.x), _dev(mc.gamma, False),
+                            pack_copies(W, "mxfp4", n_copies(W.numel() * 0.53125)), mc.x.shape[0], mc.K, mc.D,
+                            rows=mc.total_rows, group_offsets=go, row_index=ri))
+            cases.append(mc)
+    torch.cuda.synchronize()
+    return jobs, cases, pack_times
+
+
+# ----------------------------------------------------------------------------
+# timing
+# ----------------------------------------------------------------------------
+def run_step(jobs, it, events=None):
+    from sparsity_sharq_prepare_amd import ops
+    for j, job in enumerate(jobs):
+        w = job.weights[it % len(job.weights)]
+        if events is not None:
+            events[j][0].record()
+        ops.prepare(job.Xs[it % len(job.Xs)], job.gamma, 1e-6, job.fmt, out=job.act)
+        if events is not None:
+            events[j][1].record()
+        ops.linear(job.act, w, group_offsets=job.group_offsets, row_index=job.row_index, total_rows=job.rows,
+                   out=job.Y)
+        if events is not None:
+            events[j][2].record()
+
+
+def capture(jobs, first, count):
+    """One HIP graph holding `count` consecutive steps starting at step
+    `first` (step i uses weight copy i mod copies), so the timed loop is not
+    bound by host-side launch overhead."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(first, first + count):
+            run_step(jobs, i)
+    return g
+
+
+def timed(jobs, steps, warmup):
+    """Wall time of exactly `steps` steps (graph replays after `warmup`
+    steps), plus per-kernel durations from HIP events recorded around each
+    launch on the launch stream."""
+    import torch
+    R = len(jobs[0].weights)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):           # eager warm-up before capture
+        for i in range(R):
+            run_step(jobs, i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    full = capture(jobs, 0, R)              # R steps: one per weight copy
+    singles = [capture(jobs, i, 1) for i in range(R)]
+    torch.cuda.synchronize()
+
+    def run(n):
+        for _ in range(n // R):
+            full.replay()
+        for i in range(n % R):
+            singles[i].replay()
+
+    run(warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    n_steps = steps
+    # per-kernel durations: eager launches queued behind a sleep kernel so the
+    # GPU never waits for the host between an event and the kernel it brackets
+    prep_ms = [0.0] * len(jobs)
+    gemm_ms = [0.0] * len(jobs)
+    chunk = 8
+    for base in range(0, n_steps, chunk):
+        ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in jobs] for _ in range(chunk)]
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(2_000_000)
+        for i in range(chunk):
+            run_step(jobs, base + i, ev[i])
+        torch.cuda.synchronize()
+        for i in range(chunk):
+            for j in range(len(jobs)):
+                prep_ms[j] += ev[i][j][0].elapsed_time(ev[i][j][1])
+                gemm_ms[j] += ev[i][j][1].elapsed_time(ev[i][j][2])
+    n_ev = -(-n_steps // chunk) * chunk
+    return wall, n_steps, [p / n_ev for p in prep_ms], [g / n_ev for g in gemm_ms]
+
+
+# ----------------------------------------------------------------------------
+# CPU oracle baseline
+# ----------------------------------------------------------------------------
+def cpu_baseline(cases, workload, target_s):
+    """Time the CPU oracle (as it stands) on a bounded sample of the workload."""
+    import numpy as np
+    from oracle import sharq as O
+    from sparsity_sharq_prepare_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    if workload in ("decode", "prefill", "nvfp4"):
+        items = []
+        for c in cases:
+            rows = c.T if workload == "decode" else min(c.T, 64)
+            wp = O.pack_weight(c.w_f32(), c.fmt)          # offline step, not timed
+            items.append((c.x_f32()[:rows], c.gamma, wp, c.fmt, rows * c.K * c.D * 2.0))
+        flops, n, t = 0.0, 0, 0.0
+        while t < target_s and n < 50:
+            for x, g, wp, fmt, fl in items:
+                t0 = time.perf_counter()
+                act = O.prepare(x, g, 1e-6, fmt)
+                O.sharq_linear(act, wp)
+                t += time.perf_counter() - t0
+                flops += fl
+            n += 1
+        rows_desc = "all 8 rows" if workload == "decode" else "the first 64 rows"
+        sample = f"{n} pass(es) of the workload's {len(items)} linear(s) on {rows_desc} (prepare + dual GEMM, weights pre-packed)"
+        return {"value": flops / t / 1e12, "unit": "TFLOPS-eff", "cores": cores, "kind": "oracle", "sample": sample,
+                "seconds": round(t, 2)}
+    # moe: a few experts of each projection
+    flops, t = 0.0, 0.0
+    n_exp = 0
+    for mc in cases:
+        x = mc.x_f32()
+        for e in range(mc.n_experts):
+            a, b = int(mc.group_offsets[e]), int(mc.group_offsets[e + 1])
+            rows = np.arange(a, b) if mc.row_index is None else mc.row_index[a:b]
+            wp = O.pack_weight(synth.bf16_bits_to_f32(mc.w[e]), "mxfp4")     # offline step, not timed
+            t0 = time.perf_counter()
+            act = O.prepare(x[rows], mc.gamma, 1e-6)
+            O.sharq_linear(act, wp)
+            t += time.perf_counter() - t0
+            flops += 2.0 * (b - a) * mc.K * mc.D
+            n_exp += 1
+            if t > target_s / 2 * (1 + (mc is cases[-1])):
+                break
+    return {"value": flops / t / 1e12, "unit": "TFLOPS-eff", "cores": cores, "kind": "oracle",
+            "sample": f"{n_exp} experts' rows (prepare + dual GEMM, weights pre-packed)", "seconds": round(t, 2)}
+
+
+# ----------------------------------------------------------------------------
+# traffic counters recorded by rocprofv3 (profiles/<kernel>_<workload>_traffic.txt)
+# ----------------------------------------------------------------------------
+def kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "sparsity_sharq_prepare_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name, sources):
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != kernel_source_hash(sources):
+        return None                          # the kernel changed since the counters were taken
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the SharQ hot path here runs on a "
+              "single MI355X and has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sparsity_sharq_prepare_amd import _lib
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    _lib.lib()                                # fail loudly if libsharq.so is missing
+    jobs, cases, pack_times = build_jobs(args.workload, args.copies)
+    wall, n_steps, prep_ms, gemm_ms = timed(jobs, args.steps, args.warmup)
+    ms_step = wall * 1e3 / n_steps
+
+    nominal = sum(j.gemm_flops_nominal() for j in jobs)
+    tflops = nominal / (ms_step * 1e-3) / 1e12
+    tokens = sum(j.X.shape[0] for j in jobs) / len(jobs)
+    tok_s = tokens / (ms_step * 1e-3)
+
+    gemm_total_ms = sum(gemm_ms)
+    prep_total_ms = sum(prep_ms)
+    kernels = {}
+    for j, p, g in zip(jobs, prep_ms, gemm_ms):
+        kernels[j.name] = {
+            "prepare_us": round(p * 1e3, 2), "prepare_GBs": round(j.prep_bytes() / (p * 1e-3) / 1e9, 1),
+            "gemm_us": round(g * 1e3, 2), "gemm_GBs": round(j.gemm_bytes() / (g * 1e-3) / 1e9, 1),
+            "gemm_TFLOPS_alg": round(j.gemm_flops_alg() / (g * 1e-3) / 1e12, 1),
+            "gemm_TFLOPS_issued": round(j.gemm_flops_issued() / (g * 1e-3) / 1e12, 1),
+        }
+    n = len(jobs)
+    if args.workload == "decode":
+        dom, bound, unit, peak = "linear_mx_skinny", "hbm", "GB/s", HBM_PEAK_GBS
+        ach = sum(j.gemm_bytes() for j in jobs) / n / (gemm_total_ms / n * 1e-3) / 1e9
+        src = ["gemm_mx.hip", "common.h"]
+    elif args.workload == "nvfp4":
+        dom, bound, unit, peak = "linear_nv_tile", "mfma", "TFLOP/s", BF16_PEAK_TFLOPS
+        ach = sum(j.gemm_flops_alg() for j in jobs) / n / (gemm_total_ms / n * 1e-3) / 1e12
+        src = ["gemm_nv.hip", "common.h"]
+    else:
+        dom = "linear_mx_tile"
+        bound, unit, peak = "mfma", "TFLOP/s", FP4_PEAK_TFLOPS
+        ach = sum(j.gemm_flops_alg() for j in jobs) / n / (gemm_total_ms / n * 1e-3) / 1e12
+        src = ["gemm_mx.hip", "common.h"]
+    roofline = {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                "frac": round(ach / peak, 4), "traffic": read_traffic(f"{dom}_{args.workload}", src),
+                "kernel": dom, "launch_us": round(gemm_total_ms / n * 1e3, 2)}
+    prep_ach = sum(j.prep_bytes() for j in jobs) / (prep_total_ms * 1e-3) / 1e9
+    pack_us = sum(t for t, _ in pack_times) / len(pack_times)
+
+    out = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOPS-eff", "n_gpus": 1, "steps": n_steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp4" if args.workload != "nvfp4" else "nvfp4-emu(bf16 mfma)",
+        "data": "synthetic",
+        "config": {"workload": {"decode": "llama3.1-8b decode linears, T=8, (4096x4096, 4096x14336, 14336x4096), MXFP4",
+                                "prefill": "llama3.1-8b prefill linear 4096x4096x14336, MXFP4",
+                                "nvfp4": "qwen2.5-7b linears T=2048 (3584x18944, 18944x3584), NVFP4 emulated",
+                                "moe": "qwen3-30b-a3b moe linears, 128 experts top-8, 4096 tokens, up 2048x768 + down 768x2048, MXFP4"}[args.workload],
+                   "tokens_per_step": tokens, "weight_copies_rotated": len(jobs[0].weights)},
+        "tokens_per_s": round(tok_s, 1),
+        "roofline": roofline,
+        "prepare": {"achieved_GBs": round(prep_ach, 1), "frac_hbm": round(prep_ach / HBM_PEAK_GBS, 4),
+                    "launch_us": round(prep_total_ms / n * 1e3, 2)},
+        "kernels": kernels,
+        "pack_us": round(pack_us, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cases, args.workload, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

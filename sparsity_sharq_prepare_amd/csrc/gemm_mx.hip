@@ -37,6 +37,15 @@ SHARQ_DEV v4f mfma_fp4(uint4 a, uint4 b, v4f c, uint32_t sa, uint32_t sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(as_v8i(a), as_v8i(b), c, 4, 4, 0, (int)sa, 0, (int)sb);
 }
 
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// 32x32x64 FP4 x FP4 (on gfx950 about 2.5x the throughput of the 16x16x128
+// form): lane l holds row / column (l & 31), K-values 32 * (l >> 5) .. +31;
+// result register i of lane l is row 8 (i / 4) + 4 (l >> 5) + i % 4, column l & 31.
+SHARQ_DEV v16f mfma32_fp4(uint4 a, uint4 b, v16f c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_v8i(a), as_v8i(b), c, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
 // expand 4 groups (8 compacted bytes + 4 metadata nibbles) into 16 bytes
 SHARQ_DEV uint4 expand4(uint32_t c_lo, uint32_t c_hi, uint32_t meta16) {
   uint4 r;
@@ -152,24 +161,71 @@ __global__ __launch_bounds__(MT >= 8 ? 512 : 1024) void linear_mx_skinny(
 // ============================================================================
 // tile kernel (prefill / grouped)
 // ============================================================================
+// Workgroup tile BM x 256 (BM = 256 plain, 128 grouped), K steps of 128, four
+// waves stacked along M (each BM/4 rows x 256 columns, so every backbone
+// fragment is expanded by exactly one wave).  Operands are staged with
+// buffer->LDS DMA (buffer_load_dword{,x4} ... lds: no staging registers, so
+// the accumulator tile fits; the per-step offset is a scalar, so issuing a
+// stage costs no vector instructions; reads past a buffer return zeros) into
+// a 3-deep LDS ring: the loads for step s+2 are in flight while step s
+// computes, with one barrier per step.  The backbone stays compacted in LDS
+// (8 bytes + 4 metadata nibbles per 32 K-values of a row) and is expanded
+// when its fragments are read.
 namespace {
 
 constexpr int kBN = 256;
-constexpr int kRowBytes = 64;            // 128 FP4 values per staged row
+constexpr int kNS = 3;                   // LDS ring depth
 
-// 16-byte slot of (row, chunk) in a staged tile: XOR swizzle so that the 16
-// rows an MFMA fragment read touches fall in distinct banks
+// 16-byte slot of (row, chunk q) in a 64-byte-per-row staged tile; the XOR
+// keeps the 16 rows one fragment read touches in distinct banks
 SHARQ_DEV int slot(int row, int q) { return row * 4 + (q ^ (((row >> 1) ^ (row >> 3)) & 3)); }
+// 16-byte half h of a 32-byte compacted-backbone row
+SHARQ_DEV int slot_sp(int row, int h) { return row * 2 + (h ^ ((row >> 3) & 1)); }
 
 template <int BM>
-struct Stage {
-  uint4 a_sp[BM * 4];
-  uint4 a_dn[BM * 4];
-  uint4 b[kBN * 4];
-  uint32_t s_sp[BM];
+struct TileStage {
+  uint4 a_dn[BM * 4];          // residual codes, 64 B per row (swizzled 16 B slots)
+  uint4 b[kBN * 4];            // weight payload, 64 B per column
+  uint4 a_sp[BM * 2];          // compacted backbone, 32 B per row
+  uint32_t meta[BM * 2];       // backbone metadata, 8 B per row
+  uint32_t s_sp[BM];           // 4 scale bytes per row / column
   uint32_t s_dn[BM];
   uint32_t s_b[kBN];
 };
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+SHARQ_DEV __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// lane l of the wave writes its 16 (4) bytes at lds + 16 l (4 l)
+SHARQ_DEV void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+SHARQ_DEV void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, soff, 0, 0);
+}
+
+// s_waitcnt vmcnt <= N, lgkmcnt 0 (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
+// lgkmcnt[11:8] | vmcnt[5:4] at [15:14])
+template <int N>
+SHARQ_DEV void wait_vm_lgkm0() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// 4 groups (8 compacted bytes c_lo, c_hi + 4 nibbles of meta16) -> 16 bytes.
+// Moving i0 / i1 of every nibble to bits 3-4 of its nibble makes
+// (m >> 4g) & 0x18 the byte shift 8 * i of group g.
+SHARQ_DEV uint4 expand4_fast(uint32_t c_lo, uint32_t c_hi, uint32_t meta16) {
+  const uint32_t m0 = (meta16 & 0x3333u) << 3;        // 8 * i0 at bits 4g + 3 .. 4g + 4
+  const uint32_t m1 = (meta16 & 0xCCCCu) << 1;        // 8 * i1
+  uint4 r;
+  r.x = ((c_lo & 0xFFu) << (m0 & 0x18u)) | (((c_lo >> 8) & 0xFFu) << (m1 & 0x18u));
+  r.y = (((c_lo >> 16) & 0xFFu) << ((m0 >> 4) & 0x18u)) | ((c_lo >> 24) << ((m1 >> 4) & 0x18u));
+  r.z = ((c_hi & 0xFFu) << ((m0 >> 8) & 0x18u)) | (((c_hi >> 8) & 0xFFu) << ((m1 >> 8) & 0x18u));
+  r.w = (((c_hi >> 16) & 0xFFu) << ((m0 >> 12) & 0x18u)) | ((c_hi >> 24) << ((m1 >> 12) & 0x18u));
+  return r;
+}
 
 }  // namespace
 
@@ -179,8 +235,14 @@ __global__ __launch_bounds__(256, 1) void linear_mx_tile(
     const uint8_t* __restrict__ res_codes, const uint8_t* __restrict__ res_scale, const int32_t* __restrict__ row_index,
     int rows, int act_rows, int K, const uint8_t* __restrict__ payload, const uint8_t* __restrict__ wscale, int D,
     int n_groups, const int32_t* __restrict__ group_offsets, float* __restrict__ Y, int64_t ldy) {
-  constexpr int WM = BM / 2, FM = WM / 16, FN = 8, UA = BM / 64;
-  __shared__ Stage<BM> st[2];
+  using Stage = TileStage<BM>;
+  constexpr int WM = BM / 4, FM = WM / 32, FN = kBN / 32;
+  // DMA instructions per wave and stage: A_dn, B, A_sp, meta, 3 scale rows
+  constexpr int N_DN = BM / 64, N_B = 4, N_SP = BM / 128, N_MT = BM / 128;
+  constexpr int NDMA = N_DN + N_B + N_SP + N_MT + 3;
+  // three separate typed LDS objects, indexed as arrays, so the compiler can
+  // tell the buffer being read from the buffers the in-flight DMAs write
+  __shared__ Stage lds0, lds1, lds2;
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   const int tiles_n = (D + kBN - 1) / kBN;
 
@@ -214,133 +276,145 @@ __global__ __launch_bounds__(256, 1) void linear_mx_tile(
   }
 
   const int KS = K >> 7;
-  const int64_t kA = K >> 2, kM = K >> 4, kS = K >> 5, kR = K >> 1;
-  const uint8_t* pay = payload + (int64_t)grp * D * kR;
-  const uint8_t* wsc = wscale + (int64_t)grp * D * kS;
+  const uint32_t kA = K >> 2, kM = K >> 4, kS = K >> 5, kR = K >> 1;
+  const __amdgpu_buffer_rsrc_t r_dn = rsrc(res_codes, (uint32_t)act_rows * kR);
+  const __amdgpu_buffer_rsrc_t r_sp = rsrc(bb_codes, (uint32_t)act_rows * kA);
+  const __amdgpu_buffer_rsrc_t r_mt = rsrc(bb_meta, (uint32_t)act_rows * kM);
+  const __amdgpu_buffer_rsrc_t r_ssp = rsrc(bb_scale, (uint32_t)act_rows * kS);
+  const __amdgpu_buffer_rsrc_t r_sdn = rsrc(res_scale, (uint32_t)act_rows * kS);
+  const __amdgpu_buffer_rsrc_t r_b = rsrc(payload + (int64_t)grp * D * kR, (uint32_t)D * kR);
+  const __amdgpu_buffer_rsrc_t r_sb = rsrc(wscale + (int64_t)grp * D * kS, (uint32_t)D * kS);
 
-  // ---- per-thread staging rows (A: rows u >> 2 of units u = tid + 256 i)
-  int64_t arow[UA];
-  bool aok[UA];
-#pragma unroll
-  for (int i = 0; i < UA; ++i) {
-    const int r = m0 + ((tid + 256 * i) >> 2);
-    aok[i] = r < row_end;
-    arow[i] = aok[i] ? gather_row(row_index, r, act_rows) : 0;
-  }
-  const int q = tid & 3;
-  int64_t brow[4];
-  bool bok[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = n0 + ((tid + 256 * i) >> 2);
-    bok[i] = c < D;
-    brow[i] = bok[i] ? c : 0;
-  }
-  const bool srow_a = tid < BM;
-  const int sr = m0 + tid;
-  const bool sa_ok = srow_a && sr < row_end;
-  const int64_t sarow = sa_ok ? gather_row(row_index, sr, act_rows) : 0;
-  const bool sb_ok = n0 + tid < D;
-  const int64_t sbrow = sb_ok ? n0 + tid : 0;
-
-  // ---- prefetch registers
-  uint2 pc[UA];
-  uint32_t pm[UA];
-  uint4 pd[UA];
-  uint4 pb[4];
-  uint32_t ps_sp = 0, ps_dn = 0, ps_b = 0;
-
-  auto load_step = [&](int s) {
-#pragma unroll
-    for (int i = 0; i < UA; ++i) {
-      pc[i] = make_uint2(0, 0);
-      pm[i] = 0;
-      pd[i] = make_uint4(0, 0, 0, 0);
-      if (aok[i]) {
-        pc[i] = *reinterpret_cast<const uint2*>(bb_codes + arow[i] * kA + 32 * (int64_t)s + 8 * q);
-        pm[i] = *reinterpret_cast<const uint16_t*>(bb_meta + arow[i] * kM + 8 * (int64_t)s + 2 * q);
-        pd[i] = *reinterpret_cast<const uint4*>(res_codes + arow[i] * kR + 64 * (int64_t)s + 16 * q);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pb[i] = make_uint4(0, 0, 0, 0);
-      if (bok[i]) pb[i] = *reinterpret_cast<const uint4*>(pay + brow[i] * kR + 64 * (int64_t)s + 16 * q);
-    }
-    ps_sp = 0x7F7F7F7Fu;
-    ps_dn = 0x7F7F7F7Fu;
-    ps_b = 0x7F7F7F7Fu;
-    if (sa_ok) {
-      ps_sp = *reinterpret_cast<const uint32_t*>(bb_scale + sarow * kS + 4 * (int64_t)s);
-      ps_dn = *reinterpret_cast<const uint32_t*>(res_scale + sarow * kS + 4 * (int64_t)s);
-    }
-    if (sb_ok) ps_b = *reinterpret_cast<const uint32_t*>(wsc + sbrow * kS + 4 * (int64_t)s);
+  // activation row of tile row r (rows outside the tile read row 0: their
+  // products reach only outputs that are never stored)
+  auto act_row = [&](int r) -> uint32_t {
+    const int gr = m0 + r;
+    return gr < row_end ? (uint32_t)gather_row(row_index, gr, act_rows) : 0u;
   };
-  auto store_step = [&](Stage<BM>& S) {
+  auto w_row = [&](int c) -> uint32_t { return n0 + c < D ? (uint32_t)(n0 + c) : 0u; };
+
+  // ---- per-lane DMA byte offsets (step 0); instruction j of this wave fills
+  // slots [64 j', 64 j' + 64) of its region, j' = w + 4 j
+  uint32_t o_dn[N_DN], o_b[N_B], o_sp[N_SP], o_mt[N_MT];
 #pragma unroll
-    for (int i = 0; i < UA; ++i) {
-      const int row = (tid + 256 * i) >> 2;
-      S.a_sp[slot(row, q)] = expand4(pc[i].x, pc[i].y, pm[i]);
-      S.a_dn[slot(row, q)] = pd[i];
-    }
+  for (int j = 0; j < N_DN; ++j) {
+    const int sl = 64 * (w + 4 * j) + l, row = sl >> 2, q = (sl & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
+    o_dn[j] = act_row(row) * kR + 16 * q;
+  }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) S.b[slot((tid + 256 * i) >> 2, q)] = pb[i];
-    if (srow_a) {
-      S.s_sp[tid] = ps_sp;
-      S.s_dn[tid] = ps_dn;
-    }
-    S.s_b[tid] = ps_b;
+  for (int j = 0; j < N_B; ++j) {
+    const int sl = 64 * (w + 4 * j) + l, col = sl >> 2, q = (sl & 3) ^ (((col >> 1) ^ (col >> 3)) & 3);
+    o_b[j] = w_row(col) * kR + 16 * q;
+  }
+#pragma unroll
+  for (int j = 0; j < N_SP; ++j) {
+    const int sl = 64 * (w + 4 * j) + l, row = sl >> 1, h = (sl & 1) ^ ((row >> 3) & 1);
+    o_sp[j] = act_row(row) * kA + 16 * h;
+  }
+#pragma unroll
+  for (int j = 0; j < N_MT; ++j) {                      // dword slots: 2 per row
+    const int sl = 64 * (w + 4 * j) + l, row = sl >> 1, h = sl & 1;
+    o_mt[j] = act_row(row) * kM + 4 * h;
+  }
+  // scale rows: one dword (4 blocks) per row; for BM = 128 waves 2, 3 repeat
+  // the rows of waves 0, 1 (same bytes to the same place)
+  const int srow = (64 * w + l) & (BM - 1);
+  const uint32_t o_ssp = act_row(srow) * kS;
+  const uint32_t o_sb = w_row(64 * w + l) * kS;
+  const int sdst = 64 * (w & (BM / 64 - 1));
+
+  auto issue = [&](int s, Stage& st) {
+#pragma unroll
+    for (int j = 0; j < N_DN; ++j) dma16(r_dn, o_dn[j], 64u * s, (uint8_t*)&st.a_dn[64 * (w + 4 * j)]);
+#pragma unroll
+    for (int j = 0; j < N_B; ++j) dma16(r_b, o_b[j], 64u * s, (uint8_t*)&st.b[64 * (w + 4 * j)]);
+#pragma unroll
+    for (int j = 0; j < N_SP; ++j) dma16(r_sp, o_sp[j], 32u * s, (uint8_t*)&st.a_sp[64 * (w + 4 * j)]);
+#pragma unroll
+    for (int j = 0; j < N_MT; ++j) dma4(r_mt, o_mt[j], 8u * s, (uint8_t*)&st.meta[64 * (w + 4 * j)]);
+    dma4(r_ssp, o_ssp, 4u * s, (uint8_t*)&st.s_sp[sdst]);
+    dma4(r_sdn, o_ssp, 4u * s, (uint8_t*)&st.s_dn[sdst]);
+    dma4(r_sb, o_sb, 4u * s, (uint8_t*)&st.s_b[64 * w]);
   };
 
-  const int wm0 = (w >> 1) * WM, wn0 = (w & 1) * 128;
-  const int kq = l >> 4, lr = l & 15;
-  v4f acc[FM][FN];
+  const int wm0 = w * WM;
+  const int kh = l >> 5, lr = l & 31;
+  v16f acc[FM][FN];
 #pragma unroll
   for (int f = 0; f < FM; ++f)
 #pragma unroll
-    for (int n = 0; n < FN; ++n) acc[f][n] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < FN; ++n) acc[f][n] = (v16f){};
 
-  load_step(0);
-  store_step(st[0]);
-  __syncthreads();
-  for (int s = 0; s < KS; ++s) {
-    const bool more = s + 1 < KS;
-    if (more) load_step(s + 1);
-    const Stage<BM>& S = st[s & 1];
-    uint4 bf[FN];
-    uint32_t bs[FN];
+  auto step = [&](int s, const Stage& st, Stage& st2) {
+    // own DMAs of step s complete (those of step s+1 stay in flight), then publish
+    wait_vm_lgkm0<NDMA>();
+    __builtin_amdgcn_s_barrier();
+    // all fragments of step s into registers first: two K sub-steps of 64,
+    // sub-step j of lane half kh reads 16-byte chunk q = 2 j + kh of a row
+    const uint8_t* s_b = reinterpret_cast<const uint8_t*>(st.s_b);
+    const uint8_t* s_sp = reinterpret_cast<const uint8_t*>(st.s_sp);
+    const uint8_t* s_dn = reinterpret_cast<const uint8_t*>(st.s_dn);
+    uint4 bf[2][FN], adn[2][FM];
+    uint2 csp[2][FM];
+    uint32_t bs[2][FN], msp[2][FM], ssp[2][FM], sdn[2][FM];
 #pragma unroll
-    for (int n = 0; n < FN; ++n) {
-      const int c = wn0 + 16 * n + lr;
-      bf[n] = S.b[slot(c, kq)];
-      bs[n] = (S.s_b[c] >> (8 * kq)) & 0xFFu;
+    for (int j = 0; j < 2; ++j) {
+      const int q = 2 * j + kh;
+#pragma unroll
+      for (int n = 0; n < FN; ++n) {
+        const int c = 32 * n + lr;
+        bf[j][n] = st.b[slot(c, q)];
+        bs[j][n] = s_b[4 * c + q];
+      }
+#pragma unroll
+      for (int f = 0; f < FM; ++f) {
+        const int r = wm0 + 32 * f + lr;
+        csp[j][f] = reinterpret_cast<const uint2*>(&st.a_sp[slot_sp(r, q >> 1)])[q & 1];
+        msp[j][f] = reinterpret_cast<const uint16_t*>(&st.meta[2 * r])[q];
+        adn[j][f] = st.a_dn[slot(r, q)];
+        ssp[j][f] = s_sp[4 * r + q];
+        sdn[j][f] = s_dn[4 * r + q];
+      }
     }
+    // ... then the loads of step s+2 into the buffer every wave finished with
+    // at step s-1 (past the end the last step is reloaded into that idle
+    // buffer, so every step issues the same loads and one wait count fits all)
+    __builtin_amdgcn_sched_barrier(0);                 // reads stay ahead of the DMA issue
+    issue(min(s + 2, KS - 1), st2);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int f = 0; f < FM; ++f) {
-      const int r = wm0 + 16 * f + lr;
-      const uint4 asp = S.a_sp[slot(r, kq)];
-      const uint4 adn = S.a_dn[slot(r, kq)];
-      const uint32_t ssp = (S.s_sp[r] >> (8 * kq)) & 0xFFu;
-      const uint32_t sdn = (S.s_dn[r] >> (8 * kq)) & 0xFFu;
+    for (int j = 0; j < 2; ++j) {
 #pragma unroll
-      for (int n = 0; n < FN; ++n) acc[f][n] = mfma_fp4(asp, bf[n], acc[f][n], ssp, bs[n]);
+      for (int f = 0; f < FM; ++f) {
+        const uint4 asp = expand4_fast(csp[j][f].x, csp[j][f].y, msp[j][f]);
 #pragma unroll
-      for (int n = 0; n < FN; ++n) acc[f][n] = mfma_fp4(adn, bf[n], acc[f][n], sdn, bs[n]);
+        for (int n = 0; n < FN; ++n) acc[f][n] = mfma32_fp4(asp, bf[j][n], acc[f][n], ssp[j][f], bs[j][n]);
+#pragma unroll
+        for (int n = 0; n < FN; ++n) acc[f][n] = mfma32_fp4(adn[j][f], bf[j][n], acc[f][n], sdn[j][f], bs[j][n]);
+      }
     }
-    if (more) store_step(st[(s + 1) & 1]);
-    __syncthreads();
+  };
+
+  issue(0, lds0);
+  issue(min(1, KS - 1), lds1);
+  // unrolled by the ring depth: every step names its buffers statically
+  for (int s = 0; s < KS; s += kNS) {
+    step(s, lds0, lds2);
+    if (s + 1 < KS) step(s + 1, lds1, lds0);
+    if (s + 2 < KS) step(s + 2, lds2, lds1);
   }
+  wait_vm_lgkm0<0>();                                  // no DMA may land after the tile ends
 
   // ---- epilogue: fp32 store of the single accumulator tile
 #pragma unroll
   for (int f = 0; f < FM; ++f) {
 #pragma unroll
     for (int n = 0; n < FN; ++n) {
-      const int c = n0 + wn0 + 16 * n + lr;
+      const int c = n0 + 32 * n + lr;
       if (c >= D) continue;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = m0 + wm0 + 16 * f + 4 * kq + i;
+      for (int i = 0; i < 16; ++i) {
+        const int r = m0 + wm0 + 32 * f + 8 * (i >> 2) + 4 * kh + (i & 3);
         if (r < row_end) Y[(int64_t)r * ldy + c] = acc[f][n][i];
       }
     }

@@ -80,22 +80,19 @@ __global__ __launch_bounds__(256, 1) void linear_nv_tile(
     brow[i] = bok[i] ? c : 0;
   }
   uint32_t pc[4], pm[4], psb[4], pd[4], psd[4], pb[4], psw[4];
+  // branch-free staging loads (rows / columns outside the tile read row 0,
+  // whose products only reach outputs that are never stored)
   auto load_step = [&](int s) {
     const int gk = s * 8 + g;                   // global group index along K
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pc[i] = 0; pm[i] = 0; psb[i] = 0; pd[i] = 0; psd[i] = 0; pb[i] = 0; psw[i] = 0;
-      if (aok[i]) {
-        pc[i] = *reinterpret_cast<const uint16_t*>(bb_codes + arow[i] * kA + 2 * (int64_t)gk);
-        pm[i] = bb_meta[arow[i] * kM + (gk >> 1)];
-        psb[i] = bb_scale[arow[i] * kS32 + (gk >> 2)];
-        pd[i] = *reinterpret_cast<const uint32_t*>(res_codes + arow[i] * kR + 4 * (int64_t)gk);
-        psd[i] = res_scale[arow[i] * kS16 + (gk >> 1)];
-      }
-      if (bok[i]) {
-        pb[i] = *reinterpret_cast<const uint32_t*>(payload + brow[i] * kR + 4 * (int64_t)gk);
-        psw[i] = wscale[brow[i] * kS32 + (gk >> 2)];
-      }
+      pc[i] = *reinterpret_cast<const uint16_t*>(bb_codes + arow[i] * kA + 2 * (int64_t)gk);
+      pm[i] = bb_meta[arow[i] * kM + (gk >> 1)];
+      psb[i] = bb_scale[arow[i] * kS32 + (gk >> 2)];
+      pd[i] = *reinterpret_cast<const uint32_t*>(res_codes + arow[i] * kR + 4 * (int64_t)gk);
+      psd[i] = res_scale[arow[i] * kS16 + (gk >> 1)];
+      pb[i] = *reinterpret_cast<const uint32_t*>(payload + brow[i] * kR + 4 * (int64_t)gk);
+      psw[i] = wscale[brow[i] * kS32 + (gk >> 2)];
     }
   };
   auto store_step = [&](NvStage& S) {
@@ -124,8 +121,8 @@ __global__ __launch_bounds__(256, 1) void linear_nv_tile(
   store_step(st[0]);
   __syncthreads();
   for (int s = 0; s < KS; ++s) {
-    const bool more = s + 1 < KS;
-    if (more) load_step(s + 1);
+    load_step(min(s + 1, KS - 1));              // the last step reloads itself (unused)
+    __builtin_amdgcn_sched_barrier(0);          // issue the prefetch before this step's MFMAs
     const NvStage& S = st[s & 1];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {             // two MFMA K-steps of 32
@@ -144,7 +141,10 @@ __global__ __launch_bounds__(256, 1) void linear_nv_tile(
         for (int n = 0; n < 4; ++n) acc_dn[f][n] = mfma_bf16(adn, bf[n], acc_dn[f][n]);
       }
     }
-    if (more) store_step(st[(s + 1) & 1]);
+    // keep the staging writes (which wait for the prefetched global loads)
+    // behind this step's MFMAs, so the load latency hides under them
+    __builtin_amdgcn_sched_barrier(0);
+    store_step(st[(s + 1) & 1]);
     __syncthreads();
   }
   const float s_sp = a_ts[0], s_dn = a_ts[1], s_w = w_ts[0];

@@ -259,3 +259,33 @@ def test_grouped_moe_full_sampled(proj):
         rows = None if mc.row_index is None else mc.row_index
         Yr, S = O.sharq_linear_sampled(ref, wref, r, c, rows=rows)
         assert_gemm_close(Yg[r, c], Yr, S)
+
+
+# ------------------------------------------------------------------ HIP graph replay
+def test_graph_replay_matches_eager():
+    # prepare + dual GEMM captured once, replayed several times with eager work
+    # and synchronizations in between; every replay must equal the eager result
+    case = synth.random_case(77, 8, 1024, 320)
+    X, g = dev_x(case), dev_gamma(case.gamma)
+    w = ops.pack_weight(dev_w(case.w, "bf16"))
+    act = ops.empty_act("mxfp4", 8, 1024)
+    Y = torch.empty((8, 320), dtype=torch.float32, device="cuda")
+    ops.prepare(X, g, 1e-6, out=act)
+    ops.linear(act, w, out=Y)
+    torch.cuda.synchronize()
+    Y_eager = Y.clone()
+    codes_eager = act.res_codes.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ops.prepare(X, g, 1e-6, out=act)
+        ops.linear(act, w, out=Y)
+    for _ in range(4):
+        Y.zero_()
+        act.res_codes.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Y_eager)
+        assert torch.equal(act.res_codes, codes_eager)
+        ops.linear(act, w)             # eager work between replays
+        torch.cuda.synchronize()
