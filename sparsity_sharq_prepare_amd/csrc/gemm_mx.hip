@@ -23,6 +23,7 @@
 //    from its compacted bytes while staging.
 #include "common.h"
 #include "kernels.h"
+#include <type_traits>
 
 namespace sharq {
 
@@ -162,22 +163,35 @@ __global__ __launch_bounds__(MT >= 8 ? 512 : 1024) void linear_mx_skinny(
 // tile kernel (prefill / grouped)
 // ============================================================================
 // Workgroup tile BM x 256 (BM = 256 plain, 128 grouped), K steps of 128, four
-// waves stacked along M (each BM/4 rows x 256 columns, so every backbone
-// fragment is expanded by exactly one wave).  Operands are staged with
-// buffer->LDS DMA (buffer_load_dword{,x4} ... lds: no staging registers, so
-// the accumulator tile fits; the per-step offset is a scalar, so issuing a
-// stage costs no vector instructions; reads past a buffer return zeros) into
-// a 3-deep LDS ring: the loads for step s+2 are in flight while step s
-// computes, with one barrier per step.  The backbone stays compacted in LDS
-// (8 bytes + 4 metadata nibbles per 32 K-values of a row) and is expanded
-// when its fragments are read.
+// waves stacked along M (each BM/4 rows x 256 columns; every backbone
+// fragment is expanded by exactly one wave), one wave per SIMD with the whole
+// accumulator tile in the 256 AGPRs.
+//
+// Staging: buffer->LDS DMA (buffer_load_dword{,x4} ... lds) into a 3-deep LDS
+// ring, no staging registers; the per-step offset is a scalar and reads past
+// a buffer return zeros.  The DMAs are issued from inline assembly: they
+// write no registers, and keeping them out of the compiler's sight stops it
+// from waiting for every in-flight DMA before each LDS read (it cannot tell
+// the ring buffers apart); completion is tracked by the explicit vmcnt waits.
+//
+// Software pipeline over K half-steps, fragments double-buffered in
+// registers: per step s, read half 1 of s | MFMAs of half 0 | wait for
+// stage s+1, barrier, read half 0 of s+1, issue stage s+3 into the buffer
+// of step s | MFMAs of half 1.  Every fragment read overlaps a group of
+// MFMAs, the loads run about two and a half steps ahead, and there is one
+// barrier per step.
+//
+// K order inside a step: lane half kh handles the 32-value blocks 2 kh and
+// 2 kh + 1 (sub-steps j = 0, 1), so its two scale bytes are one 16-bit LDS
+// read and the MFMA's op_sel picks byte j.  A, B and both paths use the same
+// order, so the sum is unchanged.
 namespace {
 
 constexpr int kBN = 256;
 constexpr int kNS = 3;                   // LDS ring depth
 
 // 16-byte slot of (row, chunk q) in a 64-byte-per-row staged tile; the XOR
-// keeps the 16 rows one fragment read touches in distinct banks
+// keeps the 16 rows of a 16-lane LDS read phase in distinct banks
 SHARQ_DEV int slot(int row, int q) { return row * 4 + (q ^ (((row >> 1) ^ (row >> 3)) & 3)); }
 // 16-byte half h of a 32-byte compacted-backbone row
 SHARQ_DEV int slot_sp(int row, int h) { return row * 2 + (h ^ ((row >> 3) & 1)); }
@@ -193,17 +207,22 @@ struct TileStage {
   uint32_t s_b[kBN];
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
+typedef int int4v __attribute__((ext_vector_type(4)));
 
-SHARQ_DEV __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+// raw buffer resource (gfx9 layout): base, num_records = bytes, no stride
+SHARQ_DEV int4v make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return (int4v){(int)(uint32_t)p, (int)((uint32_t)(p >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
 }
-// lane l of the wave writes its 16 (4) bytes at lds + 16 l (4 l)
-SHARQ_DEV void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+SHARQ_DEV uint32_t lds_addr(const void* p) { return (uint32_t)reinterpret_cast<uintptr_t>(p); }
+// lane l of the wave writes its 16 (4) bytes at LDS address lds + 16 l (4 l)
+SHARQ_DEV void dma16(int4v rs, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(soff), "{m0}"(lds)
+               : "memory");
 }
-SHARQ_DEV void dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, soff, 0, 0);
+SHARQ_DEV void dma4(int4v rs, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(soff), "{m0}"(lds)
+               : "memory");
 }
 
 // s_waitcnt vmcnt <= N, lgkmcnt 0 (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
@@ -212,6 +231,8 @@ template <int N>
 SHARQ_DEV void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
+// s_waitcnt lgkmcnt 0 only
+SHARQ_DEV void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
 // 4 groups (8 compacted bytes c_lo, c_hi + 4 nibbles of meta16) -> 16 bytes.
 // Moving i0 / i1 of every nibble to bits 3-4 of its nibble makes
@@ -227,6 +248,23 @@ SHARQ_DEV uint4 expand4_fast(uint32_t c_lo, uint32_t c_hi, uint32_t meta16) {
   return r;
 }
 
+template <int J>
+SHARQ_DEV v16f mfma32_fp4_sel(uint4 a, uint4 b, v16f c, uint32_t sa, uint32_t sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_v8i(a), as_v8i(b), c, 4, 4, J, (int)sa, J, (int)sb);
+}
+
+// register copy of one K half-step's fragments (lane half kh, sub-step J:
+// K block 2 kh + J of the step)
+template <int FM, int FN>
+struct TileFrag {
+  uint4 b[FN];
+  uint32_t bs[FN];             // scale bytes of blocks 2 kh, 2 kh + 1 (op_sel picks J)
+  uint4 dn[FM];
+  uint2 sp[FM];                // compacted backbone of the block (4 groups x 2 bytes)
+  uint32_t mt[FM];             // its 4 metadata nibbles
+  uint32_t ssp[FM], sdn[FM];
+};
+
 }  // namespace
 
 template <int BM, bool GROUPED>
@@ -237,13 +275,13 @@ __global__ __launch_bounds__(256, 1) void linear_mx_tile(
     int n_groups, const int32_t* __restrict__ group_offsets, float* __restrict__ Y, int64_t ldy) {
   using Stage = TileStage<BM>;
   constexpr int WM = BM / 4, FM = WM / 32, FN = kBN / 32;
+  using Frag = TileFrag<FM, FN>;
   // DMA instructions per wave and stage: A_dn, B, A_sp, meta, 3 scale rows
   constexpr int N_DN = BM / 64, N_B = 4, N_SP = BM / 128, N_MT = BM / 128;
   constexpr int NDMA = N_DN + N_B + N_SP + N_MT + 3;
-  // three separate typed LDS objects, indexed as arrays, so the compiler can
-  // tell the buffer being read from the buffers the in-flight DMAs write
-  __shared__ Stage lds0, lds1, lds2;
-  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+  __shared__ Stage lds[kNS];
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int tiles_n = (D + kBN - 1) / kBN;
 
   // ---- tile -> (group, first row, row end, first column)
@@ -277,13 +315,13 @@ __global__ __launch_bounds__(256, 1) void linear_mx_tile(
 
   const int KS = K >> 7;
   const uint32_t kA = K >> 2, kM = K >> 4, kS = K >> 5, kR = K >> 1;
-  const __amdgpu_buffer_rsrc_t r_dn = rsrc(res_codes, (uint32_t)act_rows * kR);
-  const __amdgpu_buffer_rsrc_t r_sp = rsrc(bb_codes, (uint32_t)act_rows * kA);
-  const __amdgpu_buffer_rsrc_t r_mt = rsrc(bb_meta, (uint32_t)act_rows * kM);
-  const __amdgpu_buffer_rsrc_t r_ssp = rsrc(bb_scale, (uint32_t)act_rows * kS);
-  const __amdgpu_buffer_rsrc_t r_sdn = rsrc(res_scale, (uint32_t)act_rows * kS);
-  const __amdgpu_buffer_rsrc_t r_b = rsrc(payload + (int64_t)grp * D * kR, (uint32_t)D * kR);
-  const __amdgpu_buffer_rsrc_t r_sb = rsrc(wscale + (int64_t)grp * D * kS, (uint32_t)D * kS);
+  const int4v r_dn = make_rsrc(res_codes, (uint32_t)act_rows * kR);
+  const int4v r_sp = make_rsrc(bb_codes, (uint32_t)act_rows * kA);
+  const int4v r_mt = make_rsrc(bb_meta, (uint32_t)act_rows * kM);
+  const int4v r_ssp = make_rsrc(bb_scale, (uint32_t)act_rows * kS);
+  const int4v r_sdn = make_rsrc(res_scale, (uint32_t)act_rows * kS);
+  const int4v r_b = make_rsrc(payload + (int64_t)grp * D * kR, (uint32_t)D * kR);
+  const int4v r_sb = make_rsrc(wscale + (int64_t)grp * D * kS, (uint32_t)D * kS);
 
   // activation row of tile row r (rows outside the tile read row 0: their
   // products reach only outputs that are never stored)
@@ -324,85 +362,99 @@ __global__ __launch_bounds__(256, 1) void linear_mx_tile(
   const int sdst = 64 * (w & (BM / 64 - 1));
 
   auto issue = [&](int s, Stage& st) {
+    const uint32_t s64 = 64u * s, s32 = 32u * s, s8 = 8u * s, s4 = 4u * s;
 #pragma unroll
-    for (int j = 0; j < N_DN; ++j) dma16(r_dn, o_dn[j], 64u * s, (uint8_t*)&st.a_dn[64 * (w + 4 * j)]);
+    for (int j = 0; j < N_DN; ++j) dma16(r_dn, o_dn[j], s64, lds_addr(&st.a_dn[64 * (w + 4 * j)]));
 #pragma unroll
-    for (int j = 0; j < N_B; ++j) dma16(r_b, o_b[j], 64u * s, (uint8_t*)&st.b[64 * (w + 4 * j)]);
+    for (int j = 0; j < N_B; ++j) dma16(r_b, o_b[j], s64, lds_addr(&st.b[64 * (w + 4 * j)]));
 #pragma unroll
-    for (int j = 0; j < N_SP; ++j) dma16(r_sp, o_sp[j], 32u * s, (uint8_t*)&st.a_sp[64 * (w + 4 * j)]);
+    for (int j = 0; j < N_SP; ++j) dma16(r_sp, o_sp[j], s32, lds_addr(&st.a_sp[64 * (w + 4 * j)]));
 #pragma unroll
-    for (int j = 0; j < N_MT; ++j) dma4(r_mt, o_mt[j], 8u * s, (uint8_t*)&st.meta[64 * (w + 4 * j)]);
-    dma4(r_ssp, o_ssp, 4u * s, (uint8_t*)&st.s_sp[sdst]);
-    dma4(r_sdn, o_ssp, 4u * s, (uint8_t*)&st.s_dn[sdst]);
-    dma4(r_sb, o_sb, 4u * s, (uint8_t*)&st.s_b[64 * w]);
+    for (int j = 0; j < N_MT; ++j) dma4(r_mt, o_mt[j], s8, lds_addr(&st.meta[64 * (w + 4 * j)]));
+    dma4(r_ssp, o_ssp, s4, lds_addr(&st.s_sp[sdst]));
+    dma4(r_sdn, o_ssp, s4, lds_addr(&st.s_dn[sdst]));
+    dma4(r_sb, o_sb, s4, lds_addr(&st.s_b[64 * w]));
   };
 
   const int wm0 = w * WM;
   const int kh = l >> 5, lr = l & 31;
+  auto read = [&](const Stage& st, Frag& F, auto jc) {
+    constexpr int J = decltype(jc)::value;
+    const uint16_t* s_b = reinterpret_cast<const uint16_t*>(st.s_b);
+    const uint16_t* s_sp = reinterpret_cast<const uint16_t*>(st.s_sp);
+    const uint16_t* s_dn = reinterpret_cast<const uint16_t*>(st.s_dn);
+    const uint2* a_sp = reinterpret_cast<const uint2*>(st.a_sp);
+    const uint16_t* meta = reinterpret_cast<const uint16_t*>(st.meta);
+#pragma unroll
+    for (int n = 0; n < FN; ++n) {
+      const int c = 32 * n + lr;
+      F.b[n] = st.b[slot(c, 2 * kh + J)];
+      F.bs[n] = s_b[2 * c + kh];
+    }
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+      const int r = wm0 + 32 * f + lr;
+      F.dn[f] = st.a_dn[slot(r, 2 * kh + J)];
+      F.sp[f] = a_sp[2 * slot_sp(r, kh) + J];
+      F.mt[f] = meta[4 * r + 2 * kh + J];
+      F.ssp[f] = s_sp[2 * r + kh];
+      F.sdn[f] = s_dn[2 * r + kh];
+    }
+  };
+
   v16f acc[FM][FN];
 #pragma unroll
   for (int f = 0; f < FM; ++f)
 #pragma unroll
     for (int n = 0; n < FN; ++n) acc[f][n] = (v16f){};
 
-  auto step = [&](int s, const Stage& st, Stage& st2) {
-    // own DMAs of step s complete (those of step s+1 stay in flight), then publish
-    wait_vm_lgkm0<NDMA>();
-    __builtin_amdgcn_s_barrier();
-    // all fragments of step s into registers first: two K sub-steps of 64,
-    // sub-step j of lane half kh reads 16-byte chunk q = 2 j + kh of a row
-    const uint8_t* s_b = reinterpret_cast<const uint8_t*>(st.s_b);
-    const uint8_t* s_sp = reinterpret_cast<const uint8_t*>(st.s_sp);
-    const uint8_t* s_dn = reinterpret_cast<const uint8_t*>(st.s_dn);
-    uint4 bf[2][FN], adn[2][FM];
-    uint2 csp[2][FM];
-    uint32_t bs[2][FN], msp[2][FM], ssp[2][FM], sdn[2][FM];
+  auto mfma_half = [&](const Frag& F, auto jc) {
+    constexpr int J = decltype(jc)::value;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int q = 2 * j + kh;
+    for (int f = 0; f < FM; ++f) {
+      const uint4 asp = expand4_fast(F.sp[f].x, F.sp[f].y, F.mt[f]);
 #pragma unroll
-      for (int n = 0; n < FN; ++n) {
-        const int c = 32 * n + lr;
-        bf[j][n] = st.b[slot(c, q)];
-        bs[j][n] = s_b[4 * c + q];
-      }
+      for (int n = 0; n < FN; ++n) acc[f][n] = mfma32_fp4_sel<J>(asp, F.b[n], acc[f][n], F.ssp[f], F.bs[n]);
 #pragma unroll
-      for (int f = 0; f < FM; ++f) {
-        const int r = wm0 + 32 * f + lr;
-        csp[j][f] = reinterpret_cast<const uint2*>(&st.a_sp[slot_sp(r, q >> 1)])[q & 1];
-        msp[j][f] = reinterpret_cast<const uint16_t*>(&st.meta[2 * r])[q];
-        adn[j][f] = st.a_dn[slot(r, q)];
-        ssp[j][f] = s_sp[4 * r + q];
-        sdn[j][f] = s_dn[4 * r + q];
-      }
-    }
-    // ... then the loads of step s+2 into the buffer every wave finished with
-    // at step s-1 (past the end the last step is reloaded into that idle
-    // buffer, so every step issues the same loads and one wait count fits all)
-    __builtin_amdgcn_sched_barrier(0);                 // reads stay ahead of the DMA issue
-    issue(min(s + 2, KS - 1), st2);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int f = 0; f < FM; ++f) {
-        const uint4 asp = expand4_fast(csp[j][f].x, csp[j][f].y, msp[j][f]);
-#pragma unroll
-        for (int n = 0; n < FN; ++n) acc[f][n] = mfma32_fp4(asp, bf[j][n], acc[f][n], ssp[j][f], bs[j][n]);
-#pragma unroll
-        for (int n = 0; n < FN; ++n) acc[f][n] = mfma32_fp4(adn[j][f], bf[j][n], acc[f][n], sdn[j][f], bs[j][n]);
-      }
+      for (int n = 0; n < FN; ++n) acc[f][n] = mfma32_fp4_sel<J>(F.dn[f], F.b[n], acc[f][n], F.sdn[f], F.bs[n]);
     }
   };
 
-  issue(0, lds0);
-  issue(min(1, KS - 1), lds1);
-  // unrolled by the ring depth: every step names its buffers statically
-  for (int s = 0; s < KS; s += kNS) {
-    step(s, lds0, lds2);
-    if (s + 1 < KS) step(s + 1, lds1, lds0);
-    if (s + 2 < KS) step(s + 2, lds2, lds1);
+  const std::integral_constant<int, 0> j0{};
+  const std::integral_constant<int, 1> j1{};
+  Frag f0, f1;
+  issue(0, lds[0]);
+  issue(min(1, KS - 1), lds[1]);
+  issue(min(2, KS - 1), lds[2]);
+  wait_vm_lgkm0<2 * NDMA>();
+  __builtin_amdgcn_s_barrier();
+  read(lds[0], f0, j0);
+  // the last step is peeled off so that the loop body is one basic block
+  // and the phase order below is the order of issue
+  for (int s = 0; s < KS - 1; ++s) {
+    Stage& cur = lds[s % kNS];
+    // the half-0 fragments were read a whole MFMA group ago; retiring them
+    // here keeps the wait for them from also covering the reads below
+    wait_lgkm0();
+    read(cur, f1, j1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_half(f0, j0);
+    __builtin_amdgcn_sched_barrier(0);
+    // stage s+1 landed (stage s+2 may be in flight) and every wave is past
+    // its reads of the buffer of step s
+    wait_vm_lgkm0<NDMA>();
+    __builtin_amdgcn_s_barrier();
+    read(lds[(s + 1) % kNS], f0, j0);
+    // past the end the last step is reloaded into the idle buffer, so every
+    // step issues the same loads and one wait count fits all
+    issue(min(s + 3, KS - 1), cur);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_half(f1, j1);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  read(lds[(KS - 1) % kNS], f1, j1);
+  mfma_half(f0, j0);
+  mfma_half(f1, j1);
   wait_vm_lgkm0<0>();                                  // no DMA may land after the tile ends
 
   // ---- epilogue: fp32 store of the single accumulator tile
