@@ -34,11 +34,16 @@ HIP_FLAGS = [
 
 SOURCES = ["prepare.hip", "pack.hip", "gemm_mx.hip", "gemm_nv.hip", "api.cpp"]
 
+# Per-file additions.  prepare.hip: IEEE mode off, so fmax/fmin take |x|
+# operands directly instead of first quieting signalling NaNs (inputs are
+# finite; a NaN input gives unspecified codes, never a fault).
+EXTRA_FLAGS = {"prepare.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *HIP_FLAGS, *lang, "-I", os.path.join(ROOT, "include"), "-c",
+    cmd = [HIPCC, *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-I", os.path.join(ROOT, "include"), "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

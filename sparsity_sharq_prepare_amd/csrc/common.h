@@ -99,6 +99,53 @@ SHARQ_DEV float sqrt_rn(float v) {
 SHARQ_DEV float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
 SHARQ_DEV uint32_t shfl_xor_u(uint32_t v, int m) { return (uint32_t)__shfl_xor((int)v, m, kWave); }
 
+// DPP lane moves inside a row of 16 lanes (every lane reads a valid lane)
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // lane i of 8 <- lane 7 - i
+constexpr int kDppRowMirror = 0x140;    // lane i of 16 <- lane 15 - i
+template <int CTRL>
+SHARQ_DEV uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+SHARQ_DEV float dpp_f(float v) { return __uint_as_float(dpp_u<CTRL>(__float_as_uint(v))); }
+
+// this lane's bit of a wave lane mask
+SHARQ_DEV bool lane_in(uint64_t mask) { return __builtin_amdgcn_inverse_ballot_w64(mask); }
+
+// max over the 4 lanes of a quad, in every lane
+SHARQ_DEV float quad_max(float v) {
+  v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
+  return fmaxf(v, dpp_f<kDppQuadXor2>(v));
+}
+
+// Sum over the 64 lanes as a pairwise tree of aligned lane blocks (1+1, 2+2,
+// ... 32+32), the same value in every lane.  Each level adds the partner
+// block's sum; within a level every lane of a block holds the same value, so
+// the mirror moves pair whole blocks like an xor would.
+SHARQ_DEV float wave_tree_sum(float v) {
+  v = __fadd_rn(v, dpp_f<kDppQuadXor1>(v));
+  v = __fadd_rn(v, dpp_f<kDppQuadXor2>(v));
+  v = __fadd_rn(v, dpp_f<kDppHalfMirror>(v));
+  v = __fadd_rn(v, dpp_f<kDppRowMirror>(v));
+  // rows 0+1 and 2+3: permlane16_swap of v with itself yields (r0 r0 r2 r2)
+  // and (r1 r1 r3 r3)
+  const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __fadd_rn(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+  // halves: (lo lo) and (hi hi)
+  const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __fadd_rn(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+}
+
+// E8M0 code (e + 127) of the smallest e in [-127, 127] with amax <= 6 * 2^e:
+// with amax = 1.m * 2^(E-127), the carry of m + (0.5 - ulp) adds one exactly
+// when m > 0.5, so (bits + 0x3FFFFF) >> 23 = E + [m > 0.5] = e + 129.
+SHARQ_DEV uint32_t e8m0_code(float amax) {
+  const uint32_t t = (__float_as_uint(amax) + 0x3FFFFFu) >> 23;
+  return (t > 2u ? t : 2u) - 2u;
+}
+
 // 4:8 in-pairs top-2 of four pair scores, ties to the lower pair: returns the
 // kept-pair bit mask (exactly two bits).  Pair p beats pair q (p < q) when
 // s_p >= s_q; a pair is kept when fewer than two pairs beat it.
@@ -118,6 +165,24 @@ SHARQ_DEV uint32_t mask_to_nibble(uint32_t km) {
   const uint64_t lut = (4ull << 12) | (8ull << 20) | (9ull << 24) | (12ull << 36) | (13ull << 40) |
                        (14ull << 48);
   return (uint32_t)(lut >> (4u * km)) & 15u;
+}
+
+// Kept pairs of every lane's group from its four pair scores (pair p beats
+// pair q > p when s_p >= s_q; a pair is kept when at most one pair beats it,
+// i.e. when it beats at least two of the other three).  The comparisons are
+// taken as wave lane masks so that the majority logic runs on the scalar
+// unit; k[p] is the lane mask of "pair p kept", i0 < i1 the kept indices.
+SHARQ_DEV void top2_lanes(float s0, float s1, float s2, float s3, uint64_t k[4], uint32_t& i0, uint32_t& i1) {
+  const uint64_t c01 = __builtin_amdgcn_ballot_w64(s0 >= s1), c02 = __builtin_amdgcn_ballot_w64(s0 >= s2);
+  const uint64_t c03 = __builtin_amdgcn_ballot_w64(s0 >= s3), c12 = __builtin_amdgcn_ballot_w64(s1 >= s2);
+  const uint64_t c13 = __builtin_amdgcn_ballot_w64(s1 >= s3), c23 = __builtin_amdgcn_ballot_w64(s2 >= s3);
+  // majority of three: (a & b) | (c & (a | b))
+  k[0] = (c01 & c02) | (c03 & (c01 | c02));
+  k[1] = (~c01 & c12) | (c13 & (~c01 | c12));
+  k[2] = (~c02 & ~c12) | (c23 & (~c02 | ~c12));
+  k[3] = (~c03 & ~c13) | (~c23 & (~c03 | ~c13));
+  i0 = lane_in(k[0]) ? 0u : (lane_in(k[1]) ? 1u : 2u);
+  i1 = lane_in(k[3]) ? 3u : (lane_in(k[2]) ? 2u : 1u);
 }
 
 // Expand the two kept pair-bytes of one group (byte0, byte1 of `two`) into the

@@ -57,6 +57,20 @@ SHARQ_DEV uint4 expand4(uint32_t c_lo, uint32_t c_hi, uint32_t meta16) {
   return r;
 }
 
+// 4 groups (8 compacted bytes c_lo, c_hi + 4 nibbles of meta16) -> 16 bytes.
+// Moving i0 / i1 of every nibble to bits 3-4 of its nibble makes
+// (m >> 4g) & 0x18 the byte shift 8 * i of group g.
+SHARQ_DEV uint4 expand4_fast(uint32_t c_lo, uint32_t c_hi, uint32_t meta16) {
+  const uint32_t m0 = (meta16 & 0x3333u) << 3;        // 8 * i0 at bits 4g + 3 .. 4g + 4
+  const uint32_t m1 = (meta16 & 0xCCCCu) << 1;        // 8 * i1
+  uint4 r;
+  r.x = ((c_lo & 0xFFu) << (m0 & 0x18u)) | (((c_lo >> 8) & 0xFFu) << (m1 & 0x18u));
+  r.y = (((c_lo >> 16) & 0xFFu) << ((m0 >> 4) & 0x18u)) | ((c_lo >> 24) << ((m1 >> 4) & 0x18u));
+  r.z = ((c_hi & 0xFFu) << ((m0 >> 8) & 0x18u)) | (((c_hi >> 8) & 0xFFu) << ((m1 >> 8) & 0x18u));
+  r.w = (((c_hi >> 16) & 0xFFu) << ((m0 >> 12) & 0x18u)) | ((c_hi >> 24) << ((m1 >> 12) & 0x18u));
+  return r;
+}
+
 }  // namespace
 
 // ============================================================================
@@ -160,6 +174,156 @@ __global__ __launch_bounds__(MT >= 8 ? 512 : 1024) void linear_mx_skinny(
 }
 
 // ============================================================================
+// decode kernel (at most 8 activation rows)
+// ============================================================================
+// One 16x16x128 MFMA per 128-wide K-step: MFMA rows 0-7 are the backbone of
+// tokens 0-7, rows 8-15 their residual, so one accumulator holds both paths
+// and the epilogue adds row t and row t + 8.
+//
+// The workgroup stages the activation side in LDS: for 32-block kb and MFMA
+// row r the 16 code bytes (backbone expanded from its compacted pairs) sit in
+// slot 16 kb + r, the scale in byte 16 kb + r.  Its loads (L2 hits) are
+// issued first, then wave w issues the loads of the weight bytes of its J
+// consecutive K-steps from J w (lane l: column 16 blockIdx.x + (l & 15),
+// 32-block 4 s + (l >> 4)) and of their scales (one 16-byte load per four
+// steps); the LDS writes wait only for the earlier activation loads, so the
+// weight stream is in flight meanwhile.  All global loads are raw buffer
+// loads; absent tokens, columns and steps get an offset past the buffer and
+// read zero.
+//
+// grid.x = ceil(D / 16), 64 NW threads, NW J >= K / 128.
+constexpr int kDecodeMaxK = 16384;                   // staged operand + reduction fit in LDS
+
+template <int NK, int CG, int J>
+__global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
+    const uint8_t* __restrict__ bb_codes, const uint8_t* __restrict__ bb_meta, const uint8_t* __restrict__ bb_scale,
+    const uint8_t* __restrict__ res_codes, const uint8_t* __restrict__ res_scale, const int32_t* __restrict__ row_index,
+    int rows, int act_rows, int K, const uint8_t* __restrict__ payload, const uint8_t* __restrict__ wscale, int D,
+    float* __restrict__ Y, int64_t ldy) {
+  static_assert(J % 4 == 0, "weight scales load four steps at a time");
+  constexpr int NW = NK * CG;                          // K-splits x column groups
+  extern __shared__ uint4 dsm[];
+  constexpr uint32_t kOut = 0x80000000u;             // offset past every buffer here: reads zero
+  constexpr int NT = NW * 64;
+  const int KB = K >> 5, KS = K >> 7;
+  uint4* const a_sm = dsm;                                            // [KB + 1][16]
+  uint8_t* const s_sm = reinterpret_cast<uint8_t*>(dsm + (KB + 1) * 16);   // [KB + 1][16]
+  float* const red = reinterpret_cast<float*>(dsm + (KB + 1) * 17);   // [NW][64][4]
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+  auto rsrc = [](const uint8_t* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0,
+                                             __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
+  };
+
+  // ---- activation loads first (L2 hits): item i is block i >> 3 of token
+  // i & 7; a thread always serves token tid & 7 and at most IPT = J / (2 CG)
+  // items (NK J >= K / 128 gives 8 K / 32 <= 64 NW IPT)
+  constexpr int IPT = (J / (2 * CG)) > 0 ? J / (2 * CG) : 1;
+  const int t = tid & 7;
+  const bool t_ok = t < rows;
+  const uint32_t ar = t_ok ? (uint32_t)gather_row(row_index, t, act_rows) : 0u;
+  const int n_item = 8 * KB;
+  uint4 sv[IPT];
+  uint2 sc[IPT];
+  uint32_t srs[IPT], sm[IPT], sbs[IPT];
+  {
+    const int an = __builtin_amdgcn_readfirstlane(act_rows);
+    const __amdgpu_buffer_rsrc_t r_rc = rsrc(res_codes, (int64_t)an * (K >> 1));
+    const __amdgpu_buffer_rsrc_t r_rs = rsrc(res_scale, (int64_t)an * (K >> 5));
+    const __amdgpu_buffer_rsrc_t r_bc = rsrc(bb_codes, (int64_t)an * (K >> 2));
+    const __amdgpu_buffer_rsrc_t r_bm = rsrc(bb_meta, (int64_t)an * (K >> 4));
+    const __amdgpu_buffer_rsrc_t r_bs = rsrc(bb_scale, (int64_t)an * (K >> 5));
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const int i = tid + NT * j, kb = i >> 3;
+      const uint32_t out = i < n_item && t_ok ? 0u : kOut;
+      const auto cr = __builtin_amdgcn_raw_buffer_load_b128(r_rc, (ar * (uint32_t)(K >> 1) + 16u * kb) | out, 0, 0);
+      sv[j] = make_uint4(cr[0], cr[1], cr[2], cr[3]);
+      srs[j] = __builtin_amdgcn_raw_buffer_load_b8(r_rs, (ar * (uint32_t)(K >> 5) + kb) | out, 0, 0);
+      const auto cb = __builtin_amdgcn_raw_buffer_load_b64(r_bc, (ar * (uint32_t)(K >> 2) + 8u * kb) | out, 0, 0);
+      sc[j] = make_uint2(cb[0], cb[1]);
+      sm[j] = __builtin_amdgcn_raw_buffer_load_b16(r_bm, (ar * (uint32_t)(K >> 4) + 2u * kb) | out, 0, 0);
+      sbs[j] = __builtin_amdgcn_raw_buffer_load_b8(r_bs, (ar * (uint32_t)(K >> 5) + kb) | out, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- weight loads of this wave's steps (column group cg, K-split kw)
+  const int cg = w % CG, kw = w / CG;
+  const int col = (blockIdx.x * CG + cg) * 16 + (l & 15);
+  const int kq = l >> 4;
+  const int s0 = kw * J;
+  const __amdgpu_buffer_rsrc_t r_w = rsrc(payload, (int64_t)D * (K >> 1));
+  const __amdgpu_buffer_rsrc_t r_ws = rsrc(wscale, (int64_t)D * (K >> 5));
+  const uint32_t o_w = col < D ? (uint32_t)col * (uint32_t)(K >> 1) + 16u * kq : kOut;
+  const uint32_t o_ws = col < D ? (uint32_t)col * (uint32_t)(K >> 5) : kOut;
+  uint4 wv[J];
+  uint32_t wsd[J];                                    // dword j: scales of step s0 + j (byte kq)
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t out = s0 + j < KS ? 0u : kOut;
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r_w, (o_w + 64u * (uint32_t)(s0 + j)) | out, 0, 0);
+    wv[j] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+#pragma unroll
+  for (int j = 0; j < J; j += 4) {
+    // 16 bytes = blocks 4 (s0 + j) .. 4 (s0 + j + 4) - 1; past the row's end
+    // only scales of zero-weight steps are affected
+    const uint32_t out = s0 + j < KS ? 0u : kOut;
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r_ws, (o_ws + 4u * (uint32_t)(s0 + j)) | out, 0, 0);
+    wsd[j] = v[0]; wsd[j + 1] = v[1]; wsd[j + 2] = v[2]; wsd[j + 3] = v[3];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- activation operand into LDS (waits only for the activation loads,
+  // which were issued first)
+  // (unconditional: items past the end go to the spare block row KB, so no
+  // load is sunk behind the weight loads into a conditional block)
+#pragma unroll
+  for (int j = 0; j < IPT; ++j) {
+    const int i = tid + NT * j, kb = i < n_item ? i >> 3 : KB;
+    a_sm[16 * kb + 8 + t] = sv[j];
+    s_sm[16 * kb + 8 + t] = (uint8_t)srs[j];
+    a_sm[16 * kb + t] = expand4_fast(sc[j].x, sc[j].y, sm[j]);
+    s_sm[16 * kb + t] = (uint8_t)sbs[j];
+  }
+  __syncthreads();
+
+  // ---- MFMAs (steps past K carry zero weights; their LDS slot is clamped)
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int s = s0 + j < KS ? s0 + j : KS - 1;
+    const int e = 64 * s + l;                        // = 16 (4 s + kq) + (l & 15)
+    acc = mfma_fp4(a_sm[e], wv[j], acc, s_sm[e], (wsd[j] >> (8 * kq)) & 0xFFu);
+  }
+
+  // ---- fixed-order reduction over the waves; backbone row + residual row
+  {
+    float* p = red + (w * 64 + l) * 4;
+    p[0] = acc[0]; p[1] = acc[1]; p[2] = acc[2]; p[3] = acc[3];
+  }
+  __syncthreads();
+  if (kw == 0 && l < 32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float bsum = 0.0f, rsum = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const int ww = kk * CG + cg;
+        bsum += red[(ww * 64 + l) * 4 + i];
+        rsum += red[(ww * 64 + l + 32) * 4 + i];
+      }
+      // lane l < 32 holds MFMA rows 4 (l >> 4) + i (backbone of tokens 0-7);
+      // lane l + 32 holds rows 8 + 4 (l >> 4) + i (their residual)
+      const int t = 4 * (l >> 4) + i;
+      if (t < rows && col < D) Y[(int64_t)t * ldy + col] = bsum + rsum;
+    }
+  }
+}
+
+// ============================================================================
 // tile kernel (prefill / grouped)
 // ============================================================================
 // Workgroup tile BM x 256 (BM = 256 plain, 128 grouped), K steps of 128, four
@@ -234,19 +398,6 @@ SHARQ_DEV void wait_vm_lgkm0() {
 // s_waitcnt lgkmcnt 0 only
 SHARQ_DEV void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
-// 4 groups (8 compacted bytes c_lo, c_hi + 4 nibbles of meta16) -> 16 bytes.
-// Moving i0 / i1 of every nibble to bits 3-4 of its nibble makes
-// (m >> 4g) & 0x18 the byte shift 8 * i of group g.
-SHARQ_DEV uint4 expand4_fast(uint32_t c_lo, uint32_t c_hi, uint32_t meta16) {
-  const uint32_t m0 = (meta16 & 0x3333u) << 3;        // 8 * i0 at bits 4g + 3 .. 4g + 4
-  const uint32_t m1 = (meta16 & 0xCCCCu) << 1;        // 8 * i1
-  uint4 r;
-  r.x = ((c_lo & 0xFFu) << (m0 & 0x18u)) | (((c_lo >> 8) & 0xFFu) << (m1 & 0x18u));
-  r.y = (((c_lo >> 16) & 0xFFu) << ((m0 >> 4) & 0x18u)) | ((c_lo >> 24) << ((m1 >> 4) & 0x18u));
-  r.z = ((c_hi & 0xFFu) << ((m0 >> 8) & 0x18u)) | (((c_hi >> 8) & 0xFFu) << ((m1 >> 8) & 0x18u));
-  r.w = (((c_hi >> 16) & 0xFFu) << ((m0 >> 12) & 0x18u)) | ((c_hi >> 24) << ((m1 >> 12) & 0x18u));
-  return r;
-}
 
 template <int J>
 SHARQ_DEV v16f mfma32_fp4_sel(uint4 a, uint4 b, v16f c, uint32_t sa, uint32_t sb) {
@@ -481,6 +632,43 @@ hipError_t launch_linear_mx(const uint8_t* bb_codes, const uint8_t* bb_meta, con
                             int act_rows, int K, const uint8_t* payload, const uint8_t* wscale, int D, int n_groups,
                             const int32_t* group_offsets, float* Y, int64_t ldy, hipStream_t s) {
   if (rows == 0) return hipSuccess;
+  if (n_groups == 1 && rows <= 8 && K <= kDecodeMaxK) {
+    // J = 4 K-steps per wave while 16 K-splits suffice, else 8; column groups
+    // of 16 per workgroup while at least 256 workgroups remain and the
+    // workgroup stays within 16 waves
+    const int KS = K / 128;
+    const int J = KS <= 64 ? 4 : 8;
+    int NK = 1;
+    while (NK * J < KS) NK *= 2;
+    int CG = 1;
+    while (NK * CG * 2 <= 16 && (D + 16 * CG * 2 - 1) / (16 * CG * 2) >= 256) CG *= 2;
+    const size_t lds = (size_t)(K / 32 + 1) * 17 * 16 + (size_t)NK * CG * 64 * 4 * sizeof(float);
+    dim3 grid((D + 16 * CG - 1) / (16 * CG)), block(64 * NK * CG);
+#define L(NK_, CG_, J_)                                                                                                 \
+  hipLaunchKernelGGL((linear_mx_decode<NK_, CG_, J_>), grid, block, lds, s, bb_codes, bb_meta, bb_scale, res_codes,      \
+                     res_scale, row_index, rows, act_rows, K, payload, wscale, D, Y, ldy)
+    switch (J * 10000 + NK * 100 + CG) {
+      case 40101: L(1, 1, 4); break;
+      case 40102: L(1, 2, 4); break;
+      case 40104: L(1, 4, 4); break;
+      case 40108: L(1, 8, 4); break;
+      case 40116: L(1, 16, 4); break;
+      case 40201: L(2, 1, 4); break;
+      case 40202: L(2, 2, 4); break;
+      case 40204: L(2, 4, 4); break;
+      case 40208: L(2, 8, 4); break;
+      case 40401: L(4, 1, 4); break;
+      case 40402: L(4, 2, 4); break;
+      case 40404: L(4, 4, 4); break;
+      case 40801: L(8, 1, 4); break;
+      case 40802: L(8, 2, 4); break;
+      case 41601: L(16, 1, 4); break;
+      case 81601: L(16, 1, 8); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef L
+    return hipGetLastError();
+  }
   if (n_groups == 1 && rows <= 64) {
     const int KS = K / 128;
     const int mt = (rows + 7) / 8;

@@ -90,9 +90,7 @@ SHARQ_DEV float row_inv_rms(const RowRegs<TPR, MAXC, BF16>& rr, int K, float eps
   for (int c = 0; c < MAXC; ++c) {
     float x[8];
     rr.get(c, x);
-    part[c] = tree8_sq(x);             // zeros beyond K contribute +0
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) part[c] = __fadd_rn(part[c], shfl_xor_f(part[c], m));
+    part[c] = wave_tree_sum(tree8_sq(x));   // zeros beyond K contribute +0
   }
   if (WPR > 1) {
     const int w = t / kWave;
@@ -103,9 +101,17 @@ SHARQ_DEV float row_inv_rms(const RowRegs<TPR, MAXC, BF16>& rr, int K, float eps
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
+      // pairwise tree over the row's waves (aligned wave blocks, in order)
       const float* r = red + (rsub * MAXC + c) * WPR;
-      part[c] = WPR == 2 ? __fadd_rn(r[0], r[1])
-                         : __fadd_rn(__fadd_rn(r[0], r[1]), __fadd_rn(r[2], r[3]));
+      float v[WPR];
+#pragma unroll
+      for (int i = 0; i < WPR; ++i) v[i] = r[i];
+#pragma unroll
+      for (int n = WPR / 2; n >= 1; n >>= 1) {
+#pragma unroll
+        for (int i = 0; i < n; ++i) v[i] = __fadd_rn(v[2 * i], v[2 * i + 1]);
+      }
+      part[c] = v[0];
     }
   }
 #pragma unroll
@@ -143,97 +149,184 @@ SHARQ_DEV uint32_t select_kept(uint32_t word, uint32_t nib) {
   return ((word >> (8u * i0)) & 0xFFu) | (((word >> (8u * i1)) & 0xFFu) << 8);
 }
 
-SHARQ_DEV float quad_max(float v) {
-  v = fmaxf(v, shfl_xor_f(v, 1));
-  return fmaxf(v, shfl_xor_f(v, 2));
-}
-
-SHARQ_DEV void store_meta_scales(uint8_t* meta_row, uint8_t* sb_row, uint8_t* sr_row, int g, uint32_t nib,
-                                 uint32_t sb, uint32_t sr, bool ok, int res_per_group) {
-  const uint32_t other = shfl_xor_u(nib, 1);
-  if (!ok) return;
-  if ((g & 1) == 0) meta_row[g >> 1] = (uint8_t)(nib | (other << 4));
-  if ((g & 3) == 0) sb_row[g >> 2] = (uint8_t)sb;
-  if (res_per_group == 1) {               // MXFP4: one residual scale per 32
-    if ((g & 3) == 0) sr_row[g >> 2] = (uint8_t)sr;
-  } else {                                 // NVFP4: one residual scale per 16
-    if ((g & 1) == 0) sr_row[g >> 1] = (uint8_t)sr;
-  }
-}
-
 }  // namespace
 
 // ============================================================================
 // MXFP4: one pass
 // ============================================================================
-template <int TPR, int MAXC, bool BF16>
-__global__ __launch_bounds__(256) void prepare_mx_kernel(const void* __restrict__ X, int T, int K, int64_t ldx,
+// Per group of 8 (one lane): normalize, pair scores, kept pair indices, then
+// per 32-value block (the 4 lanes of a quad) the backbone scale, the codes of
+// all four pairs (the kept two are compacted with one byte permute), the exact
+// residual (y minus the dequantized kept pairs, y itself on dropped pairs) and
+// its codes.  Metadata nibbles and scales of a block are gathered into the
+// quad's first lane and stored from there.
+//
+// Workgroups loop over blocks of RPW rows (block b, b + grid, ...).  gamma of
+// the thread's groups is read once, and the next block's rows are loaded while
+// the current block is quantized, so HBM reads, the arithmetic and the stores
+// of different rows overlap inside every wave.
+template <int TPR, int MAXC, bool BF16, bool NORM>
+struct MxRowPass {
+  static constexpr int WGT = TPR > 256 ? TPR : 256;  // threads per workgroup
+  static constexpr int RPW = WGT / TPR, WPR = TPR / kWave;
+  static constexpr int RED = RPW * MAXC * WPR;      // LDS floats per parity
+  // gamma staged in LDS once per workgroup when the padded row fits in 32 KB,
+  // else read from global memory per chunk
+  static constexpr bool GLDS = NORM && TPR * MAXC * 8 * 4 <= 32768;
+  static constexpr int GSM = GLDS ? TPR * MAXC * 2 : 1;   // float4s
+  // the next rows are prefetched into registers when two row copies fit
+  static constexpr bool CACHE = 2 * MAXC * (BF16 ? 4 : 8) <= 64;
+
+  const float* gp;
+  const float4* gs;
+
+  // every thread of the workgroup calls this (it ends with a barrier)
+  SHARQ_DEV void load_gamma(const float* gamma, int K, float4* gsm) {
+    gp = gamma;
+    gs = gsm;
+    if (!GLDS) return;
+    for (int i = threadIdx.x; i < GSM; i += WGT)
+      gsm[i] = 4 * i < K ? *reinterpret_cast<const float4*>(gamma + 4 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
+  }
+
+  SHARQ_DEV void run(const RowRegs<TPR, MAXC, BF16>& rr, int row, bool row_ok, int K, float eps, int t, int rsub,
+                     float* red, uint8_t* bb_codes, uint8_t* bb_meta, uint8_t* bb_scale, uint8_t* res_codes,
+                     uint8_t* res_scale) const {
+    const int G = K >> 3;
+    const float inv = NORM ? row_inv_rms<TPR, MAXC, BF16>(rr, K, eps, t, rsub, red) : 1.0f;
+    const int64_t r = __builtin_amdgcn_readfirstlane(row_ok ? row : 0);   // uniform per wave
+    uint8_t* const meta_row = bb_meta + r * (K >> 4);
+    uint8_t* const sb_row = bb_scale + r * (K >> 5);
+    uint8_t* const sr_row = res_scale + r * (K >> 5);
+    uint8_t* const bc_row = bb_codes + r * (K >> 2);
+    uint8_t* const rc_row = res_codes + r * (K >> 1);
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const uint32_t g = (uint32_t)(c * TPR + t);
+      if (c * TPR >= G) break;                       // whole chunk beyond the row (uniform)
+      const bool ok = row_ok && g < (uint32_t)G;
+      float y[8];
+      rr.get(c, y);
+      if (NORM) {
+        float4 ga, gb;
+        if (GLDS) {
+          ga = gs[2 * g];
+          gb = gs[2 * g + 1];
+        } else {
+          const uint32_t k0 = ok ? 8u * g : 0u;      // lanes past K hold zeros
+          ga = *reinterpret_cast<const float4*>(gp + k0);
+          gb = *reinterpret_cast<const float4*>(gp + k0 + 4);
+        }
+        const float gm[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = __fmul_rn(__fmul_rn(y[i], inv), gm[i]);
+      }
+      // ---- pair scores, kept pairs, backbone scale
+      const float s0 = fmaxf(fabsf(y[0]), fabsf(y[1]));
+      const float s1 = fmaxf(fabsf(y[2]), fabsf(y[3]));
+      const float s2 = fmaxf(fabsf(y[4]), fabsf(y[5]));
+      const float s3 = fmaxf(fabsf(y[6]), fabsf(y[7]));
+      uint64_t kp[4];
+      uint32_t i0, i1;
+      top2_lanes(s0, s1, s2, s3, kp, i0, i1);
+      const uint32_t eb = e8m0_code(quad_max(fmaxf(fmaxf(s0, s1), fmaxf(s2, s3))));
+      const float s_bb = exp2i((int)eb - 127);
+      uint32_t bw = 0;
+      bw = cvt_fp4x2<0>(bw, y[0], y[1], s_bb);
+      bw = cvt_fp4x2<1>(bw, y[2], y[3], s_bb);
+      bw = cvt_fp4x2<2>(bw, y[4], y[5], s_bb);
+      bw = cvt_fp4x2<3>(bw, y[6], y[7], s_bb);
+      // ---- residual R = y - X~_sp (exact), X~_sp = 0 on dropped pairs
+      float R[8];
+      {
+        const v2f d[4] = {dq_fp4x2<0>(bw, s_bb), dq_fp4x2<1>(bw, s_bb), dq_fp4x2<2>(bw, s_bb),
+                          dq_fp4x2<3>(bw, s_bb)};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const bool kept = lane_in(kp[p]);
+          R[2 * p] = __fsub_rn(y[2 * p], kept ? d[p].x : 0.0f);
+          R[2 * p + 1] = __fsub_rn(y[2 * p + 1], kept ? d[p].y : 0.0f);
+        }
+      }
+      const float rmax = fmaxf(fmaxf(fmaxf(fabsf(R[0]), fabsf(R[1])), fmaxf(fabsf(R[2]), fabsf(R[3]))),
+                               fmaxf(fmaxf(fabsf(R[4]), fabsf(R[5])), fmaxf(fabsf(R[6]), fabsf(R[7]))));
+      const uint32_t er = e8m0_code(quad_max(rmax));
+      const float s_r = exp2i((int)er - 127);
+      uint32_t rw = 0;
+      rw = cvt_fp4x2<0>(rw, R[0], R[1], s_r);
+      rw = cvt_fp4x2<1>(rw, R[2], R[3], s_r);
+      rw = cvt_fp4x2<2>(rw, R[4], R[5], s_r);
+      rw = cvt_fp4x2<3>(rw, R[6], R[7], s_r);
+      // ---- compacted kept pair bytes (byte permute; selector 0x0C reads zero)
+      const uint32_t kept2 = __builtin_amdgcn_perm(0u, bw, i0 | (i1 << 8) | 0x0C0C0000u);
+      // metadata of the quad's 4 groups as 16 bits in its first lane
+      const uint32_t nib = i0 | (i1 << 2);
+      const uint32_t b8 = nib | (dpp_u<kDppQuadXor1>(nib) << 4);
+      const uint32_t m16 = (b8 & 0xFFu) | (dpp_u<kDppQuadXor2>(b8) << 8);
+      if (ok) {
+        *reinterpret_cast<uint16_t*>(bc_row + 2 * g) = (uint16_t)kept2;
+        *reinterpret_cast<uint32_t*>(rc_row + 4 * g) = rw;
+        if ((g & 3) == 0) {
+          *reinterpret_cast<uint16_t*>(meta_row + (g >> 1)) = (uint16_t)m16;
+          sb_row[g >> 2] = (uint8_t)eb;
+          sr_row[g >> 2] = (uint8_t)er;
+        }
+      }
+    }
+  }
+};
+
+template <int TPR, int MAXC, bool BF16, bool NORM>
+__global__ __launch_bounds__(TPR > 256 ? TPR : 256) void prepare_mx_kernel(const void* __restrict__ X, int T, int K, int64_t ldx,
                                                          const float* __restrict__ gamma, float eps,
                                                          uint8_t* __restrict__ bb_codes, uint8_t* __restrict__ bb_meta,
                                                          uint8_t* __restrict__ bb_scale,
                                                          uint8_t* __restrict__ res_codes,
                                                          uint8_t* __restrict__ res_scale) {
-  constexpr int RPW = 256 / TPR;
-  __shared__ float red[RPW * MAXC * (TPR / kWave)];
+  using Pass = MxRowPass<TPR, MAXC, BF16, NORM>;
+  constexpr int RPW = Pass::RPW;
+  // two parities: a block's cross-wave partial sums are read before the
+  // barrier of the next block, so the block after next may overwrite them
+  __shared__ float red[2 * Pass::RED];
+  __shared__ float4 gsm[Pass::GSM];
   const int tid = threadIdx.x;
-  const int rsub = tid / TPR, t = tid % TPR;
-  const int row = blockIdx.x * RPW + rsub;
-  const bool row_ok = row < T;
+  const int rsub = __builtin_amdgcn_readfirstlane(tid / TPR);   // TPR is a multiple of the wave
+  const int t = tid % TPR;
   const int G = K >> 3;
+  const int nblk = (T + RPW - 1) / RPW;
 
-  RowRegs<TPR, MAXC, BF16> rr;
-  rr.load(X, (int64_t)(row_ok ? row : 0) * ldx, G, t, row_ok);
-  const float inv = gamma ? row_inv_rms<TPR, MAXC, BF16>(rr, K, eps, t, rsub, red) : 1.0f;
-
-  const int64_t r = row_ok ? row : 0;
-  uint8_t* meta_row = bb_meta + r * (K >> 4);
-  uint8_t* sb_row = bb_scale + r * (K >> 5);
-  uint8_t* sr_row = res_scale + r * (K >> 5);
-#pragma unroll
-  for (int c = 0; c < MAXC; ++c) {
-    const int g = c * TPR + t;
-    if (c * TPR >= G) break;                       // whole chunk beyond the row (uniform)
-    const bool ok = row_ok && g < G;
-    float y[8];
-    rr.get(c, y);
-    if (ok) normalize(y, inv, gamma, 8 * (int64_t)g);
-    // ---- 4:8 in-pairs mask and backbone scale (block = 4 groups = 4 lanes)
-    float gmax;
-    const uint32_t km = group_mask(y, gmax);
-    const uint32_t nib = mask_to_nibble(km);
-    const int e_bb = e8m0_exponent(quad_max(gmax));
-    const float s_bb = exp2i(e_bb);
-    // ---- backbone codes of all four pairs (only kept ones are stored)
-    uint32_t bw = 0;
-    bw = cvt_fp4x2<0>(bw, y[0], y[1], s_bb);
-    bw = cvt_fp4x2<1>(bw, y[2], y[3], s_bb);
-    bw = cvt_fp4x2<2>(bw, y[4], y[5], s_bb);
-    bw = cvt_fp4x2<3>(bw, y[6], y[7], s_bb);
-    // ---- residual R = y - X~_sp (exact), X~_sp = 0 on dropped pairs
-    float R[8];
-    {
-      const v2f d0 = dq_fp4x2<0>(bw, s_bb), d1 = dq_fp4x2<1>(bw, s_bb);
-      const v2f d2 = dq_fp4x2<2>(bw, s_bb), d3 = dq_fp4x2<3>(bw, s_bb);
-      const float xt[8] = {d0.x, d0.y, d1.x, d1.y, d2.x, d2.y, d3.x, d3.y};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) R[i] = ((km >> (i >> 1)) & 1u) ? __fsub_rn(y[i], xt[i]) : y[i];
+  Pass pass;
+  pass.load_gamma(gamma, K, gsm);
+  RowRegs<TPR, MAXC, BF16> ra, rb;
+  auto load = [&](RowRegs<TPR, MAXC, BF16>& rr, int blk) {
+    const int row = blk * RPW + rsub;
+    const bool ok = blk < nblk && row < T;
+    rr.load(X, (int64_t)(ok ? row : 0) * ldx, G, t, ok);
+  };
+  auto step = [&](const RowRegs<TPR, MAXC, BF16>& cur, RowRegs<TPR, MAXC, BF16>& nxt, int blk, int par) {
+    load(nxt, blk + (int)gridDim.x);
+    const int row = blk * RPW + rsub;
+    pass.run(cur, row, row < T, K, eps, t, rsub, red + par * Pass::RED, bb_codes, bb_meta, bb_scale, res_codes,
+             res_scale);
+  };
+  int blk = blockIdx.x;
+  if (Pass::CACHE) {
+    load(ra, blk);
+    while (blk < nblk) {
+      step(ra, rb, blk, 0);
+      blk += gridDim.x;
+      if (blk >= nblk) break;
+      step(rb, ra, blk, 1);
+      blk += gridDim.x;
     }
-    float rmax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) rmax = fmaxf(rmax, fabsf(R[i]));
-    const int e_r = e8m0_exponent(quad_max(rmax));
-    const float s_r = exp2i(e_r);
-    uint32_t rw = 0;
-    rw = cvt_fp4x2<0>(rw, R[0], R[1], s_r);
-    rw = cvt_fp4x2<1>(rw, R[2], R[3], s_r);
-    rw = cvt_fp4x2<2>(rw, R[4], R[5], s_r);
-    rw = cvt_fp4x2<3>(rw, R[6], R[7], s_r);
-    // ---- stores
-    if (ok) {
-      *reinterpret_cast<uint16_t*>(bb_codes + r * (K >> 2) + 2 * (int64_t)g) = (uint16_t)select_kept(bw, nib);
-      *reinterpret_cast<uint32_t*>(res_codes + r * (K >> 1) + 4 * (int64_t)g) = rw;
+  } else {
+    for (int par = 0; blk < nblk; blk += gridDim.x, par ^= 1) {
+      load(ra, blk);
+      const int row = blk * RPW + rsub;
+      pass.run(ra, row, row < T, K, eps, t, rsub, red + par * Pass::RED, bb_codes, bb_meta, bb_scale, res_codes,
+               res_scale);
     }
-    store_meta_scales(meta_row, sb_row, sr_row, g, nib, (uint32_t)(e_bb + 127), (uint32_t)(e_r + 127), ok, 1);
   }
 }
 
@@ -406,7 +499,21 @@ namespace {
 
 struct PrepGeom {
   int tpr, maxc, rpw, blocks;
+  int threads = 256;
 };
+
+// compute units of the current device (queried once per device)
+int num_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 PrepGeom prep_geometry(int T, int K) {
   const int G = K / 8;
@@ -437,6 +544,55 @@ PrepGeom prep_geometry(int T, int K) {
     default: return hipErrorInvalidValue;                                 \
   }
 
+// MXFP4 kernel: up to 4 groups per thread before the row is spread over more
+// threads, so per-row work (1/rms) is shared by several groups
+PrepGeom prep_geometry_mx(int T, int K) {
+  const int G = K / 8;
+  // Few rows (decode): a row spreads over up to 16 waves (one workgroup), one
+  // group of 8 per thread where possible, to shorten its dependent chain.
+  // Many rows: one wave per row and up to 8 groups per thread, so the
+  // per-row work (1/rms) is shared by more groups and no cross-wave
+  // reduction is needed.
+  const bool wide = (int64_t)T * G < (int64_t)1024 * 64 * 8;
+  int tpr = 64;
+  if (wide) {
+    while (tpr < 1024 && tpr < G) tpr *= 2;
+  } else {
+    while (tpr < 256 && tpr * 8 < G) tpr *= 2;
+  }
+  const int nc = (G + tpr - 1) / tpr;
+  int maxc = 1;
+  while (maxc < nc) maxc *= 2;
+  PrepGeom g;
+  g.tpr = tpr;
+  g.maxc = maxc;
+  g.threads = tpr > 256 ? tpr : 256;
+  g.rpw = g.threads / tpr;
+  const int nblk = (T + g.rpw - 1) / g.rpw;
+  // two workgroups of four waves per CU (two waves per SIMD), each looping
+  // over row blocks
+  g.blocks = nblk < 2 * num_cus() ? nblk : 2 * num_cus();
+  return g;
+}
+
+#define SHARQ_PREP_MX_DISPATCH(MACRO)                                     \
+  switch (g.tpr * 100 + g.maxc) {                                         \
+    case 6401: MACRO(64, 1); break;                                       \
+    case 6402: MACRO(64, 2); break;                                       \
+    case 6404: MACRO(64, 4); break;                                       \
+    case 6408: MACRO(64, 8); break;                                       \
+    case 12801: MACRO(128, 1); break;                                     \
+    case 12808: MACRO(128, 8); break;                                     \
+    case 25601: MACRO(256, 1); break;                                     \
+    case 25608: MACRO(256, 8); break;                                     \
+    case 25616: MACRO(256, 16); break;                                    \
+    case 51201: MACRO(512, 1); break;                                     \
+    case 102401: MACRO(1024, 1); break;                                   \
+    case 102402: MACRO(1024, 2); break;                                   \
+    case 102404: MACRO(1024, 4); break;                                   \
+    default: return hipErrorInvalidValue;                                 \
+  }
+
 }  // namespace
 
 int prepare_max_k() { return 256 * 8 * 16; }
@@ -449,16 +605,21 @@ size_t prepare_nv_workspace(int T, int K) {
 hipError_t launch_prepare_mx(const void* X, bool bf16, int T, int K, int64_t ldx, const float* gamma, float eps,
                              uint8_t* bb_codes, uint8_t* bb_meta, uint8_t* bb_scale, uint8_t* res_codes,
                              uint8_t* res_scale, hipStream_t s) {
-  const PrepGeom g = prep_geometry(T, K);
-#define L(TPR, MAXC)                                                                                   \
-  if (bf16)                                                                                            \
-    hipLaunchKernelGGL((prepare_mx_kernel<TPR, MAXC, true>), dim3(g.blocks), dim3(256), 0, s, X, T, K, ldx, \
-                       gamma, eps, bb_codes, bb_meta, bb_scale, res_codes, res_scale);                 \
-  else                                                                                                 \
-    hipLaunchKernelGGL((prepare_mx_kernel<TPR, MAXC, false>), dim3(g.blocks), dim3(256), 0, s, X, T, K, ldx, \
-                       gamma, eps, bb_codes, bb_meta, bb_scale, res_codes, res_scale);
-  SHARQ_PREP_DISPATCH(L)
+  const PrepGeom g = prep_geometry_mx(T, K);
+#define L2(TPR, MAXC, B, N)                                                                           \
+  hipLaunchKernelGGL((prepare_mx_kernel<TPR, MAXC, B, N>), dim3(g.blocks), dim3(g.threads), 0, s, X, T, K, ldx, gamma, \
+                     eps, bb_codes, bb_meta, bb_scale, res_codes, res_scale)
+#define L(TPR, MAXC)                                   \
+  if (bf16) {                                          \
+    if (gamma) L2(TPR, MAXC, true, true);              \
+    else L2(TPR, MAXC, true, false);                   \
+  } else {                                             \
+    if (gamma) L2(TPR, MAXC, false, true);             \
+    else L2(TPR, MAXC, false, false);                  \
+  }
+  SHARQ_PREP_MX_DISPATCH(L)
 #undef L
+#undef L2
   return hipGetLastError();
 }
 

@@ -37,6 +37,8 @@ PREP_SHAPES = [  # (T, K, dtype, gamma): spans 64/128/256 threads per row, 1..16
     (37, 256, "bf16", True), (5, 768, "bf16", True), (3, 32, "f32", True), (64, 4096, "bf16", False),
     (17, 14336, "bf16", True), (9, 18944, "bf16", True), (33, 2048, "f32", True), (2, 3584, "bf16", True),
     (1, 96, "bf16", True), (300, 512, "bf16", True),
+    # one wave per row, rows looped per workgroup (ragged last block; fp32 rows not prefetched)
+    (4099, 2048, "bf16", True), (2100, 4096, "f32", True),
 ]
 
 
@@ -129,6 +131,9 @@ def test_linear_tiny_config():
 LINEAR_SHAPES = [  # skinny (T <= 64) and tile paths, ragged rows and columns
     (1, 512, 200), (8, 512, 200), (13, 256, 64), (64, 384, 130), (65, 512, 300), (300, 512, 520),
     (256, 1024, 256), (700, 128, 40),
+    # decode path (<= 8 rows): uneven steps per wave, the largest staged K, and
+    # a K beyond it (general skinny path)
+    (5, 1152, 72), (7, 16384, 48), (2, 18944, 40),
 ]
 
 
