@@ -20,7 +20,6 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -45,6 +44,9 @@ def parse():
     p.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = enough for > 512 MB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="first run one plain device-to-device copy of MIB MiB (a reference dispatch of known "
+                        "size for HBM byte counters)")
     return p.parse_args()
 
 
@@ -157,19 +159,13 @@ def build_jobs(workload: str, copies: int):
 # ----------------------------------------------------------------------------
 # timing
 # ----------------------------------------------------------------------------
-def run_step(jobs, it, events=None):
+def run_step(jobs, it):
     from sparsity_sharq_prepare_amd import ops
-    for j, job in enumerate(jobs):
+    for job in jobs:
         w = job.weights[it % len(job.weights)]
-        if events is not None:
-            events[j][0].record()
         ops.prepare(job.Xs[it % len(job.Xs)], job.gamma, 1e-6, job.fmt, out=job.act)
-        if events is not None:
-            events[j][1].record()
         ops.linear(job.act, w, group_offsets=job.group_offsets, row_index=job.row_index, total_rows=job.rows,
                    out=job.Y)
-        if events is not None:
-            events[j][2].record()
 
 
 def capture(jobs, first, count):
@@ -186,8 +182,7 @@ def capture(jobs, first, count):
 
 def timed(jobs, steps, warmup):
     """Wall time of exactly `steps` steps (graph replays after `warmup`
-    steps), plus per-kernel durations from HIP events recorded around each
-    launch on the launch stream."""
+    steps), plus each kernel's average launch duration (kernel_times)."""
     import torch
     R = len(jobs[0].weights)
     side = torch.cuda.Stream()
@@ -214,24 +209,43 @@ def timed(jobs, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     n_steps = steps
-    # per-kernel durations: eager launches queued behind a sleep kernel so the
-    # GPU never waits for the host between an event and the kernel it brackets
-    prep_ms = [0.0] * len(jobs)
-    gemm_ms = [0.0] * len(jobs)
-    chunk = 8
-    for base in range(0, n_steps, chunk):
-        ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in jobs] for _ in range(chunk)]
-        if hasattr(torch.cuda, "_sleep"):
-            torch.cuda._sleep(2_000_000)
-        for i in range(chunk):
-            run_step(jobs, base + i, ev[i])
-        torch.cuda.synchronize()
-        for i in range(chunk):
-            for j in range(len(jobs)):
-                prep_ms[j] += ev[i][j][0].elapsed_time(ev[i][j][1])
-                gemm_ms[j] += ev[i][j][1].elapsed_time(ev[i][j][2])
-    n_ev = -(-n_steps // chunk) * chunk
-    return wall, n_steps, [p / n_ev for p in prep_ms], [g / n_ev for g in gemm_ms]
+    prep_ms, gemm_ms = kernel_times(jobs, R)
+    return wall, n_steps, prep_ms, gemm_ms
+
+
+def kernel_times(jobs, R, reps=3):
+    """Average launch duration of each job's prepare and GEMM: a HIP graph of
+    R back-to-back launches of that kernel alone (the GEMM rotating over the R
+    weight copies, the prepare over the input copies), replayed `reps` times
+    between two HIP events on the stream it runs on, divided by the launch
+    count.  Back-to-back launches inside a graph are how the kernels run in
+    the timed steps, so this agrees with a kernel trace of the same run."""
+    import torch
+    from sparsity_sharq_prepare_amd import ops
+    prep_ms, gemm_ms = [], []
+    for job in jobs:
+        gp, gg = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gp):
+            for i in range(R):
+                ops.prepare(job.Xs[i % len(job.Xs)], job.gamma, 1e-6, job.fmt, out=job.act)
+        with torch.cuda.graph(gg):
+            for i in range(R):
+                ops.linear(job.act, job.weights[i % len(job.weights)], group_offsets=job.group_offsets,
+                           row_index=job.row_index, total_rows=job.rows, out=job.Y)
+        res = []
+        for g in (gp, gg):
+            g.replay()                                  # warm
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            res.append(e0.elapsed_time(e1) / (reps * R))
+        prep_ms.append(res[0])
+        gemm_ms.append(res[1])
+    return prep_ms, gemm_ms
 
 
 # ----------------------------------------------------------------------------
@@ -290,14 +304,6 @@ def cpu_baseline(cases, workload, target_s):
 # ----------------------------------------------------------------------------
 # traffic counters recorded by rocprofv3 (profiles/<kernel>_<workload>_traffic.txt)
 # ----------------------------------------------------------------------------
-def kernel_source_hash(files):
-    h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(ROOT, "sparsity_sharq_prepare_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def read_traffic(name, sources):
     path = os.path.join(ROOT, "profiles", f"{name}_traffic.txt")
     if not os.path.exists(path):
@@ -307,7 +313,8 @@ def read_traffic(name, sources):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_sha256") != kernel_source_hash(sources):
+    from sparsity_sharq_prepare_amd.profiling import source_hash
+    if vals.get("source_sha256") != source_hash(sources):
         return None                          # the kernel changed since the counters were taken
     try:
         return float(vals["traffic_bytes_per_launch"])
@@ -329,6 +336,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     _lib.lib()                                # fail loudly if libsharq.so is missing
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.full((n,), 7, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     jobs, cases, pack_times = build_jobs(args.workload, args.copies)
     wall, n_steps, prep_ms, gemm_ms = timed(jobs, args.steps, args.warmup)
     ms_step = wall * 1e3 / n_steps
@@ -350,7 +365,7 @@ def main():
         }
     n = len(jobs)
     if args.workload == "decode":
-        dom, bound, unit, peak = "linear_mx_skinny", "hbm", "GB/s", HBM_PEAK_GBS
+        dom, bound, unit, peak = "linear_mx_decode", "hbm", "GB/s", HBM_PEAK_GBS
         ach = sum(j.gemm_bytes() for j in jobs) / n / (gemm_total_ms / n * 1e-3) / 1e9
         src = ["gemm_mx.hip", "common.h"]
     elif args.workload == "nvfp4":

@@ -1,0 +1,99 @@
+"""HBM traffic of a kernel from rocprofv3 counter passes.
+
+Two `rocprofv3 --pmc` passes of the same command, one collecting FETCH_SIZE
+and one WRITE_SIZE (KiB per dispatch), give the bytes a kernel moved between
+L2 and HBM.  The counters are scaled by what they read for a reference
+dispatch of known size: a plain device-to-device copy of C bytes reads C and
+writes C, so the factor is C / counter for each pass.  `bench.py
+--copy-calibration MIB` runs such a copy (the runtime's copyBuffer blit) first;
+it is the largest copyBuffer dispatch of the run.
+
+    python -m sparsity_sharq_prepare_amd.profiling \\
+        --fetch <fetch pass counter_collection.csv> \\
+        --write <write pass counter_collection.csv> \\
+        --kernel linear_mx_decode --copy-mib 256 --workload decode \\
+        --out profiles/linear_mx_decode_decode_traffic.txt --command "..."
+
+The summary records traffic_bytes_per_launch (the kernel's average over its
+dispatches) and source_sha256, a hash of the kernel sources, so that bench.py
+ignores it once the kernel has changed.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SOURCES = {
+    "linear_mx_decode": ["gemm_mx.hip", "common.h"],
+    "linear_mx_tile": ["gemm_mx.hip", "common.h"],
+    "linear_nv_tile": ["gemm_nv.hip", "common.h"],
+    "prepare_mx_kernel": ["prepare.hip", "common.h"],
+}
+
+
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "sparsity_sharq_prepare_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def per_dispatch(path: str, counter: str) -> dict:
+    """{dispatch id: (kernel name, counter value summed over its rows)}."""
+    vals = defaultdict(float)
+    names = {}
+    with open(path, newline="") as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            d = r["Dispatch_Id"]
+            vals[d] += float(r["Counter_Value"])
+            names[d] = r["Kernel_Name"]
+    return {d: (names[d], v) for d, v in vals.items()}
+
+
+def kernel_bytes(path: str, counter: str, kernel: str, copy_bytes: int):
+    disp = per_dispatch(path, counter)
+    copies = [v for n, v in disp.values() if "copyBuffer" in n]
+    if not copies:
+        raise SystemExit(f"{path}: no copyBuffer dispatch for the calibration")
+    factor = copy_bytes / (max(copies) * 1024.0)
+    ks = [v for n, v in disp.values() if kernel in n]
+    if not ks:
+        raise SystemExit(f"{path}: no dispatch of {kernel}")
+    return sum(ks) / len(ks) * 1024.0 * factor, factor, len(ks)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--kernel", required=True, choices=sorted(SOURCES))
+    ap.add_argument("--copy-mib", type=int, required=True)
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--command", default="")
+    a = ap.parse_args()
+    cb = a.copy_mib << 20
+    fb, ff, nf = kernel_bytes(a.fetch, "FETCH_SIZE", a.kernel, cb)
+    wb, fw, nw = kernel_bytes(a.write, "WRITE_SIZE", a.kernel, cb)
+    with open(a.out, "w") as fh:
+        fh.write(f"# HBM traffic of {a.kernel} ({a.workload} workload), rocprofv3 FETCH_SIZE / WRITE_SIZE passes\n")
+        if a.command:
+            fh.write(f"# command: {a.command}\n")
+        fh.write(f"# calibration: copy of {cb} bytes; fetch factor {ff:.4f}, write factor {fw:.4f}\n")
+        fh.write(f"# dispatches: fetch pass {nf}, write pass {nw}\n")
+        fh.write(f"fetch_bytes_per_launch = {fb:.0f}\n")
+        fh.write(f"write_bytes_per_launch = {wb:.0f}\n")
+        fh.write(f"traffic_bytes_per_launch = {fb + wb:.0f}\n")
+        fh.write(f"source_sha256 = {source_hash(SOURCES[a.kernel])}\n")
+    print(open(a.out).read())
+
+
+if __name__ == "__main__":
+    main()
