@@ -418,18 +418,23 @@ struct TileFrag {
 
 }  // namespace
 
-template <int BM, bool GROUPED>
-__global__ __launch_bounds__(256, 1) void linear_mx_tile(
+template <int BM, bool GROUPED, int WN>
+__global__ __launch_bounds__(256 * WN, 1) void linear_mx_tile(
     const uint8_t* __restrict__ bb_codes, const uint8_t* __restrict__ bb_meta, const uint8_t* __restrict__ bb_scale,
     const uint8_t* __restrict__ res_codes, const uint8_t* __restrict__ res_scale, const int32_t* __restrict__ row_index,
     int rows, int act_rows, int K, const uint8_t* __restrict__ payload, const uint8_t* __restrict__ wscale, int D,
     int n_groups, const int32_t* __restrict__ group_offsets, float* __restrict__ Y, int64_t ldy) {
   using Stage = TileStage<BM>;
-  constexpr int WM = BM / 4, FM = WM / 32, FN = kBN / 32;
+  // 4 x WN waves: wave w covers rows (w & 3) * WM .. and columns (w >> 2) * WNC ..
+  constexpr int NW = 4 * WN;
+  constexpr int WM = BM / 4, WNC = kBN / WN, FM = WM / 32, FN = WNC / 32;
+  static_assert(WN == 1 || BM == 256, "two waves per SIMD only for the 256-row tile");
   using Frag = TileFrag<FM, FN>;
-  // DMA instructions per wave and stage: A_dn, B, A_sp, meta, 3 scale rows
-  constexpr int N_DN = BM / 64, N_B = 4, N_SP = BM / 128, N_MT = BM / 128;
-  constexpr int NDMA = N_DN + N_B + N_SP + N_MT + 3;
+  // DMA instructions per wave and stage: A_dn, B, A_sp, meta, scale rows
+  // (WN = 1: s_sp, s_dn, s_b; WN = 2: waves 0-3 s_sp and s_dn, waves 4-7 s_b
+  // twice, so every wave issues the same number and one wait count fits all)
+  constexpr int N_DN = BM / (16 * NW), N_B = 16 / NW, N_SP = BM / (32 * NW), N_MT = BM / (32 * NW);
+  constexpr int NDMA = N_DN + N_B + N_SP + N_MT + (WN == 1 ? 3 : 2);
   __shared__ Stage lds[kNS];
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
@@ -487,47 +492,56 @@ __global__ __launch_bounds__(256, 1) void linear_mx_tile(
   uint32_t o_dn[N_DN], o_b[N_B], o_sp[N_SP], o_mt[N_MT];
 #pragma unroll
   for (int j = 0; j < N_DN; ++j) {
-    const int sl = 64 * (w + 4 * j) + l, row = sl >> 2, q = (sl & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
+    const int sl = 64 * (w + NW * j) + l, row = sl >> 2, q = (sl & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
     o_dn[j] = act_row(row) * kR + 16 * q;
   }
 #pragma unroll
   for (int j = 0; j < N_B; ++j) {
-    const int sl = 64 * (w + 4 * j) + l, col = sl >> 2, q = (sl & 3) ^ (((col >> 1) ^ (col >> 3)) & 3);
+    const int sl = 64 * (w + NW * j) + l, col = sl >> 2, q = (sl & 3) ^ (((col >> 1) ^ (col >> 3)) & 3);
     o_b[j] = w_row(col) * kR + 16 * q;
   }
 #pragma unroll
   for (int j = 0; j < N_SP; ++j) {
-    const int sl = 64 * (w + 4 * j) + l, row = sl >> 1, h = (sl & 1) ^ ((row >> 3) & 1);
+    const int sl = 64 * (w + NW * j) + l, row = sl >> 1, h = (sl & 1) ^ ((row >> 3) & 1);
     o_sp[j] = act_row(row) * kA + 16 * h;
   }
 #pragma unroll
   for (int j = 0; j < N_MT; ++j) {                      // dword slots: 2 per row
-    const int sl = 64 * (w + 4 * j) + l, row = sl >> 1, h = sl & 1;
+    const int sl = 64 * (w + NW * j) + l, row = sl >> 1, h = sl & 1;
     o_mt[j] = act_row(row) * kM + 4 * h;
   }
   // scale rows: one dword (4 blocks) per row; for BM = 128 waves 2, 3 repeat
   // the rows of waves 0, 1 (same bytes to the same place)
-  const int srow = (64 * w + l) & (BM - 1);
+  const int wq = w & 3;
+  const int srow = (64 * wq + l) & (BM - 1);
   const uint32_t o_ssp = act_row(srow) * kS;
-  const uint32_t o_sb = w_row(64 * w + l) * kS;
-  const int sdst = 64 * (w & (BM / 64 - 1));
+  const uint32_t o_sb = w_row(64 * wq + l) * kS;
+  const int sdst = 64 * (wq & (BM / 64 - 1));
 
   auto issue = [&](int s, Stage& st) {
     const uint32_t s64 = 64u * s, s32 = 32u * s, s8 = 8u * s, s4 = 4u * s;
 #pragma unroll
-    for (int j = 0; j < N_DN; ++j) dma16(r_dn, o_dn[j], s64, lds_addr(&st.a_dn[64 * (w + 4 * j)]));
+    for (int j = 0; j < N_DN; ++j) dma16(r_dn, o_dn[j], s64, lds_addr(&st.a_dn[64 * (w + NW * j)]));
 #pragma unroll
-    for (int j = 0; j < N_B; ++j) dma16(r_b, o_b[j], s64, lds_addr(&st.b[64 * (w + 4 * j)]));
+    for (int j = 0; j < N_B; ++j) dma16(r_b, o_b[j], s64, lds_addr(&st.b[64 * (w + NW * j)]));
 #pragma unroll
-    for (int j = 0; j < N_SP; ++j) dma16(r_sp, o_sp[j], s32, lds_addr(&st.a_sp[64 * (w + 4 * j)]));
+    for (int j = 0; j < N_SP; ++j) dma16(r_sp, o_sp[j], s32, lds_addr(&st.a_sp[64 * (w + NW * j)]));
 #pragma unroll
-    for (int j = 0; j < N_MT; ++j) dma4(r_mt, o_mt[j], s8, lds_addr(&st.meta[64 * (w + 4 * j)]));
-    dma4(r_ssp, o_ssp, s4, lds_addr(&st.s_sp[sdst]));
-    dma4(r_sdn, o_ssp, s4, lds_addr(&st.s_dn[sdst]));
-    dma4(r_sb, o_sb, s4, lds_addr(&st.s_b[64 * w]));
+    for (int j = 0; j < N_MT; ++j) dma4(r_mt, o_mt[j], s8, lds_addr(&st.meta[64 * (w + NW * j)]));
+    if (WN == 1) {
+      dma4(r_ssp, o_ssp, s4, lds_addr(&st.s_sp[sdst]));
+      dma4(r_sdn, o_ssp, s4, lds_addr(&st.s_dn[sdst]));
+      dma4(r_sb, o_sb, s4, lds_addr(&st.s_b[64 * w]));
+    } else if (w < 4) {                                // uniform branch
+      dma4(r_ssp, o_ssp, s4, lds_addr(&st.s_sp[sdst]));
+      dma4(r_sdn, o_ssp, s4, lds_addr(&st.s_dn[sdst]));
+    } else {
+      dma4(r_sb, o_sb, s4, lds_addr(&st.s_b[64 * wq]));
+      dma4(r_sb, o_sb, s4, lds_addr(&st.s_b[64 * wq]));   // same bytes again: equal counts
+    }
   };
 
-  const int wm0 = w * WM;
+  const int wm0 = (w & 3) * WM, wn0 = (w >> 2) * WNC;
   const int kh = l >> 5, lr = l & 31;
   auto read = [&](const Stage& st, Frag& F, auto jc) {
     constexpr int J = decltype(jc)::value;
@@ -538,7 +552,7 @@ __global__ __launch_bounds__(256, 1) void linear_mx_tile(
     const uint16_t* meta = reinterpret_cast<const uint16_t*>(st.meta);
 #pragma unroll
     for (int n = 0; n < FN; ++n) {
-      const int c = 32 * n + lr;
+      const int c = wn0 + 32 * n + lr;
       F.b[n] = st.b[slot(c, 2 * kh + J)];
       F.bs[n] = s_b[2 * c + kh];
     }
@@ -573,39 +587,60 @@ __global__ __launch_bounds__(256, 1) void linear_mx_tile(
 
   const std::integral_constant<int, 0> j0{};
   const std::integral_constant<int, 1> j1{};
-  Frag f0, f1;
-  issue(0, lds[0]);
-  issue(min(1, KS - 1), lds[1]);
-  issue(min(2, KS - 1), lds[2]);
-  wait_vm_lgkm0<2 * NDMA>();
-  __builtin_amdgcn_s_barrier();
-  read(lds[0], f0, j0);
-  // the last step is peeled off so that the loop body is one basic block
-  // and the phase order below is the order of issue
-  for (int s = 0; s < KS - 1; ++s) {
-    Stage& cur = lds[s % kNS];
-    // the half-0 fragments were read a whole MFMA group ago; retiring them
-    // here keeps the wait for them from also covering the reads below
-    wait_lgkm0();
-    read(cur, f1, j1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_half(f0, j0);
-    __builtin_amdgcn_sched_barrier(0);
-    // stage s+1 landed (stage s+2 may be in flight) and every wave is past
-    // its reads of the buffer of step s
-    wait_vm_lgkm0<NDMA>();
+  if constexpr (WN == 1) {
+    Frag f0, f1;
+    issue(0, lds[0]);
+    issue(min(1, KS - 1), lds[1]);
+    issue(min(2, KS - 1), lds[2]);
+    wait_vm_lgkm0<2 * NDMA>();
     __builtin_amdgcn_s_barrier();
-    read(lds[(s + 1) % kNS], f0, j0);
-    // past the end the last step is reloaded into the idle buffer, so every
-    // step issues the same loads and one wait count fits all
-    issue(min(s + 3, KS - 1), cur);
-    __builtin_amdgcn_sched_barrier(0);
+    read(lds[0], f0, j0);
+    // the last step is peeled off so that the loop body is one basic block
+    // and the phase order below is the order of issue
+    for (int s = 0; s < KS - 1; ++s) {
+      Stage& cur = lds[s % kNS];
+      // the half-0 fragments were read a whole MFMA group ago; retiring them
+      // here keeps the wait for them from also covering the reads below
+      wait_lgkm0();
+      read(cur, f1, j1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_half(f0, j0);
+      __builtin_amdgcn_sched_barrier(0);
+      // stage s+1 landed (stage s+2 may be in flight) and every wave is past
+      // its reads of the buffer of step s
+      wait_vm_lgkm0<NDMA>();
+      __builtin_amdgcn_s_barrier();
+      read(lds[(s + 1) % kNS], f0, j0);
+      // past the end the last step is reloaded into the idle buffer, so every
+      // step issues the same loads and one wait count fits all
+      issue(min(s + 3, KS - 1), cur);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_half(f1, j1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    read(lds[(KS - 1) % kNS], f1, j1);
+    mfma_half(f0, j0);
     mfma_half(f1, j1);
-    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    // two waves per SIMD: the other wave covers this one's LDS latency, so
+    // fragments are read right before their MFMAs (single-buffered) and the
+    // loads run two steps ahead
+    Frag f;
+    issue(0, lds[0]);
+    issue(min(1, KS - 1), lds[1]);
+    for (int s = 0; s < KS; ++s) {
+      // stage s landed (s+1 may be in flight); after the barrier every wave is
+      // also past its reads of the buffer of step s-1, which stage s+2 reuses
+      wait_vm_lgkm0<NDMA>();
+      __builtin_amdgcn_s_barrier();
+      issue(min(s + 2, KS - 1), lds[(s + 2) % kNS]);
+      const Stage& cur = lds[s % kNS];
+      read(cur, f, j0);
+      mfma_half(f, j0);
+      read(cur, f, j1);
+      mfma_half(f, j1);
+    }
   }
-  read(lds[(KS - 1) % kNS], f1, j1);
-  mfma_half(f0, j0);
-  mfma_half(f1, j1);
   wait_vm_lgkm0<0>();                                  // no DMA may land after the tile ends
 
   // ---- epilogue: fp32 store of the single accumulator tile
@@ -613,12 +648,204 @@ __global__ __launch_bounds__(256, 1) void linear_mx_tile(
   for (int f = 0; f < FM; ++f) {
 #pragma unroll
     for (int n = 0; n < FN; ++n) {
-      const int c = n0 + 32 * n + lr;
+      const int c = n0 + wn0 + 32 * n + lr;
       if (c >= D) continue;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int r = m0 + wm0 + 32 * f + 8 * (i >> 2) + 4 * kh + (i & 3);
         if (r < row_end) Y[(int64_t)r * ldy + c] = acc[f][n][i];
+      }
+    }
+  }
+}
+
+// ============================================================================
+// prefill tile kernel, two waves per SIMD (K % 512 == 0)
+// ============================================================================
+// Tile 256 x 256, eight waves: wave w covers rows 64 (w & 3) .. and columns
+// 128 (w >> 2) .., a 64 x 128 accumulator (128 registers), so two waves share
+// each SIMD and cover each other's LDS and barrier latency.
+//
+// Operand bytes per row and 128-step (codes: 64 B residual, 32 B backbone,
+// 64 B weight) go through a 3-deep LDS ring as before.  The small per-row
+// data (4 B of scales per row and step, 8 B of metadata) would cost one cache
+// line per 4-8 bytes if fetched per step, so it comes in groups of four steps
+// (16 B of scales, 32 B of metadata per row) into a double-buffered side
+// ring, fetched two steps before the group starts.  Every wave issues the
+// same loads (5 per step, 3 more on the third step of a group), so the
+// explicit wait counts are per step of a group: 5, 5, 5, 8.
+namespace {
+
+struct Tile8Main {
+  uint4 a_dn[256 * 4];         // residual codes, 64 B per row (swizzled 16 B slots)
+  uint4 b[256 * 4];            // weight payload, 64 B per column
+  uint4 a_sp[256 * 2];         // compacted backbone, 32 B per row
+};
+struct Tile8Side {             // four steps
+  uint4 meta[256 * 2];         // 32 B per row: step p at bytes 8 p .. 8 p + 7
+  uint4 s_sp[256];             // 16 B per row: step p at bytes 4 p .. 4 p + 3
+  uint4 s_dn[256];
+  uint4 s_b[256];
+};
+
+}  // namespace
+
+__global__ __launch_bounds__(512, 1) void linear_mx_tile8(
+    const uint8_t* __restrict__ bb_codes, const uint8_t* __restrict__ bb_meta, const uint8_t* __restrict__ bb_scale,
+    const uint8_t* __restrict__ res_codes, const uint8_t* __restrict__ res_scale, const int32_t* __restrict__ row_index,
+    int rows, int act_rows, int K, const uint8_t* __restrict__ payload, const uint8_t* __restrict__ wscale, int D,
+    float* __restrict__ Y, int64_t ldy) {
+  constexpr int BM = 256, WM = 64, WNC = 128, FM = 2, FN = 4;
+  using Frag = TileFrag<FM, FN>;
+  __shared__ Tile8Main lds[kNS];
+  __shared__ Tile8Side side[2];
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+  const int wq = w & 3;
+
+  // ---- tile -> (first row, first column); consecutive tiles on one XCD
+  const int tiles_n = (D + kBN - 1) / kBN, tiles_m = (rows + BM - 1) / BM;
+  const int nt = tiles_m * tiles_n;
+  int bi = blockIdx.x;
+  if ((nt & 7) == 0) bi = (bi & 7) * (nt >> 3) + (bi >> 3);
+  const int m0 = (bi % tiles_m) * BM, n0 = (bi / tiles_m) * kBN;
+
+  const int KS = K >> 7, G = KS >> 2;
+  const uint32_t kA = K >> 2, kM = K >> 4, kS = K >> 5, kR = K >> 1;
+  const int4v r_dn = make_rsrc(res_codes, (uint32_t)act_rows * kR);
+  const int4v r_sp = make_rsrc(bb_codes, (uint32_t)act_rows * kA);
+  const int4v r_mt = make_rsrc(bb_meta, (uint32_t)act_rows * kM);
+  const int4v r_ssp = make_rsrc(bb_scale, (uint32_t)act_rows * kS);
+  const int4v r_sdn = make_rsrc(res_scale, (uint32_t)act_rows * kS);
+  const int4v r_b = make_rsrc(payload, (uint32_t)D * kR);
+  const int4v r_sb = make_rsrc(wscale, (uint32_t)D * kS);
+
+  // activation row of tile row r (rows past the end read row 0: their
+  // products reach only outputs that are never stored)
+  auto act_row = [&](int r) -> uint32_t {
+    const int gr = m0 + r;
+    return gr < rows ? (uint32_t)gather_row(row_index, gr, act_rows) : 0u;
+  };
+  auto w_row = [&](int c) -> uint32_t { return n0 + c < D ? (uint32_t)(n0 + c) : 0u; };
+
+  // ---- per-lane DMA byte offsets at step / group 0
+  uint32_t o_dn[2], o_b[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int sl = 64 * (w + 8 * j) + l, row = sl >> 2, q = (sl & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
+    o_dn[j] = act_row(row) * kR + 16 * q;
+    o_b[j] = w_row(row) * kR + 16 * q;
+  }
+  uint32_t o_sp;
+  {
+    const int sl = 64 * w + l, row = sl >> 1, h = (sl & 1) ^ ((row >> 3) & 1);
+    o_sp = act_row(row) * kA + 16 * h;
+  }
+  const uint32_t o_mt = act_row((64 * w + l) >> 1) * kM + 16 * (l & 1);   // 2 lanes x 16 B per row
+  // waves 0-3: backbone scale rows and weight scale columns 64 wq + l;
+  // waves 4-7: residual scale rows and the same weight columns again
+  const uint32_t o_sa = act_row(64 * wq + l) * kS;
+  const uint32_t o_sw = w_row(64 * wq + l) * kS;
+  const int4v r_sa = w < 4 ? r_ssp : r_sdn;
+
+  auto issue_main = [&](int s, Tile8Main& st) {
+    const uint32_t s64 = 64u * s, s32 = 32u * s;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(r_dn, o_dn[j], s64, lds_addr(&st.a_dn[64 * (w + 8 * j)]));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(r_b, o_b[j], s64, lds_addr(&st.b[64 * (w + 8 * j)]));
+    dma16(r_sp, o_sp, s32, lds_addr(&st.a_sp[64 * w]));
+  };
+  auto issue_side = [&](int g, Tile8Side& sd) {
+    dma16(r_mt, o_mt, 32u * g, lds_addr(&sd.meta[64 * w]));
+    dma16(r_sa, o_sa, 16u * g, lds_addr(w < 4 ? &sd.s_sp[64 * wq] : &sd.s_dn[64 * wq]));
+    dma16(r_sb, o_sw, 16u * g, lds_addr(&sd.s_b[64 * wq]));   // waves w and w + 4: same bytes
+  };
+
+  const int wm0 = wq * WM, wn0 = (w >> 2) * WNC;
+  const int kh = l >> 5, lr = l & 31;
+  auto read = [&](const Tile8Main& st, const Tile8Side& sd, int p, Frag& F, auto jc) {
+    constexpr int J = decltype(jc)::value;
+    const uint16_t* s_b = reinterpret_cast<const uint16_t*>(sd.s_b);
+    const uint16_t* s_sp = reinterpret_cast<const uint16_t*>(sd.s_sp);
+    const uint16_t* s_dn = reinterpret_cast<const uint16_t*>(sd.s_dn);
+    const uint16_t* meta = reinterpret_cast<const uint16_t*>(sd.meta);
+    const uint2* a_sp = reinterpret_cast<const uint2*>(st.a_sp);
+#pragma unroll
+    for (int n = 0; n < FN; ++n) {
+      const int c = wn0 + 32 * n + lr;
+      F.b[n] = st.b[slot(c, 2 * kh + J)];
+      F.bs[n] = s_b[8 * c + 2 * p + kh];
+    }
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+      const int r = wm0 + 32 * f + lr;
+      F.dn[f] = st.a_dn[slot(r, 2 * kh + J)];
+      F.sp[f] = a_sp[2 * slot_sp(r, kh) + J];
+      F.mt[f] = meta[16 * r + 4 * p + 2 * kh + J];
+      F.ssp[f] = s_sp[8 * r + 2 * p + kh];
+      F.sdn[f] = s_dn[8 * r + 2 * p + kh];
+    }
+  };
+
+  v16f acc[FM][FN];
+#pragma unroll
+  for (int f = 0; f < FM; ++f)
+#pragma unroll
+    for (int n = 0; n < FN; ++n) acc[f][n] = (v16f){};
+
+  auto mfma_half = [&](const Frag& F, auto jc) {
+    constexpr int J = decltype(jc)::value;
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+      const uint4 asp = expand4_fast(F.sp[f].x, F.sp[f].y, F.mt[f]);
+#pragma unroll
+      for (int n = 0; n < FN; ++n) acc[f][n] = mfma32_fp4_sel<J>(asp, F.b[n], acc[f][n], F.ssp[f], F.bs[n]);
+#pragma unroll
+      for (int n = 0; n < FN; ++n) acc[f][n] = mfma32_fp4_sel<J>(F.dn[f], F.b[n], acc[f][n], F.sdn[f], F.bs[n]);
+    }
+  };
+  const std::integral_constant<int, 0> j0{};
+  const std::integral_constant<int, 1> j1{};
+
+  Frag f;
+  issue_main(0, lds[0]);
+  issue_side(0, side[0]);
+  issue_main(min(1, KS - 1), lds[1]);
+  for (int g = 0; g < G; ++g) {
+    const Tile8Side& sd = side[g & 1];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int s = 4 * g + p;
+      // stage s (and at p = 0 side group g) landed; stage s+1 (and after
+      // p = 2 side group g+1) may still be in flight.  After the barrier every
+      // wave is past its reads of step s-1, whose buffer stage s+2 reuses.
+      if (p == 3) wait_vm_lgkm0<8>();
+      else wait_vm_lgkm0<5>();
+      __builtin_amdgcn_s_barrier();
+      issue_main(min(s + 2, KS - 1), lds[(s + 2) % kNS]);
+      // side group g+1 replaces group g-1, last read at step 4 g - 1
+      if (p == 2) issue_side(min(g + 1, G - 1), side[(g + 1) & 1]);
+      const Tile8Main& cur = lds[s % kNS];
+      read(cur, sd, p, f, j0);
+      mfma_half(f, j0);
+      read(cur, sd, p, f, j1);
+      mfma_half(f, j1);
+    }
+  }
+  wait_vm_lgkm0<0>();                                  // no DMA may land after the tile ends
+
+  // ---- epilogue: fp32 store of the accumulator tile
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+    for (int n = 0; n < FN; ++n) {
+      const int c = n0 + wn0 + 32 * n + lr;
+      if (c >= D) continue;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = m0 + wm0 + 32 * fm + 8 * (i >> 2) + 4 * kh + (i & 3);
+        if (r < rows) Y[(int64_t)r * ldy + c] = acc[fm][n][i];
       }
     }
   }
@@ -695,12 +922,17 @@ hipError_t launch_linear_mx(const uint8_t* bb_codes, const uint8_t* bb_meta, con
   const int tiles_n = (D + kBN - 1) / kBN;
   if (n_groups == 1) {
     const int tiles_m = (rows + 255) / 256;
-    hipLaunchKernelGGL((linear_mx_tile<256, false>), dim3(tiles_m * tiles_n), dim3(256), 0, s, bb_codes, bb_meta,
+    if (K % 512 == 0) {
+      hipLaunchKernelGGL(linear_mx_tile8, dim3(tiles_m * tiles_n), dim3(512), 0, s, bb_codes, bb_meta, bb_scale,
+                         res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, Y, ldy);
+      return hipGetLastError();
+    }
+    hipLaunchKernelGGL((linear_mx_tile<256, false, 2>), dim3(tiles_m * tiles_n), dim3(512), 0, s, bb_codes, bb_meta,
                        bb_scale, res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, 1, group_offsets, Y,
                        ldy);
   } else {
     const int bound = ((rows + 127) / 128 + n_groups) * tiles_n;
-    hipLaunchKernelGGL((linear_mx_tile<128, true>), dim3(bound), dim3(256), 0, s, bb_codes, bb_meta, bb_scale,
+    hipLaunchKernelGGL((linear_mx_tile<128, true, 1>), dim3(bound), dim3(256), 0, s, bb_codes, bb_meta, bb_scale,
                        res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, n_groups, group_offsets, Y,
                        ldy);
   }
