@@ -696,7 +696,6 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
     int rows, int act_rows, int K, const uint8_t* __restrict__ payload, const uint8_t* __restrict__ wscale, int D,
     float* __restrict__ Y, int64_t ldy) {
   constexpr int BM = 256, WM = 64, WNC = 128, FM = 2, FN = 4;
-  using Frag = TileFrag<FM, FN>;
   __shared__ Tile8Main lds[kNS];
   __shared__ Tile8Side side[2];
   const int tid = threadIdx.x, l = tid & 63;
@@ -764,28 +763,38 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
 
   const int wm0 = wq * WM, wn0 = (w >> 2) * WNC;
   const int kh = l >> 5, lr = l & 31;
-  auto read = [&](const Tile8Main& st, const Tile8Side& sd, int p, Frag& F, auto jc) {
-    constexpr int J = decltype(jc)::value;
+  // per step: scales (both halves: op_sel picks the byte), metadata (low /
+  // high 16 bits) and the compacted backbone (low / high 8 bytes) are read
+  // once; per half-step only the weight and residual code fragments
+  struct StepFrag {
+    uint32_t bs[FN], ssp[FM], sdn[FM], mt[FM];
+    uint4 sp[FM];
+  };
+  struct HalfFrag {
+    uint4 b[FN], dn[FM];
+  };
+  auto read_step = [&](const Tile8Main& st, const Tile8Side& sd, int p, StepFrag& S) {
     const uint16_t* s_b = reinterpret_cast<const uint16_t*>(sd.s_b);
     const uint16_t* s_sp = reinterpret_cast<const uint16_t*>(sd.s_sp);
     const uint16_t* s_dn = reinterpret_cast<const uint16_t*>(sd.s_dn);
-    const uint16_t* meta = reinterpret_cast<const uint16_t*>(sd.meta);
-    const uint2* a_sp = reinterpret_cast<const uint2*>(st.a_sp);
+    const uint32_t* meta = reinterpret_cast<const uint32_t*>(sd.meta);
 #pragma unroll
-    for (int n = 0; n < FN; ++n) {
-      const int c = wn0 + 32 * n + lr;
-      F.b[n] = st.b[slot(c, 2 * kh + J)];
-      F.bs[n] = s_b[8 * c + 2 * p + kh];
-    }
+    for (int n = 0; n < FN; ++n) S.bs[n] = s_b[8 * (wn0 + 32 * n + lr) + 2 * p + kh];
 #pragma unroll
     for (int f = 0; f < FM; ++f) {
       const int r = wm0 + 32 * f + lr;
-      F.dn[f] = st.a_dn[slot(r, 2 * kh + J)];
-      F.sp[f] = a_sp[2 * slot_sp(r, kh) + J];
-      F.mt[f] = meta[16 * r + 4 * p + 2 * kh + J];
-      F.ssp[f] = s_sp[8 * r + 2 * p + kh];
-      F.sdn[f] = s_dn[8 * r + 2 * p + kh];
+      S.sp[f] = st.a_sp[slot_sp(r, kh)];
+      S.mt[f] = meta[8 * r + 2 * p + kh];
+      S.ssp[f] = s_sp[8 * r + 2 * p + kh];
+      S.sdn[f] = s_dn[8 * r + 2 * p + kh];
     }
+  };
+  auto read_half = [&](const Tile8Main& st, HalfFrag& H, auto jc) {
+    constexpr int J = decltype(jc)::value;
+#pragma unroll
+    for (int n = 0; n < FN; ++n) H.b[n] = st.b[slot(wn0 + 32 * n + lr, 2 * kh + J)];
+#pragma unroll
+    for (int f = 0; f < FM; ++f) H.dn[f] = st.a_dn[slot(wm0 + 32 * f + lr, 2 * kh + J)];
   };
 
   v16f acc[FM][FN];
@@ -794,21 +803,23 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
 #pragma unroll
     for (int n = 0; n < FN; ++n) acc[f][n] = (v16f){};
 
-  auto mfma_half = [&](const Frag& F, auto jc) {
+  auto mfma_half = [&](const StepFrag& S, const HalfFrag& H, auto jc) {
     constexpr int J = decltype(jc)::value;
 #pragma unroll
     for (int f = 0; f < FM; ++f) {
-      const uint4 asp = expand4_fast(F.sp[f].x, F.sp[f].y, F.mt[f]);
+      const uint4 asp = J == 0 ? expand4_fast(S.sp[f].x, S.sp[f].y, S.mt[f] & 0xFFFFu)
+                               : expand4_fast(S.sp[f].z, S.sp[f].w, S.mt[f] >> 16);
 #pragma unroll
-      for (int n = 0; n < FN; ++n) acc[f][n] = mfma32_fp4_sel<J>(asp, F.b[n], acc[f][n], F.ssp[f], F.bs[n]);
+      for (int n = 0; n < FN; ++n) acc[f][n] = mfma32_fp4_sel<J>(asp, H.b[n], acc[f][n], S.ssp[f], S.bs[n]);
 #pragma unroll
-      for (int n = 0; n < FN; ++n) acc[f][n] = mfma32_fp4_sel<J>(F.dn[f], F.b[n], acc[f][n], F.sdn[f], F.bs[n]);
+      for (int n = 0; n < FN; ++n) acc[f][n] = mfma32_fp4_sel<J>(H.dn[f], H.b[n], acc[f][n], S.sdn[f], S.bs[n]);
     }
   };
   const std::integral_constant<int, 0> j0{};
   const std::integral_constant<int, 1> j1{};
 
-  Frag f;
+  StepFrag sf;
+  HalfFrag hf;
   issue_main(0, lds[0]);
   issue_side(0, side[0]);
   issue_main(min(1, KS - 1), lds[1]);
@@ -827,10 +838,11 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
       // side group g+1 replaces group g-1, last read at step 4 g - 1
       if (p == 2) issue_side(min(g + 1, G - 1), side[(g + 1) & 1]);
       const Tile8Main& cur = lds[s % kNS];
-      read(cur, sd, p, f, j0);
-      mfma_half(f, j0);
-      read(cur, sd, p, f, j1);
-      mfma_half(f, j1);
+      read_step(cur, sd, p, sf);
+      read_half(cur, hf, j0);
+      mfma_half(sf, hf, j0);
+      read_half(cur, hf, j1);
+      mfma_half(sf, hf, j1);
     }
   }
   wait_vm_lgkm0<0>();                                  // no DMA may land after the tile ends
