@@ -22,19 +22,6 @@ namespace sharq {
 namespace {
 
 template <bool BF16>
-SHARQ_DEV void load_group(const void* X, int64_t off, bool ok, uint4& a, uint4& b) {
-  if (!ok) { a = make_uint4(0, 0, 0, 0); b = a; return; }
-  if (BF16) {
-    a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(X) + off);
-    b = make_uint4(0, 0, 0, 0);
-  } else {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(X) + off);
-    a = p[0];
-    b = p[1];
-  }
-}
-
-template <bool BF16>
 SHARQ_DEV void unpack_group(const uint4& a, const uint4& b, float x[8]) {
   if (BF16) {
     const uint32_t w[4] = {a.x, a.y, a.z, a.w};
@@ -59,19 +46,31 @@ SHARQ_DEV float tree8_sq(const float x[8]) {
                    __fadd_rn(__fadd_rn(q[4], q[5]), __fadd_rn(q[6], q[7])));
 }
 
-// Row-resident state of one thread: its raw groups and the row's 1/rms.
+// Row-resident state of one thread: its raw groups.  Loads go through a raw
+// buffer descriptor spanning the row (no bytes for an absent row), so groups
+// past K and absent rows read zeros without branches.
 template <int TPR, int MAXC, bool BF16>
 struct RowRegs {
   uint4 ra[MAXC];
   uint4 rb[BF16 ? 1 : MAXC];
 
   SHARQ_DEV void load(const void* X, int64_t row_off, int G, int t, bool row_ok) {
+    constexpr int ES = BF16 ? 2 : 4;                   // bytes per element
+    const uint64_t base = reinterpret_cast<uint64_t>(X) + (uint64_t)row_off * ES;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+    const int bytes = __builtin_amdgcn_readfirstlane(row_ok ? G * 8 * ES : 0);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, bytes, 0x00020000);
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
-      const int g = c * TPR + t;
-      uint4 b;
-      load_group<BF16>(X, row_off + 8 * (int64_t)g, row_ok && g < G, ra[c], b);
-      if (!BF16) rb[BF16 ? 0 : c] = b;
+      const uint32_t g = (uint32_t)(c * TPR + t);
+      const auto a = __builtin_amdgcn_raw_buffer_load_b128(rs, g * (8u * ES), 0, 0);
+      ra[c] = make_uint4(a[0], a[1], a[2], a[3]);
+      if (!BF16) {
+        const auto b = __builtin_amdgcn_raw_buffer_load_b128(rs, g * (8u * ES) + 16u, 0, 0);
+        rb[BF16 ? 0 : c] = make_uint4(b[0], b[1], b[2], b[3]);
+      }
     }
   }
   SHARQ_DEV void get(int c, float x[8]) const {
@@ -195,12 +194,20 @@ struct MxRowPass {
                      uint8_t* res_scale) const {
     const int G = K >> 3;
     const float inv = NORM ? row_inv_rms<TPR, MAXC, BF16>(rr, K, eps, t, rsub, red) : 1.0f;
-    const int64_t r = __builtin_amdgcn_readfirstlane(row_ok ? row : 0);   // uniform per wave
-    uint8_t* const meta_row = bb_meta + r * (K >> 4);
-    uint8_t* const sb_row = bb_scale + r * (K >> 5);
-    uint8_t* const sr_row = res_scale + r * (K >> 5);
-    uint8_t* const bc_row = bb_codes + r * (K >> 2);
-    uint8_t* const rc_row = res_codes + r * (K >> 1);
+    // output rows through raw buffer descriptors (uniform per wave): stores
+    // at an offset past the row (lanes past K, absent rows) are dropped
+    const int64_t r = __builtin_amdgcn_readfirstlane(row_ok ? row : 0);
+    auto orow = [&](uint8_t* base, int row_bytes) {
+      const uint64_t a = reinterpret_cast<uint64_t>(base) + (uint64_t)r * row_bytes;
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+      return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
+                                               __builtin_amdgcn_readfirstlane(row_ok ? row_bytes : 0), 0x00020000);
+    };
+    const __amdgpu_buffer_rsrc_t o_bc = orow(bb_codes, K >> 2), o_rc = orow(res_codes, K >> 1);
+    const __amdgpu_buffer_rsrc_t o_mt = orow(bb_meta, K >> 4), o_sb = orow(bb_scale, K >> 5);
+    const __amdgpu_buffer_rsrc_t o_sr = orow(res_scale, K >> 5);
+    constexpr uint32_t kOut = 0x80000000u;
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
       const uint32_t g = (uint32_t)(c * TPR + t);
@@ -264,15 +271,14 @@ struct MxRowPass {
       const uint32_t nib = i0 | (i1 << 2);
       const uint32_t b8 = nib | (dpp_u<kDppQuadXor1>(nib) << 4);
       const uint32_t m16 = (b8 & 0xFFu) | (dpp_u<kDppQuadXor2>(b8) << 8);
-      if (ok) {
-        *reinterpret_cast<uint16_t*>(bc_row + 2 * g) = (uint16_t)kept2;
-        *reinterpret_cast<uint32_t*>(rc_row + 4 * g) = rw;
-        if ((g & 3) == 0) {
-          *reinterpret_cast<uint16_t*>(meta_row + (g >> 1)) = (uint16_t)m16;
-          sb_row[g >> 2] = (uint8_t)eb;
-          sr_row[g >> 2] = (uint8_t)er;
-        }
-      }
+      // (groups past K have offsets past the row; block values only from the
+      // quad's first lane)
+      const uint32_t qo = (g & 3) == 0 ? 0u : kOut;
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)kept2, o_bc, 2 * g, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(rw, o_rc, 4 * g, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)m16, o_mt, (g >> 1) | qo, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)eb, o_sb, (g >> 2) | qo, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)er, o_sr, (g >> 2) | qo, 0, 0);
     }
   }
 };
