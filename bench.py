@@ -322,6 +322,29 @@ def read_traffic(name, sources):
         return None
 
 
+def oracle_errors(cases, y_gpu, workload):
+    """Relative Frobenius error against the unquantized product y W (fp64),
+    y = RMSNorm(x), for the GPU's SharQ output and for plain FP4 of the same
+    activations and packed weights (oracle), on the rows the CPU baseline
+    samples: all rows at decode, the first 64 otherwise (MoE: not reported)."""
+    import numpy as np
+    from oracle import sharq as O
+    if workload == "moe":
+        return None
+    out = {}
+    for c, Yg in zip(cases, y_gpu):
+        rows = Yg.shape[0]
+        prep = O.prepare(c.x_f32()[:rows], c.gamma, 1e-6, c.fmt)
+        y = prep["y"].astype(np.float64)
+        W = c.w_f32().astype(np.float64)
+        ref = y @ W
+        wp = O.pack_weight(c.w_f32(), c.fmt)
+        plain = O.plain_quantized(prep["y"], c.fmt) @ O.weight_dequant(wp, "dn")
+        out[c.name] = {"rows": rows, "sharq": round(O.rel_frobenius(Yg.astype(np.float64), ref), 6),
+                       f"plain_{c.fmt}": round(O.rel_frobenius(plain, ref), 6)}
+    return out
+
+
 # ----------------------------------------------------------------------------
 def main():
     args = parse()
@@ -402,6 +425,9 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cases, args.workload, args.cpu_seconds)
+        if args.workload != "moe":
+            y_gpu = [j.Y[: (j.rows if args.workload == "decode" else 64)].float().cpu().numpy() for j in jobs]
+            out["errors"] = oracle_errors(cases, y_gpu, args.workload)
     print(json.dumps(out))
 
 
