@@ -303,7 +303,6 @@ __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void prepare_mx_kernel(const
   const int nblk = (T + RPW - 1) / RPW;
 
   Pass pass;
-  pass.load_gamma(gamma, K, gsm);
   RowRegs<TPR, MAXC, BF16> ra, rb;
   auto load = [&](RowRegs<TPR, MAXC, BF16>& rr, int blk) {
     const int row = blk * RPW + rsub;
@@ -317,8 +316,9 @@ __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void prepare_mx_kernel(const
              res_scale);
   };
   int blk = blockIdx.x;
+  load(ra, blk);                                       // first rows in flight while gamma is staged
+  pass.load_gamma(gamma, K, gsm);
   if (Pass::CACHE) {
-    load(ra, blk);
     while (blk < nblk) {
       step(ra, rb, blk, 0);
       blk += gridDim.x;
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void prepare_mx_kernel(const
     }
   } else {
     for (int par = 0; blk < nblk; blk += gridDim.x, par ^= 1) {
-      load(ra, blk);
+      if (blk != (int)blockIdx.x) load(ra, blk);
       const int row = blk * RPW + rsub;
       pass.run(ra, row, row < T, K, eps, t, rsub, red + par * Pass::RED, bb_codes, bb_meta, bb_scale, res_codes,
                res_scale);
