@@ -184,6 +184,21 @@ def test_linear_prefill_full_sampled_and_deterministic():
     assert_gemm_close(Y.cpu().numpy()[r, c], Yr, S)
 
 
+@pytest.mark.parametrize("T,K,D", [(4096, 512, 4096), (4000, 1024, 3000)])
+def test_linear_tile_widths_sampled(T, K, D):
+    # 4096 x 4096: 256 tiles of 256 columns fill one round, so the 256-wide
+    # tile is chosen; 4000 x 3000: 224-wide tiles with ragged rows and columns
+    case = synth.random_case(T + K + D, T, K, D)
+    act, w, Y = run_case(case)
+    ref = oracle_prepare(case)
+    r, c = sample_pairs(case.T, case.D, 2000, seed=2)
+    cols = np.unique(c)
+    wref = O.weight_cols(O.pack_weight(case.w_f32()[:, cols]), slice(None))
+    ci = np.searchsorted(cols, c)
+    Yr, S = O.sharq_linear_sampled(ref, wref, r, ci)
+    assert_gemm_close(Y.cpu().numpy()[r, c], Yr, S)
+
+
 # ------------------------------------------------------------------ NVFP4 (emulated)
 @pytest.mark.parametrize("T,K,D", [(16, 256, 64), (130, 512, 200), (64, 3584, 300)])
 def test_nvfp4_linear_shapes(T, K, D):
