@@ -373,7 +373,7 @@ def main():
 
     nominal = sum(j.gemm_flops_nominal() for j in jobs)
     tflops = nominal / (ms_step * 1e-3) / 1e12
-    tokens = sum(j.X.shape[0] for j in jobs) / len(jobs)
+    tokens = jobs[0].X.shape[0]                      # tokens of the step (MoE: before routing)
     tok_s = tokens / (ms_step * 1e-3)
 
     gemm_total_ms = sum(gemm_ms)

@@ -452,17 +452,43 @@ __global__ __launch_bounds__(256 * WN, 1) void linear_mx_tile(
     row_end = rows;
     n0 = tn * kBN;
   } else {
-    int b = blockIdx.x;
-    int e = 0, start = 0, cnt = 0;
-    for (; e < n_groups; ++e) {
-      start = min(max(group_offsets[e], 0), rows);
-      cnt = min(max(group_offsets[e + 1], start), rows) - start;
-      const int te = ((cnt + BM - 1) / BM) * tiles_n;
-      if (b < te) break;
-      b -= te;
+    // tile -> expert: every thread loads one expert's offsets (coalesced),
+    // tile counts are prefix-summed across the workgroup in LDS, and the
+    // thread whose range holds this tile publishes it
+    __shared__ int g_scan[256];
+    __shared__ int g_hit[4];                            // expert, first row, rows, tile within expert
+    const int bid = blockIdx.x;
+    if (tid == 0) g_hit[0] = -1;
+    int carry = 0;
+    for (int e0 = 0; e0 < n_groups; e0 += 256) {        // uniform
+      const int e = e0 + tid;
+      int st = 0, cnt = 0, te = 0;
+      if (tid < 256 && e < n_groups) {
+        st = min(max(group_offsets[e], 0), rows);
+        cnt = min(max(group_offsets[e + 1], st), rows) - st;
+        te = ((cnt + BM - 1) / BM) * tiles_n;
+      }
+      if (tid < 256) g_scan[tid] = te;
+      __syncthreads();
+      for (int off = 1; off < 256; off <<= 1) {         // inclusive Hillis-Steele scan
+        const int v = (tid < 256 && tid >= off) ? g_scan[tid - off] : 0;
+        __syncthreads();
+        if (tid < 256) g_scan[tid] += v;
+        __syncthreads();
+      }
+      if (tid < 256 && e < n_groups) {
+        const int incl = carry + g_scan[tid], excl = incl - te;
+        if (bid >= excl && bid < incl) {
+          g_hit[0] = e; g_hit[1] = st; g_hit[2] = cnt; g_hit[3] = bid - excl;
+        }
+      }
+      carry += g_scan[255];
+      __syncthreads();
     }
-    if (e >= n_groups) return;                          // surplus workgroup (uniform)
+    const int e = g_hit[0];
+    if (e < 0) return;                                  // surplus workgroup (uniform)
     grp = e;
+    const int start = g_hit[1], cnt = g_hit[2], b = g_hit[3];
     const int tm = b / tiles_n, tn = b % tiles_n;
     m0 = start + tm * BM;
     row_end = start + cnt;
