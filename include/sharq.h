@@ -161,6 +161,9 @@ sharq_status sharq_prepare(const void *X, int32_t dtype, int32_t T, int32_t K, i
  * nondecreasing, [0] = 0, [E] = total_rows): rows group_offsets[e] ..
  * group_offsets[e+1]-1 use expert e's weights; row_index as above.
  * Y: (device) fp32 total_rows x D, row r at Y + r * ldy (ldy >= D).
+ * Size limit: a->T * K / 2 and D * K / 2 (one group's payload) must each
+ * stay under 4 GiB - 256 bytes (32-bit buffer offsets), else
+ * UNSUPPORTED_SHAPE.
  * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, FORMAT_MISMATCH, HIP. */
 sharq_status sharq_linear(const sharq_act *a, const sharq_weight *w, const int32_t *group_offsets,
                           const int32_t *row_index, int32_t total_rows, float *Y, int64_t ldy,

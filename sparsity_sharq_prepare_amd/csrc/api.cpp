@@ -43,6 +43,7 @@ bool valid_dtype(int32_t d) { return d == SHARQ_F32 || d == SHARQ_BF16; }
 size_t dtype_size(int32_t d) { return d == SHARQ_F32 ? 4 : 2; }
 
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
+constexpr int64_t kMaxDescBytes = ((int64_t)1 << 32) - 256;
 
 sharq_status check_k(int32_t K, int mult) {
   if (K <= 0 || K % mult != 0)
@@ -197,6 +198,11 @@ sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, const int32
     if (!aligned16(p)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "activation / weight buffers must be 16-byte aligned");
   }
   if ((int64_t)total_rows * w->D > kMaxElems) return fail(SHARQ_ERR_UNSUPPORTED_SHAPE, "output too large");
+  // the GEMM kernels address activation and weight buffers through buffer
+  // descriptors with 32-bit byte offsets
+  if ((int64_t)a->T * (a->K / 2) > kMaxDescBytes || (int64_t)w->D * (w->K / 2) > kMaxDescBytes)
+    return fail(SHARQ_ERR_UNSUPPORTED_SHAPE, "activation residual (T*K/2) or per-group weight payload (D*K/2) over %lld bytes",
+                (long long)kMaxDescBytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (a->fmt == SHARQ_MXFP4) {
     return from_hip(sharq::launch_linear_mx(a->bb_codes, a->bb_meta, a->bb_scale, a->res_codes, a->res_scale,

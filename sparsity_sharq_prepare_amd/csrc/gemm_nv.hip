@@ -6,7 +6,9 @@
 // significant bits) and an E4M3 scale (4 significant bits) has at most 6
 // significant bits and is exact in bf16, so each operand element is
 // dequantized to q * dec(scale) in bf16 while staging and multiplied on the
-// bf16 MFMA (v_mfma_f32_16x16x32_bf16, exact products, fp32 accumulation).
+// bf16 MFMA (v_mfma_f32_32x32x16_bf16, exact products, fp32 accumulation).
+// (v_cvt_scalef32_pk_bf16_fp4 cannot do the dequantization: it applies only
+// the power-of-two part of its scale, measured on MI355X.)
 // The fp32 tensor scales differ between the paths, so the backbone and the
 // residual keep one accumulator each inside the same tile and the epilogue
 // forms Y = s_w * (s_sp * acc_sp + s_dn * acc_dn).
@@ -18,13 +20,17 @@ namespace sharq {
 namespace {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kNB = 128;                  // tile rows and columns
-constexpr int kKS = 64;                   // K per staged step
-constexpr int kRowB = kKS * 2;            // bytes of one staged bf16 row
+constexpr int kNM = 256;                  // tile rows
+constexpr int kNN = 128;                  // tile columns
+constexpr int kKS = 32;                   // K per step (one backbone block, two residual blocks)
 
-SHARQ_DEV v4f mfma_bf16(uint4 a, uint4 b, v4f c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+// 32x32x16 bf16: lane l holds row / column (l & 31), K-values 8 (l >> 5) .. +7
+// of the 16; result register i of lane l is row 8 (i / 4) + 4 (l >> 5) + i % 4,
+// column l & 31
+SHARQ_DEV v16f mfma_bf16(uint4 a, uint4 b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
 }
 
 // 8 E2M1 codes (one 32-bit word) times dec -> 8 bf16 (exact: q * dec has <= 6 significant bits)
@@ -39,124 +45,192 @@ SHARQ_DEV uint4 dequant8_bf16(uint32_t word, float dec) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// 16-byte slot of (row, chunk 0..7) in a staged bf16 tile (row = 128 bytes)
-SHARQ_DEV int nslot(int row, int q) { return row * 8 + (q ^ (row & 7)); }
+// 16-byte chunk q (0..3, 8 bf16) of a staged 64-byte row; the XOR keeps the
+// 16 rows of a read phase in distinct banks
+SHARQ_DEV int nslot(int row, int q) { return row * 4 + (q ^ (((row >> 1) ^ (row >> 3)) & 3)); }
 
 struct NvStage {
-  uint4 a_sp[kNB * 8];
-  uint4 a_dn[kNB * 8];
-  uint4 b[kNB * 8];
+  uint4 a_sp[kNM * 4];        // backbone, bf16, 64 B per row
+  uint4 a_dn[kNM * 4];        // residual
+  uint4 b[kNN * 4];           // weight columns
 };
+
+// expand 4 groups (8 compacted bytes + 4 metadata nibbles) into 16 code bytes
+SHARQ_DEV uint4 expand4(uint32_t c_lo, uint32_t c_hi, uint32_t meta16) {
+  const uint32_t m0 = (meta16 & 0x3333u) << 3, m1 = (meta16 & 0xCCCCu) << 1;
+  uint4 r;
+  r.x = ((c_lo & 0xFFu) << (m0 & 0x18u)) | (((c_lo >> 8) & 0xFFu) << (m1 & 0x18u));
+  r.y = (((c_lo >> 16) & 0xFFu) << ((m0 >> 4) & 0x18u)) | ((c_lo >> 24) << ((m1 >> 4) & 0x18u));
+  r.z = ((c_hi & 0xFFu) << ((m0 >> 8) & 0x18u)) | (((c_hi >> 8) & 0xFFu) << ((m1 >> 8) & 0x18u));
+  r.w = (((c_hi >> 16) & 0xFFu) << ((m0 >> 12) & 0x18u)) | ((c_hi >> 24) << ((m1 >> 12) & 0x18u));
+  return r;
+}
 
 }  // namespace
 
+// Tile 256 x 128, four waves (one per SIMD): wave w covers rows 64 w ..
+// and all 128 columns, with one accumulator per path (the two paths have
+// different tensor scales), 256 accumulator registers.  K advances 32 per step.
+//
+// Staging (no DMA: operands are dequantized on the way): every thread owns
+// one backbone row and one residual row of the tile, threads 0-127 also one
+// weight column; per step a thread loads its rows' 32 values (raw buffer
+// loads; rows and columns outside the tile read row 0, whose products reach
+// only outputs that are never stored), dequantizes them to bf16 and writes
+// 16-byte chunks to LDS.  Loads run two steps ahead; the dequantization of
+// step s+1 comes after step s's fragment reads so that it can fill the
+// shadow of step s's MFMAs.
 __global__ __launch_bounds__(256, 1) void linear_nv_tile(
     const uint8_t* __restrict__ bb_codes, const uint8_t* __restrict__ bb_meta, const uint8_t* __restrict__ bb_scale,
     const uint8_t* __restrict__ res_codes, const uint8_t* __restrict__ res_scale, const float* __restrict__ a_ts,
     const int32_t* __restrict__ row_index, int rows, int act_rows, int K, const uint8_t* __restrict__ payload,
     const uint8_t* __restrict__ wscale, const float* __restrict__ w_ts, int D, float* __restrict__ Y, int64_t ldy) {
   __shared__ NvStage st[2];
-  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
-  const int tiles_m = (rows + kNB - 1) / kNB;
-  const int tiles_n = (D + kNB - 1) / kNB;
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tiles_m = (rows + kNM - 1) / kNM, tiles_n = (D + kNN - 1) / kNN;
   const int nt = tiles_m * tiles_n;
-  int b = blockIdx.x;
-  if ((nt & 7) == 0) b = (b & 7) * (nt >> 3) + (b >> 3);
-  const int m0 = (b % tiles_m) * kNB, n0 = (b / tiles_m) * kNB;
-  const int64_t kA = K >> 2, kM = K >> 4, kS32 = K >> 5, kS16 = K >> 4, kR = K >> 1;
+  int bi = blockIdx.x;
+  if ((nt & 7) == 0) bi = (bi & 7) * (nt >> 3) + (bi >> 3);   // consecutive tiles on one XCD
+  const int m0 = (bi % tiles_m) * kNM, n0 = (bi / tiles_m) * kNN;
   const int KS = K / kKS;
+  const uint32_t kA = K >> 2, kM = K >> 4, kS32 = K >> 5, kS16 = K >> 4, kR = K >> 1;
 
-  // staging units: u = tid + 256 i (i < 4): row/col = u >> 3, group g = u & 7 (8 K-values)
-  const int g = tid & 7;
-  int64_t arow[4], brow[4];
-  bool aok[4], bok[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = m0 + ((tid + 256 * i) >> 3);
-    aok[i] = r < rows;
-    arow[i] = aok[i] ? gather_row(row_index, r, act_rows) : 0;
-    const int c = n0 + ((tid + 256 * i) >> 3);
-    bok[i] = c < D;
-    brow[i] = bok[i] ? c : 0;
-  }
-  uint32_t pc[4], pm[4], psb[4], pd[4], psd[4], pb[4], psw[4];
-  // branch-free staging loads (rows / columns outside the tile read row 0,
-  // whose products only reach outputs that are never stored)
-  auto load_step = [&](int s) {
-    const int gk = s * 8 + g;                   // global group index along K
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pc[i] = *reinterpret_cast<const uint16_t*>(bb_codes + arow[i] * kA + 2 * (int64_t)gk);
-      pm[i] = bb_meta[arow[i] * kM + (gk >> 1)];
-      psb[i] = bb_scale[arow[i] * kS32 + (gk >> 2)];
-      pd[i] = *reinterpret_cast<const uint32_t*>(res_codes + arow[i] * kR + 4 * (int64_t)gk);
-      psd[i] = res_scale[arow[i] * kS16 + (gk >> 1)];
-      pb[i] = *reinterpret_cast<const uint32_t*>(payload + brow[i] * kR + 4 * (int64_t)gk);
-      psw[i] = wscale[brow[i] * kS32 + (gk >> 2)];
+  auto rsrc = [](const uint8_t* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0,
+                                             __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
+  };
+  const int an = __builtin_amdgcn_readfirstlane(act_rows);
+  const __amdgpu_buffer_rsrc_t r_bc = rsrc(bb_codes, (int64_t)an * kA), r_bm = rsrc(bb_meta, (int64_t)an * kM);
+  const __amdgpu_buffer_rsrc_t r_bs = rsrc(bb_scale, (int64_t)an * kS32), r_rc = rsrc(res_codes, (int64_t)an * kR);
+  const __amdgpu_buffer_rsrc_t r_rs = rsrc(res_scale, (int64_t)an * kS16);
+  const __amdgpu_buffer_rsrc_t r_w = rsrc(payload, (int64_t)D * kR), r_ws = rsrc(wscale, (int64_t)D * kS32);
+
+  // ---- staging roles
+  const bool b_role = w < 2;                           // waves 0-1: also weight columns (uniform)
+  const int srow = tid;
+  const int gr = m0 + srow;
+  const uint32_t ar = gr < rows ? (uint32_t)gather_row(row_index, gr, act_rows) : 0u;
+  const int gc = n0 + (tid & 127);
+  const uint32_t wc = gc < D ? (uint32_t)gc : 0u;
+
+  struct Ld {
+    uint2 bc;            // backbone: compacted codes of 4 groups
+    uint32_t bm, bsc;    // backbone metadata (16 bits), scale byte
+    uint4 rc;            // residual codes (16 B)
+    uint32_t rsc;        // residual: two scale bytes
+    uint4 wcd;           // weight codes
+    uint32_t wsc;        // weight scale byte
+  };
+  auto load = [&](int s, Ld& L) {
+    const uint32_t ss = (uint32_t)min(s, KS - 1);      // past the end: reload the last step (unused)
+    const auto c = __builtin_amdgcn_raw_buffer_load_b64(r_bc, ar * kA + 8u * ss, 0, 0);
+    L.bc = make_uint2(c[0], c[1]);
+    L.bm = __builtin_amdgcn_raw_buffer_load_b16(r_bm, ar * kM + 2u * ss, 0, 0);
+    L.bsc = __builtin_amdgcn_raw_buffer_load_b8(r_bs, ar * kS32 + ss, 0, 0);
+    const auto r = __builtin_amdgcn_raw_buffer_load_b128(r_rc, ar * kR + 16u * ss, 0, 0);
+    L.rc = make_uint4(r[0], r[1], r[2], r[3]);
+    L.rsc = __builtin_amdgcn_raw_buffer_load_b16(r_rs, ar * kS16 + 2u * ss, 0, 0);
+    if (b_role) {
+      const auto b = __builtin_amdgcn_raw_buffer_load_b128(r_w, wc * kR + 16u * ss, 0, 0);
+      L.wcd = make_uint4(b[0], b[1], b[2], b[3]);
+      L.wsc = __builtin_amdgcn_raw_buffer_load_b8(r_ws, wc * kS32 + ss, 0, 0);
     }
   };
-  auto store_step = [&](NvStage& S) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rc = (tid + 256 * i) >> 3;
-      const uint32_t nib = (g & 1) ? (pm[i] >> 4) : (pm[i] & 15u);
-      S.a_sp[nslot(rc, g)] = dequant8_bf16(expand_group(pc[i], nib), e4m3_decode(psb[i]));
-      S.a_dn[nslot(rc, g)] = dequant8_bf16(pd[i], e4m3_decode(psd[i]));
-      S.b[nslot(rc, g)] = dequant8_bf16(pb[i], e4m3_decode(psw[i]));
+  auto store = [&](const Ld& L, NvStage& S) {
+    const uint4 e = expand4(L.bc.x, L.bc.y, L.bm);
+    const float dec = e4m3_decode(L.bsc & 0xFFu);
+    S.a_sp[nslot(srow, 0)] = dequant8_bf16(e.x, dec);
+    S.a_sp[nslot(srow, 1)] = dequant8_bf16(e.y, dec);
+    S.a_sp[nslot(srow, 2)] = dequant8_bf16(e.z, dec);
+    S.a_sp[nslot(srow, 3)] = dequant8_bf16(e.w, dec);
+    const float d0 = e4m3_decode(L.rsc & 0xFFu), d1 = e4m3_decode((L.rsc >> 8) & 0xFFu);
+    S.a_dn[nslot(srow, 0)] = dequant8_bf16(L.rc.x, d0);
+    S.a_dn[nslot(srow, 1)] = dequant8_bf16(L.rc.y, d0);
+    S.a_dn[nslot(srow, 2)] = dequant8_bf16(L.rc.z, d1);
+    S.a_dn[nslot(srow, 3)] = dequant8_bf16(L.rc.w, d1);
+    if (b_role) {
+      const float db = e4m3_decode(L.wsc & 0xFFu);
+      const int cc = tid & 127;
+      S.b[nslot(cc, 0)] = dequant8_bf16(L.wcd.x, db);
+      S.b[nslot(cc, 1)] = dequant8_bf16(L.wcd.y, db);
+      S.b[nslot(cc, 2)] = dequant8_bf16(L.wcd.z, db);
+      S.b[nslot(cc, 3)] = dequant8_bf16(L.wcd.w, db);
     }
   };
 
-  const int wm0 = (w >> 1) * 64, wn0 = (w & 1) * 64;
-  const int kq = l >> 4, lr = l & 15;
-  v4f acc_sp[4][4], acc_dn[4][4];
+  // ---- MFMA fragments and accumulators
+  const int wm0 = w * 64;
+  const int kh = l >> 5, lr = l & 31;
+  v16f acc_sp[2][4], acc_dn[2][4];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < 2; ++f)
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-      acc_sp[f][n] = (v4f){0.f, 0.f, 0.f, 0.f};
-      acc_dn[f][n] = (v4f){0.f, 0.f, 0.f, 0.f};
+      acc_sp[f][n] = (v16f){};
+      acc_dn[f][n] = (v16f){};
     }
-
-  load_step(0);
-  store_step(st[0]);
-  __syncthreads();
-  for (int s = 0; s < KS; ++s) {
-    load_step(min(s + 1, KS - 1));              // the last step reloads itself (unused)
-    __builtin_amdgcn_sched_barrier(0);          // issue the prefetch before this step's MFMAs
-    const NvStage& S = st[s & 1];
+  struct Frag {
+    uint4 sp[2][2], dn[2][2], b[2][4];   // [k-slice][f or n]
+  };
+  auto read = [&](const NvStage& S, Frag& F) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {             // two MFMA K-steps of 32
-      const int q = 4 * ks + kq;                 // 16-byte chunk: K = 8 q .. 8 q + 7
-      uint4 bf[4];
+    for (int ks = 0; ks < 2; ++ks) {
+      const int q = 2 * ks + kh;                       // chunk: K-values 8 q .. 8 q + 7
 #pragma unroll
-      for (int n = 0; n < 4; ++n) bf[n] = S.b[nslot(wn0 + 16 * n + lr, q)];
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const int r = wm0 + 16 * f + lr;
-        const uint4 asp = S.a_sp[nslot(r, q)];
-        const uint4 adn = S.a_dn[nslot(r, q)];
-#pragma unroll
-        for (int n = 0; n < 4; ++n) acc_sp[f][n] = mfma_bf16(asp, bf[n], acc_sp[f][n]);
-#pragma unroll
-        for (int n = 0; n < 4; ++n) acc_dn[f][n] = mfma_bf16(adn, bf[n], acc_dn[f][n]);
+      for (int f = 0; f < 2; ++f) {
+        F.sp[ks][f] = S.a_sp[nslot(wm0 + 32 * f + lr, q)];
+        F.dn[ks][f] = S.a_dn[nslot(wm0 + 32 * f + lr, q)];
       }
+#pragma unroll
+      for (int n = 0; n < 4; ++n) F.b[ks][n] = S.b[nslot(32 * n + lr, q)];
     }
-    // keep the staging writes (which wait for the prefetched global loads)
-    // behind this step's MFMAs, so the load latency hides under them
-    __builtin_amdgcn_sched_barrier(0);
-    store_step(st[(s + 1) & 1]);
+  };
+  auto mfma = [&](const Frag& F) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          acc_sp[f][n] = mfma_bf16(F.sp[ks][f], F.b[ks][n], acc_sp[f][n]);
+          acc_dn[f][n] = mfma_bf16(F.dn[ks][f], F.b[ks][n], acc_dn[f][n]);
+        }
+  };
+
+  Ld l0, l1;
+  Frag fr;
+  load(0, l0);
+  load(1, l1);
+  store(l0, st[0]);
+  __syncthreads();
+  // K % 128 == 0 (checked by the caller), so the number of steps is even
+  for (int s = 0; s < KS; s += 2) {
+    // step s: st[0] holds step s, st[1] receives step s+1
+    load(s + 2, l0);
+    read(st[0], fr);
+    store(l1, st[1]);
+    mfma(fr);
+    __syncthreads();
+    // step s+1
+    load(s + 3, l1);
+    read(st[1], fr);
+    store(l0, st[0]);
+    mfma(fr);
     __syncthreads();
   }
+
+  // ---- epilogue: Y = s_w * (s_sp * acc_sp + s_dn * acc_dn)
   const float s_sp = a_ts[0], s_dn = a_ts[1], s_w = w_ts[0];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
+  for (int f = 0; f < 2; ++f) {
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-      const int c = n0 + wn0 + 16 * n + lr;
+      const int c = n0 + 32 * n + lr;
       if (c >= D) continue;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = m0 + wm0 + 16 * f + 4 * kq + i;
+      for (int i = 0; i < 16; ++i) {
+        const int r = m0 + wm0 + 32 * f + 8 * (i >> 2) + 4 * kh + (i & 3);
         if (r < rows) Y[(int64_t)r * ldy + c] = s_w * (s_sp * acc_sp[f][n][i] + s_dn * acc_dn[f][n][i]);
       }
     }
@@ -168,7 +242,7 @@ hipError_t launch_linear_nv(const uint8_t* bb_codes, const uint8_t* bb_meta, con
                             const int32_t* row_index, int rows, int act_rows, int K, const uint8_t* payload,
                             const uint8_t* wscale, const float* w_ts, int D, float* Y, int64_t ldy, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  const int nt = ((rows + kNB - 1) / kNB) * ((D + kNB - 1) / kNB);
+  const int nt = ((rows + kNM - 1) / kNM) * ((D + kNN - 1) / kNN);
   hipLaunchKernelGGL(linear_nv_tile, dim3(nt), dim3(256), 0, s, bb_codes, bb_meta, bb_scale, res_codes, res_scale,
                      a_ts, row_index, rows, act_rows, K, payload, wscale, w_ts, D, Y, ldy);
   return hipGetLastError();

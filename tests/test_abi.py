@@ -83,6 +83,13 @@ def test_linear_validation_errors():
     assert lib.sharq_linear(a, _fake_weight(G=4), None, None, 8, Y, 64, None) == L.SHARQ_ERR_INVALID_ARGUMENT
     assert lib.sharq_linear(_fake_act(fmt=1), _fake_weight(fmt=1, G=4), 0x40000, None, 8, Y, 64, None) == \
         L.SHARQ_ERR_UNSUPPORTED_SHAPE
+    # buffers past the 32-bit buffer-descriptor range
+    big_t = (1 << 33) // 4096
+    assert lib.sharq_linear(_fake_act(T=big_t, K=4096), _fake_weight(K=4096), None, None, 8, Y, 64, None) == \
+        L.SHARQ_ERR_UNSUPPORTED_SHAPE
+    assert lib.sharq_linear(_fake_act(K=4096), _fake_weight(K=4096, D=big_t), None, None, 8, Y, big_t, None) == \
+        L.SHARQ_ERR_UNSUPPORTED_SHAPE
+    assert "bytes" in lib.sharq_last_error().decode()
     # null activation buffer
     bad = _fake_act()
     bad.res_codes = None
