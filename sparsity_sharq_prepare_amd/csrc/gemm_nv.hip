@@ -45,9 +45,11 @@ SHARQ_DEV uint4 dequant8_bf16(uint32_t word, float dec) {
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// 16-byte chunk q (0..3, 8 bf16) of a staged 64-byte row; the XOR keeps the
-// 16 rows of a read phase in distinct banks
-SHARQ_DEV int nslot(int row, int q) { return row * 4 + (q ^ (((row >> 1) ^ (row >> 3)) & 3)); }
+// 16-byte chunk q (0..3, 8 bf16) of a staged 64-byte row.  A 16-byte LDS
+// access is served 16 lanes at a time over 256 bytes of banks; 16
+// consecutive rows at one chunk land on 4 (row & 3) x 4 (q ^ ((row >> 2) & 3))
+// distinct 16-byte bank groups, so reads and writes are conflict-free
+SHARQ_DEV int nslot(int row, int q) { return row * 4 + (q ^ ((row >> 2) & 3)); }
 
 struct NvStage {
   uint4 a_sp[kNM * 4];        // backbone, bf16, 64 B per row
