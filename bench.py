@@ -69,6 +69,9 @@ class Job:
         self.act = ops.empty_act(fmt, X.shape[0], K, X.device)
         self.Y = torch.empty((self.rows, D), dtype=torch.float32, device=X.device)
         self.groups = weights[0].n_groups
+        # decode linears: also timed as one launch (sharq_prepare_linear)
+        self.fused = fmt == "mxfp4" and self.groups == 1 and rows is None and T <= 8
+        self.step_fused = False          # the step uses it when it is the faster form
 
     # algorithmic work (SURVEY-defined units)
     def gemm_flops_nominal(self):
@@ -89,6 +92,10 @@ class Job:
         xb = self.X.element_size()
         out = 0.875 if self.fmt == "mxfp4" else 0.90625
         return self.X.shape[0] * self.K * (xb + out) + 4.0 * self.K
+
+    def fused_bytes(self):               # X, gamma and weights in; prepared activations and Y out
+        w = self.D * self.K * (0.5 + 1.0 / 32)
+        return w + self.prep_bytes() + 4.0 * self.rows * self.D
 
 
 def _dev(a, bf16=True):
@@ -163,6 +170,9 @@ def run_step(jobs, it):
     from sparsity_sharq_prepare_amd import ops
     for job in jobs:
         w = job.weights[it % len(job.weights)]
+        if job.step_fused:
+            ops.prepare_linear(job.Xs[it % len(job.Xs)], job.gamma, w, 1e-6, act=job.act, out=job.Y)
+            continue
         ops.prepare(job.Xs[it % len(job.Xs)], job.gamma, 1e-6, job.fmt, out=job.act)
         ops.linear(job.act, w, group_offsets=job.group_offsets, row_index=job.row_index, total_rows=job.rows,
                    out=job.Y)
@@ -209,12 +219,13 @@ def timed(jobs, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     n_steps = steps
-    prep_ms, gemm_ms = kernel_times(jobs, R)
-    return wall, n_steps, prep_ms, gemm_ms
+    prep_ms, gemm_ms, fused_ms = kernel_times(jobs, R)
+    return wall, n_steps, prep_ms, gemm_ms, fused_ms
 
 
 def kernel_times(jobs, R, reps=3):
-    """Average launch duration of each job's prepare and GEMM: a HIP graph of
+    """Average launch duration of each job's prepare, GEMM and (decode) single-
+    launch prepare + GEMM: a HIP graph of
     R back-to-back launches of that kernel alone (the GEMM rotating over the R
     weight copies, the prepare over the input copies), replayed `reps` times
     between two HIP events on the stream it runs on, divided by the launch
@@ -222,7 +233,7 @@ def kernel_times(jobs, R, reps=3):
     the timed steps, so this agrees with a kernel trace of the same run."""
     import torch
     from sparsity_sharq_prepare_amd import ops
-    prep_ms, gemm_ms = [], []
+    prep_ms, gemm_ms, fused_ms = [], [], []
     for job in jobs:
         gp, gg = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
         with torch.cuda.graph(gp):
@@ -232,8 +243,16 @@ def kernel_times(jobs, R, reps=3):
             for i in range(R):
                 ops.linear(job.act, job.weights[i % len(job.weights)], group_offsets=job.group_offsets,
                            row_index=job.row_index, total_rows=job.rows, out=job.Y)
+        graphs = [gp, gg]
+        if job.fused:
+            gf = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gf):
+                for i in range(R):
+                    ops.prepare_linear(job.Xs[i % len(job.Xs)], job.gamma, job.weights[i % len(job.weights)],
+                                       1e-6, act=job.act, out=job.Y)
+            graphs.append(gf)
         res = []
-        for g in (gp, gg):
+        for g in graphs:
             g.replay()                                  # warm
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -245,7 +264,8 @@ def kernel_times(jobs, R, reps=3):
             res.append(e0.elapsed_time(e1) / (reps * R))
         prep_ms.append(res[0])
         gemm_ms.append(res[1])
-    return prep_ms, gemm_ms
+        fused_ms.append(res[2] if job.fused else None)
+    return prep_ms, gemm_ms, fused_ms
 
 
 # ----------------------------------------------------------------------------
@@ -368,7 +388,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     jobs, cases, pack_times = build_jobs(args.workload, args.copies)
-    wall, n_steps, prep_ms, gemm_ms = timed(jobs, args.steps, args.warmup)
+    wall, n_steps, prep_ms, gemm_ms, fused_ms = timed(jobs, args.steps, args.warmup)
     ms_step = wall * 1e3 / n_steps
 
     nominal = sum(j.gemm_flops_nominal() for j in jobs)
@@ -379,29 +399,37 @@ def main():
     gemm_total_ms = sum(gemm_ms)
     prep_total_ms = sum(prep_ms)
     kernels = {}
-    for j, p, g in zip(jobs, prep_ms, gemm_ms):
+    for j, p, g, f in zip(jobs, prep_ms, gemm_ms, fused_ms):
         kernels[j.name] = {
             "prepare_us": round(p * 1e3, 2), "prepare_GBs": round(j.prep_bytes() / (p * 1e-3) / 1e9, 1),
             "gemm_us": round(g * 1e3, 2), "gemm_GBs": round(j.gemm_bytes() / (g * 1e-3) / 1e9, 1),
             "gemm_TFLOPS_alg": round(j.gemm_flops_alg() / (g * 1e-3) / 1e12, 1),
             "gemm_TFLOPS_issued": round(j.gemm_flops_issued() / (g * 1e-3) / 1e12, 1),
         }
+        if f is not None:
+            kernels[j.name]["prepare_linear_us"] = round(f * 1e3, 2)
+            kernels[j.name]["prepare_linear_GBs"] = round(j.fused_bytes() / (f * 1e-3) / 1e9, 1)
     n = len(jobs)
-    if args.workload == "decode":
+    if args.workload == "decode" and any(j.step_fused for j in jobs):
+        # the step runs one single-launch prepare + GEMM kernel per linear
+        dom, bound, unit, peak = "linear_mx_decode", "hbm", "GB/s", HBM_PEAK_GBS
+        fused_total_ms = sum(fused_ms)
+        ach = sum(j.fused_bytes() for j in jobs) / n / (fused_total_ms / n * 1e-3) / 1e9
+        gemm_total_ms = fused_total_ms
+    elif args.workload == "decode":
         dom, bound, unit, peak = "linear_mx_decode", "hbm", "GB/s", HBM_PEAK_GBS
         ach = sum(j.gemm_bytes() for j in jobs) / n / (gemm_total_ms / n * 1e-3) / 1e9
-        src = ["gemm_mx.hip", "common.h"]
     elif args.workload == "nvfp4":
         dom, bound, unit, peak = "linear_nv_tile", "mfma", "TFLOP/s", BF16_PEAK_TFLOPS
         ach = sum(j.gemm_flops_alg() for j in jobs) / n / (gemm_total_ms / n * 1e-3) / 1e12
-        src = ["gemm_nv.hip", "common.h"]
     else:
         dom = "linear_mx_tile"
         bound, unit, peak = "mfma", "TFLOP/s", FP4_PEAK_TFLOPS
         ach = sum(j.gemm_flops_alg() for j in jobs) / n / (gemm_total_ms / n * 1e-3) / 1e12
-        src = ["gemm_mx.hip", "common.h"]
+
+    from sparsity_sharq_prepare_amd.profiling import SOURCES
     roofline = {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
-                "frac": round(ach / peak, 4), "traffic": read_traffic(f"{dom}_{args.workload}", src),
+                "frac": round(ach / peak, 4), "traffic": read_traffic(f"{dom}_{args.workload}", SOURCES[dom]),
                 "kernel": dom, "launch_us": round(gemm_total_ms / n * 1e3, 2)}
     prep_ach = sum(j.prep_bytes() for j in jobs) / (prep_total_ms * 1e-3) / 1e9
     pack_us = sum(t for t, _ in pack_times) / len(pack_times)

@@ -169,6 +169,29 @@ sharq_status sharq_linear(const sharq_act *a, const sharq_weight *w, const int32
                           const int32_t *row_index, int32_t total_rows, float *Y, int64_t ldy,
                           void *stream);
 
+/* Single-launch decode (review §3.5: preparation fused ahead of the dual-
+ * path GEMM, here in the same kernel launch): sharq_prepare of the T rows
+ * of X into act, then sharq_linear(act, w) into Y (plain linear: row t of Y
+ * from activation row t, total_rows = T).  For T <= 8 and K <= 16384 one
+ * kernel does both: its first T workgroups prepare one row each and signal
+ * through counters in `workspace`; the GEMM workgroups stream their weights
+ * meanwhile and wait (bounded polling) before reading the activations.
+ * Larger shapes run sharq_prepare's and sharq_linear's kernels one after the
+ * other.  Either way act holds exactly sharq_prepare's bytes and Y exactly
+ * sharq_linear's values.
+ * X, dtype, T, K, ldx, gamma, eps: as sharq_prepare; act: (host) MXFP4
+ * activation buffers for T rows; w: (host) MXFP4 weight, n_groups == 1;
+ * Y, ldy: as sharq_linear.
+ * workspace: (device) >= 8 bytes, 16-byte aligned, all zero before the first
+ * call; every call leaves it zero.  Calls that share a workspace must not
+ * run concurrently.
+ * Errors: INVALID_ARGUMENT (also for NVFP4 or n_groups > 1),
+ * UNSUPPORTED_SHAPE, FORMAT_MISMATCH, WORKSPACE_TOO_SMALL, HIP. */
+sharq_status sharq_prepare_linear(const void *X, int32_t dtype, int32_t T, int32_t K, int64_t ldx,
+                                  const float *gamma, float eps, const sharq_act *act,
+                                  const sharq_weight *w, float *Y, int64_t ldy, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 /* Static string naming a status code. */
 const char *sharq_status_string(sharq_status s);
 

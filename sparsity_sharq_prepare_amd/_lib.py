@@ -28,7 +28,7 @@ FORMATS = {"mxfp4": SHARQ_MXFP4, "nvfp4": SHARQ_NVFP4_EMU}
 
 # every entry point include/sharq.h declares
 EXPORTS = ("sharq_weight_sizes", "sharq_act_sizes", "sharq_pack_weight", "sharq_prepare", "sharq_linear",
-           "sharq_status_string", "sharq_last_error")
+           "sharq_prepare_linear", "sharq_status_string", "sharq_last_error")
 
 
 class SharqWeight(ctypes.Structure):
@@ -67,7 +67,11 @@ def lib() -> ctypes.CDLL:
                                     POINTER(SharqAct), c_void_p, c_size_t, c_void_p]
         L.sharq_linear.argtypes = [POINTER(SharqAct), POINTER(SharqWeight), c_void_p, c_void_p, c_int32,
                                    c_void_p, c_int64, c_void_p]
-        for name in ("sharq_weight_sizes", "sharq_act_sizes", "sharq_pack_weight", "sharq_prepare", "sharq_linear"):
+        L.sharq_prepare_linear.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_int64, c_void_p, c_float,
+                                           POINTER(SharqAct), POINTER(SharqWeight), c_void_p, c_int64, c_void_p,
+                                           c_size_t, c_void_p]
+        for name in ("sharq_weight_sizes", "sharq_act_sizes", "sharq_pack_weight", "sharq_prepare", "sharq_linear",
+                     "sharq_prepare_linear"):
             getattr(L, name).restype = c_int32
         L.sharq_status_string.argtypes = [c_int32]
         L.sharq_status_string.restype = c_char_p

@@ -51,6 +51,76 @@ sharq_status check_k(int32_t K, int mult) {
   return SHARQ_OK;
 }
 
+// argument checks shared by the entry points (nothing is enqueued)
+sharq_status prepare_checks(const void* X, int32_t dtype, int32_t T, int32_t K, int64_t ldx, const float* gamma,
+                            float eps, const sharq_act* out, void* workspace, size_t workspace_bytes) {
+  if (!X || !out) return fail(SHARQ_ERR_INVALID_ARGUMENT, "X and out must not be NULL");
+  if (!valid_dtype(dtype)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  size_t sz[7];
+  if (sharq_status s = sharq_act_sizes(out->fmt, T, K, sz)) return s;
+  if (K > sharq::prepare_max_k())
+    return fail(SHARQ_ERR_UNSUPPORTED_SHAPE, "K = %d exceeds the supported maximum %d", K, sharq::prepare_max_k());
+  if (out->T != T || out->K != K)
+    return fail(SHARQ_ERR_INVALID_ARGUMENT, "out describes T=%d K=%d, call has T=%d K=%d", out->T, out->K, T, K);
+  if (ldx < K) return fail(SHARQ_ERR_INVALID_ARGUMENT, "ldx = %lld < K = %d", (long long)ldx, K);
+  if (!aligned16(X) || ((size_t)ldx * dtype_size(dtype)) % 16 != 0)
+    return fail(SHARQ_ERR_INVALID_ARGUMENT, "X rows must start 16-byte aligned");
+  if (gamma && !aligned16(gamma)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "gamma must be 16-byte aligned");
+  if (!(eps >= 0.0f)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "eps must be >= 0");
+  const uint8_t* bufs[5] = {out->bb_codes, out->bb_meta, out->bb_scale, out->res_codes, out->res_scale};
+  for (const uint8_t* p : bufs) {
+    if (!p) return fail(SHARQ_ERR_INVALID_ARGUMENT, "output buffers must not be NULL");
+    if (!aligned16(p)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "output buffers must be 16-byte aligned");
+  }
+  if (out->fmt == SHARQ_NVFP4_EMU) {
+    if (!out->tensor_scales) return fail(SHARQ_ERR_INVALID_ARGUMENT, "NVFP4 activations need tensor_scales");
+    if (!workspace || workspace_bytes < sz[6])
+      return fail(SHARQ_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", sz[6], workspace_bytes);
+    if (!aligned16(workspace)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  }
+  return SHARQ_OK;
+}
+
+sharq_status linear_checks(const sharq_act* a, const sharq_weight* w, const int32_t* group_offsets,
+                           const int32_t* row_index, int32_t total_rows, float* Y, int64_t ldy) {
+  if (!a || !w || !Y) return fail(SHARQ_ERR_INVALID_ARGUMENT, "a, w and Y must not be NULL");
+  if (!valid_fmt(a->fmt) || !valid_fmt(w->fmt)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "unknown format");
+  if (a->fmt != w->fmt)
+    return fail(SHARQ_ERR_FORMAT_MISMATCH, "activation format %d != weight format %d", a->fmt, w->fmt);
+  if (a->K != w->K) return fail(SHARQ_ERR_FORMAT_MISMATCH, "activation K = %d != weight K = %d", a->K, w->K);
+  if (sharq_status s = check_k(a->K, 128)) return s;
+  if (a->T < 1 || w->D < 1 || w->n_groups < 1)
+    return fail(SHARQ_ERR_UNSUPPORTED_SHAPE, "T, D and n_groups must be >= 1");
+  if (total_rows < 0) return fail(SHARQ_ERR_INVALID_ARGUMENT, "total_rows < 0");
+  if (ldy < w->D) return fail(SHARQ_ERR_INVALID_ARGUMENT, "ldy = %lld < D = %d", (long long)ldy, w->D);
+  if (!aligned16(Y)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "Y must be 16-byte aligned");
+  if (w->n_groups == 1) {
+    if (group_offsets) return fail(SHARQ_ERR_INVALID_ARGUMENT, "group_offsets must be NULL for one group");
+    if (!row_index && total_rows > a->T)
+      return fail(SHARQ_ERR_INVALID_ARGUMENT, "total_rows = %d > T = %d without row_index", total_rows, a->T);
+  } else {
+    if (!group_offsets) return fail(SHARQ_ERR_INVALID_ARGUMENT, "grouped linear needs group_offsets");
+    if (!row_index && total_rows > a->T)
+      return fail(SHARQ_ERR_INVALID_ARGUMENT, "total_rows = %d > T = %d without row_index", total_rows, a->T);
+    if (w->fmt != SHARQ_MXFP4) return fail(SHARQ_ERR_UNSUPPORTED_SHAPE, "grouped linear supports MXFP4 only");
+  }
+  const uint8_t* bufs[7] = {a->bb_codes, a->bb_meta, a->bb_scale, a->res_codes, a->res_scale, w->payload,
+                            w->scale_sp};
+  for (const uint8_t* p : bufs) {
+    if (!p) return fail(SHARQ_ERR_INVALID_ARGUMENT, "activation / weight buffers must not be NULL");
+    if (!aligned16(p)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "activation / weight buffers must be 16-byte aligned");
+  }
+  if ((int64_t)total_rows * w->D > kMaxElems) return fail(SHARQ_ERR_UNSUPPORTED_SHAPE, "output too large");
+  // the GEMM kernels address activation and weight buffers through buffer
+  // descriptors with 32-bit byte offsets
+  if ((int64_t)a->T * (a->K / 2) > kMaxDescBytes || (int64_t)w->D * (w->K / 2) > kMaxDescBytes)
+    return fail(SHARQ_ERR_UNSUPPORTED_SHAPE, "activation residual (T*K/2) or per-group weight payload (D*K/2) over %lld bytes",
+                (long long)kMaxDescBytes);
+  if (a->fmt == SHARQ_NVFP4_EMU && (!a->tensor_scales || !w->tensor_scale))
+    return fail(SHARQ_ERR_INVALID_ARGUMENT, "NVFP4 needs activation and weight tensor scales");
+  return SHARQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -134,34 +204,13 @@ sharq_status sharq_pack_weight(const void* W, int32_t dtype, int32_t K, int32_t 
 
 sharq_status sharq_prepare(const void* X, int32_t dtype, int32_t T, int32_t K, int64_t ldx, const float* gamma,
                            float eps, const sharq_act* out, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!X || !out) return fail(SHARQ_ERR_INVALID_ARGUMENT, "X and out must not be NULL");
-  if (!valid_dtype(dtype)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
-  size_t sz[7];
-  if (sharq_status s = sharq_act_sizes(out->fmt, T, K, sz)) return s;
-  if (K > sharq::prepare_max_k())
-    return fail(SHARQ_ERR_UNSUPPORTED_SHAPE, "K = %d exceeds the supported maximum %d", K, sharq::prepare_max_k());
-  if (out->T != T || out->K != K)
-    return fail(SHARQ_ERR_INVALID_ARGUMENT, "out describes T=%d K=%d, call has T=%d K=%d", out->T, out->K, T, K);
-  if (ldx < K) return fail(SHARQ_ERR_INVALID_ARGUMENT, "ldx = %lld < K = %d", (long long)ldx, K);
-  if (!aligned16(X) || ((size_t)ldx * dtype_size(dtype)) % 16 != 0)
-    return fail(SHARQ_ERR_INVALID_ARGUMENT, "X rows must start 16-byte aligned");
-  if (gamma && !aligned16(gamma)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "gamma must be 16-byte aligned");
-  if (!(eps >= 0.0f)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "eps must be >= 0");
-  const uint8_t* bufs[5] = {out->bb_codes, out->bb_meta, out->bb_scale, out->res_codes, out->res_scale};
-  for (const uint8_t* p : bufs) {
-    if (!p) return fail(SHARQ_ERR_INVALID_ARGUMENT, "output buffers must not be NULL");
-    if (!aligned16(p)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "output buffers must be 16-byte aligned");
-  }
+  if (sharq_status st = prepare_checks(X, dtype, T, K, ldx, gamma, eps, out, workspace, workspace_bytes)) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (out->fmt == SHARQ_MXFP4) {
     return from_hip(sharq::launch_prepare_mx(X, dtype == SHARQ_BF16, T, K, ldx, gamma, eps, out->bb_codes,
                                              out->bb_meta, out->bb_scale, out->res_codes, out->res_scale, s),
                     "sharq_prepare launch");
   }
-  if (!out->tensor_scales) return fail(SHARQ_ERR_INVALID_ARGUMENT, "NVFP4 activations need tensor_scales");
-  if (!workspace || workspace_bytes < sz[6])
-    return fail(SHARQ_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes, got %zu", sz[6], workspace_bytes);
-  if (!aligned16(workspace)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
   return from_hip(sharq::launch_prepare_nv(X, dtype == SHARQ_BF16, T, K, ldx, gamma, eps, out->bb_codes,
                                            out->bb_meta, out->bb_scale, out->res_codes, out->res_scale,
                                            out->tensor_scales, workspace, s),
@@ -170,39 +219,7 @@ sharq_status sharq_prepare(const void* X, int32_t dtype, int32_t T, int32_t K, i
 
 sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, const int32_t* group_offsets,
                           const int32_t* row_index, int32_t total_rows, float* Y, int64_t ldy, void* stream) {
-  if (!a || !w || !Y) return fail(SHARQ_ERR_INVALID_ARGUMENT, "a, w and Y must not be NULL");
-  if (!valid_fmt(a->fmt) || !valid_fmt(w->fmt)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "unknown format");
-  if (a->fmt != w->fmt)
-    return fail(SHARQ_ERR_FORMAT_MISMATCH, "activation format %d != weight format %d", a->fmt, w->fmt);
-  if (a->K != w->K) return fail(SHARQ_ERR_FORMAT_MISMATCH, "activation K = %d != weight K = %d", a->K, w->K);
-  if (sharq_status s = check_k(a->K, 128)) return s;
-  if (a->T < 1 || w->D < 1 || w->n_groups < 1)
-    return fail(SHARQ_ERR_UNSUPPORTED_SHAPE, "T, D and n_groups must be >= 1");
-  if (total_rows < 0) return fail(SHARQ_ERR_INVALID_ARGUMENT, "total_rows < 0");
-  if (ldy < w->D) return fail(SHARQ_ERR_INVALID_ARGUMENT, "ldy = %lld < D = %d", (long long)ldy, w->D);
-  if (!aligned16(Y)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "Y must be 16-byte aligned");
-  if (w->n_groups == 1) {
-    if (group_offsets) return fail(SHARQ_ERR_INVALID_ARGUMENT, "group_offsets must be NULL for one group");
-    if (!row_index && total_rows > a->T)
-      return fail(SHARQ_ERR_INVALID_ARGUMENT, "total_rows = %d > T = %d without row_index", total_rows, a->T);
-  } else {
-    if (!group_offsets) return fail(SHARQ_ERR_INVALID_ARGUMENT, "grouped linear needs group_offsets");
-    if (!row_index && total_rows > a->T)
-      return fail(SHARQ_ERR_INVALID_ARGUMENT, "total_rows = %d > T = %d without row_index", total_rows, a->T);
-    if (w->fmt != SHARQ_MXFP4) return fail(SHARQ_ERR_UNSUPPORTED_SHAPE, "grouped linear supports MXFP4 only");
-  }
-  const uint8_t* bufs[7] = {a->bb_codes, a->bb_meta, a->bb_scale, a->res_codes, a->res_scale, w->payload,
-                            w->scale_sp};
-  for (const uint8_t* p : bufs) {
-    if (!p) return fail(SHARQ_ERR_INVALID_ARGUMENT, "activation / weight buffers must not be NULL");
-    if (!aligned16(p)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "activation / weight buffers must be 16-byte aligned");
-  }
-  if ((int64_t)total_rows * w->D > kMaxElems) return fail(SHARQ_ERR_UNSUPPORTED_SHAPE, "output too large");
-  // the GEMM kernels address activation and weight buffers through buffer
-  // descriptors with 32-bit byte offsets
-  if ((int64_t)a->T * (a->K / 2) > kMaxDescBytes || (int64_t)w->D * (w->K / 2) > kMaxDescBytes)
-    return fail(SHARQ_ERR_UNSUPPORTED_SHAPE, "activation residual (T*K/2) or per-group weight payload (D*K/2) over %lld bytes",
-                (long long)kMaxDescBytes);
+  if (sharq_status st = linear_checks(a, w, group_offsets, row_index, total_rows, Y, ldy)) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (a->fmt == SHARQ_MXFP4) {
     return from_hip(sharq::launch_linear_mx(a->bb_codes, a->bb_meta, a->bb_scale, a->res_codes, a->res_scale,
@@ -210,12 +227,38 @@ sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, const int32
                                             group_offsets, Y, ldy, s),
                     "sharq_linear launch");
   }
-  if (!a->tensor_scales || !w->tensor_scale)
-    return fail(SHARQ_ERR_INVALID_ARGUMENT, "NVFP4 needs activation and weight tensor scales");
   return from_hip(sharq::launch_linear_nv(a->bb_codes, a->bb_meta, a->bb_scale, a->res_codes, a->res_scale,
                                           a->tensor_scales, row_index, total_rows, a->T, a->K, w->payload, w->scale_sp,
                                           w->tensor_scale, w->D, Y, ldy, s),
                   "sharq_linear launch");
+}
+
+sharq_status sharq_prepare_linear(const void* X, int32_t dtype, int32_t T, int32_t K, int64_t ldx, const float* gamma,
+                                  float eps, const sharq_act* act, const sharq_weight* w, float* Y, int64_t ldy,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (!act || !w) return fail(SHARQ_ERR_INVALID_ARGUMENT, "act and w must not be NULL");
+  if (act->fmt != SHARQ_MXFP4)
+    return fail(SHARQ_ERR_INVALID_ARGUMENT, "sharq_prepare_linear supports MXFP4 only (NVFP4: sharq_prepare + sharq_linear)");
+  if (w->n_groups != 1) return fail(SHARQ_ERR_INVALID_ARGUMENT, "sharq_prepare_linear is a plain linear (n_groups = 1)");
+  if (sharq_status st = prepare_checks(X, dtype, T, K, ldx, gamma, eps, act, nullptr, 0)) return st;
+  if (sharq_status st = linear_checks(act, w, nullptr, nullptr, T, Y, ldy)) return st;
+  if (!workspace || workspace_bytes < 8)
+    return fail(SHARQ_ERR_WORKSPACE_TOO_SMALL, "workspace needs 8 bytes, got %zu", workspace ? workspace_bytes : 0);
+  if (!aligned16(workspace)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = dtype == SHARQ_BF16;
+  if (T <= 8 && K <= sharq::decode_max_k())
+    return from_hip(sharq::launch_prepare_linear_mx(X, bf16, T, K, ldx, gamma, eps, act->bb_codes, act->bb_meta,
+                                                    act->bb_scale, act->res_codes, act->res_scale, w->payload,
+                                                    w->scale_sp, w->D, Y, ldy, static_cast<uint32_t*>(workspace), s),
+                    "sharq_prepare_linear launch");
+  if (sharq_status st = from_hip(sharq::launch_prepare_mx(X, bf16, T, K, ldx, gamma, eps, act->bb_codes, act->bb_meta,
+                                                          act->bb_scale, act->res_codes, act->res_scale, s),
+                                 "sharq_prepare_linear launch"))
+    return st;
+  return from_hip(sharq::launch_linear_mx(act->bb_codes, act->bb_meta, act->bb_scale, act->res_codes, act->res_scale,
+                                          nullptr, T, T, K, w->payload, w->scale_sp, w->D, 1, nullptr, Y, ldy, s),
+                  "sharq_prepare_linear launch");
 }
 
 }  // extern "C"

@@ -23,6 +23,8 @@
 //    from its compacted bytes while staging.
 #include "common.h"
 #include "kernels.h"
+#include "prep_device.h"
+#include <algorithm>
 #include <type_traits>
 
 namespace sharq {
@@ -191,15 +193,43 @@ __global__ __launch_bounds__(MT >= 8 ? 512 : 1024) void linear_mx_skinny(
 // loads; absent tokens, columns and steps get an offset past the buffer and
 // read zero.
 //
-// grid.x = ceil(D / 16), 64 NW threads, NW J >= K / 128.
+// grid.x = ceil(D / 16 CG) (+ rows producer workgroups first when fused),
+// 64 NW threads, NW J >= K / 128.
+//
+// Fused (single-launch decode, rows <= 8): workgroups 0, 8, .., 8 (rows-1)
+// each prepare one activation row (prepare_row_mx: the standalone prepare's
+// outputs, bit for bit) into the activation buffers, write their L2 back
+// (agent-scope release) and increment sync[0].  Workgroups go to the 8 XCDs
+// round robin, so all producers share XCD 0 and its L2: every prepared byte
+// is written through one L2.  The other workgroups are the GEMM's: they issue
+// their weight loads first, then wait (one lane, bounded polling) until
+// sync[0] reaches rows, and only then load the prepared activations with
+// ordinary loads: on XCD 0 they hit the producers' L2, elsewhere the L2 holds
+// no line of these buffers (caches are invalidated at kernel start and
+// nothing reads them before the wait), so the first read fetches the
+// written-back bytes and later ones hit.  The weight stream overlaps the
+// preparation.  Workgroups are dispatched in index order on every XCD, so
+// the producers are resident before any waiting workgroup can hold their
+// place.  The last GEMM workgroup past the wait resets sync[0] and sync[1] to
+// zero for the next call.
 constexpr int kDecodeMaxK = 16384;                   // staged operand + reduction fit in LDS
+constexpr uint32_t kFusedSpinMax = 1u << 20;         // polls before giving up (the kernel always ends)
 
-template <int NK, int CG, int J>
+struct FusedPrep {
+  const void* X;               // activation rows (bf16 or fp32), row r at X + r * ldx elements
+  int bf16;
+  int64_t ldx;
+  const float* gamma;          // RMSNorm weights or null (no normalization)
+  float eps;
+  uint32_t* sync;              // [2] counters, zero between calls
+};
+
+template <int NK, int CG, int J, bool FUSED>
 __global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
-    const uint8_t* __restrict__ bb_codes, const uint8_t* __restrict__ bb_meta, const uint8_t* __restrict__ bb_scale,
-    const uint8_t* __restrict__ res_codes, const uint8_t* __restrict__ res_scale, const int32_t* __restrict__ row_index,
-    int rows, int act_rows, int K, const uint8_t* __restrict__ payload, const uint8_t* __restrict__ wscale, int D,
-    float* __restrict__ Y, int64_t ldy) {
+    const uint8_t* bb_codes, const uint8_t* bb_meta, const uint8_t* bb_scale, const uint8_t* res_codes,
+    const uint8_t* res_scale, const int32_t* __restrict__ row_index, int rows, int act_rows, int K,
+    const uint8_t* __restrict__ payload, const uint8_t* __restrict__ wscale, int D, float* __restrict__ Y, int64_t ldy,
+    FusedPrep fp) {
   static_assert(J % 4 == 0, "weight scales load four steps at a time");
   constexpr int NW = NK * CG;                          // K-splits x column groups
   extern __shared__ uint4 dsm[];
@@ -216,9 +246,32 @@ __global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
                                              __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
   };
 
-  // ---- activation loads first (L2 hits): item i is block i >> 3 of token
-  // i & 7; a thread always serves token tid & 7 and at most IPT = J / (2 CG)
-  // items (NK J >= K / 128 gives 8 K / 32 <= 64 NW IPT)
+  const int n_gemm = (D + 16 * CG - 1) / (16 * CG);
+  int bx = blockIdx.x;
+  if constexpr (FUSED) {
+    const int b = blockIdx.x;
+    if ((b & 7) == 0 && (b >> 3) < rows) {         // producer of row b / 8 (uniform)
+      const int r = b >> 3;
+      prepare_row_mx<NT, 0>(fp.X, fp.bf16 != 0, K, (int64_t)r * fp.ldx, fp.gamma, fp.eps, r,
+                         const_cast<uint8_t*>(bb_codes), const_cast<uint8_t*>(bb_meta), const_cast<uint8_t*>(bb_scale),
+                         const_cast<uint8_t*>(res_codes), const_cast<uint8_t*>(res_scale),
+                         reinterpret_cast<float*>(dsm));
+      // every wave's stores have reached the L2, then one write-back of it
+      // (the release of the increment) publishes the whole row
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) __hip_atomic_fetch_add(&fp.sync[0], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    bx = b - min(rows, (b + 7) >> 3);               // producers before b: 0, 8, ..
+    if (bx >= n_gemm) return;                        // padding (grid covers producer 8 (rows-1))
+  }
+
+  // ---- activation loads (L2 hits): item i is block i >> 3 of token i & 7; a
+  // thread always serves token tid & 7 and at most IPT = J / (2 CG) items
+  // (NK J >= K / 128 gives 8 K / 32 <= 64 NW IPT).  Issued before the weight
+  // loads (the LDS writes then wait only for them), except when fused: there
+  // the activations exist only once the producers are done.
   constexpr int IPT = (J / (2 * CG)) > 0 ? J / (2 * CG) : 1;
   const int t = tid & 7;
   const bool t_ok = t < rows;
@@ -227,7 +280,7 @@ __global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
   uint4 sv[IPT];
   uint2 sc[IPT];
   uint32_t srs[IPT], sm[IPT], sbs[IPT];
-  {
+  auto load_act = [&]() {
     const int an = __builtin_amdgcn_readfirstlane(act_rows);
     const __amdgpu_buffer_rsrc_t r_rc = rsrc(res_codes, (int64_t)an * (K >> 1));
     const __amdgpu_buffer_rsrc_t r_rs = rsrc(res_scale, (int64_t)an * (K >> 5));
@@ -246,12 +299,13 @@ __global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
       sm[j] = __builtin_amdgcn_raw_buffer_load_b16(r_bm, (ar * (uint32_t)(K >> 4) + 2u * kb) | out, 0, 0);
       sbs[j] = __builtin_amdgcn_raw_buffer_load_b8(r_bs, (ar * (uint32_t)(K >> 5) + kb) | out, 0, 0);
     }
-  }
+  };
+  if (!FUSED) load_act();
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- weight loads of this wave's steps (column group cg, K-split kw)
   const int cg = w % CG, kw = w / CG;
-  const int col = (blockIdx.x * CG + cg) * 16 + (l & 15);
+  const int col = (bx * CG + cg) * 16 + (l & 15);
   const int kq = l >> 4;
   const int s0 = kw * J;
   const __amdgpu_buffer_rsrc_t r_w = rsrc(payload, (int64_t)D * (K >> 1));
@@ -275,6 +329,23 @@ __global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
     wsd[j] = v[0]; wsd[j + 1] = v[1]; wsd[j + 2] = v[2]; wsd[j + 3] = v[3];
   }
   __builtin_amdgcn_sched_barrier(0);
+
+  if constexpr (FUSED) {
+    if (tid == 0) {
+      for (uint32_t it = 0; it < kFusedSpinMax; ++it) {
+        if (__hip_atomic_load(&fp.sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)rows) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      const uint32_t n = __hip_atomic_fetch_add(&fp.sync[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (n + 1 == (uint32_t)n_gemm) {               // every GEMM workgroup is past the wait
+        __hip_atomic_store(&fp.sync[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&fp.sync[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __syncthreads();
+    load_act();
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
   // ---- activation operand into LDS (waits only for the activation loads,
   // which were issued first)
@@ -917,50 +988,72 @@ int num_cus_gemm() {
   }
   return cached[dev];
 }
+
+// decode geometry: J = 4 K-steps per wave while 16 K-splits suffice, else 8;
+// column groups of 16 per workgroup while at least 256 workgroups remain and
+// the workgroup stays within 16 waves.  Fused: rows producer workgroups first.
+template <bool FUSED>
+hipError_t launch_decode(const uint8_t* bb_codes, const uint8_t* bb_meta, const uint8_t* bb_scale,
+                         const uint8_t* res_codes, const uint8_t* res_scale, const int32_t* row_index, int rows,
+                         int act_rows, int K, const uint8_t* payload, const uint8_t* wscale, int D, float* Y, int64_t ldy,
+                         FusedPrep fp, hipStream_t s) {
+  const int KS = K / 128;
+  const int J = KS <= 64 ? 4 : 8;
+  int NK = 1;
+  while (NK * J < KS) NK *= 2;
+  int CG = 1;
+  while (NK * CG * 2 <= 16 && (D + 16 * CG * 2 - 1) / (16 * CG * 2) >= 256) CG *= 2;
+  const size_t lds = (size_t)(K / 32 + 1) * 17 * 16 + (size_t)NK * CG * 64 * 4 * sizeof(float);
+  const int n_gemm = (D + 16 * CG - 1) / (16 * CG);
+  // fused: rows producers at workgroups 0, 8, .. among the GEMM workgroups
+  dim3 grid(FUSED ? std::max(n_gemm + rows, 8 * (rows - 1) + 1) : n_gemm), block(64 * NK * CG);
+#define L(NK_, CG_, J_)                                                                                                 \
+  hipLaunchKernelGGL((linear_mx_decode<NK_, CG_, J_, FUSED>), grid, block, lds, s, bb_codes, bb_meta, bb_scale,         \
+                     res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, Y, ldy, fp)
+  switch (J * 10000 + NK * 100 + CG) {
+    case 40101: L(1, 1, 4); break;
+    case 40102: L(1, 2, 4); break;
+    case 40104: L(1, 4, 4); break;
+    case 40108: L(1, 8, 4); break;
+    case 40116: L(1, 16, 4); break;
+    case 40201: L(2, 1, 4); break;
+    case 40202: L(2, 2, 4); break;
+    case 40204: L(2, 4, 4); break;
+    case 40208: L(2, 8, 4); break;
+    case 40401: L(4, 1, 4); break;
+    case 40402: L(4, 2, 4); break;
+    case 40404: L(4, 4, 4); break;
+    case 40801: L(8, 1, 4); break;
+    case 40802: L(8, 2, 4); break;
+    case 41601: L(16, 1, 4); break;
+    case 81601: L(16, 1, 8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef L
+  return hipGetLastError();
+}
 }  // namespace
+
+int decode_max_k() { return kDecodeMaxK; }
+
+hipError_t launch_prepare_linear_mx(const void* X, bool bf16, int T, int K, int64_t ldx, const float* gamma, float eps,
+                                    uint8_t* bb_codes, uint8_t* bb_meta, uint8_t* bb_scale, uint8_t* res_codes,
+                                    uint8_t* res_scale, const uint8_t* payload, const uint8_t* wscale, int D, float* Y,
+                                    int64_t ldy, uint32_t* sync, hipStream_t s) {
+  if (T < 1 || T > 8 || K > kDecodeMaxK) return hipErrorInvalidValue;
+  const FusedPrep fp{X, bf16 ? 1 : 0, ldx, gamma, eps, sync};
+  return launch_decode<true>(bb_codes, bb_meta, bb_scale, res_codes, res_scale, nullptr, T, T, K, payload, wscale, D, Y,
+                             ldy, fp, s);
+}
 
 hipError_t launch_linear_mx(const uint8_t* bb_codes, const uint8_t* bb_meta, const uint8_t* bb_scale,
                             const uint8_t* res_codes, const uint8_t* res_scale, const int32_t* row_index, int rows,
                             int act_rows, int K, const uint8_t* payload, const uint8_t* wscale, int D, int n_groups,
                             const int32_t* group_offsets, float* Y, int64_t ldy, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  if (n_groups == 1 && rows <= 8 && K <= kDecodeMaxK) {
-    // J = 4 K-steps per wave while 16 K-splits suffice, else 8; column groups
-    // of 16 per workgroup while at least 256 workgroups remain and the
-    // workgroup stays within 16 waves
-    const int KS = K / 128;
-    const int J = KS <= 64 ? 4 : 8;
-    int NK = 1;
-    while (NK * J < KS) NK *= 2;
-    int CG = 1;
-    while (NK * CG * 2 <= 16 && (D + 16 * CG * 2 - 1) / (16 * CG * 2) >= 256) CG *= 2;
-    const size_t lds = (size_t)(K / 32 + 1) * 17 * 16 + (size_t)NK * CG * 64 * 4 * sizeof(float);
-    dim3 grid((D + 16 * CG - 1) / (16 * CG)), block(64 * NK * CG);
-#define L(NK_, CG_, J_)                                                                                                 \
-  hipLaunchKernelGGL((linear_mx_decode<NK_, CG_, J_>), grid, block, lds, s, bb_codes, bb_meta, bb_scale, res_codes,      \
-                     res_scale, row_index, rows, act_rows, K, payload, wscale, D, Y, ldy)
-    switch (J * 10000 + NK * 100 + CG) {
-      case 40101: L(1, 1, 4); break;
-      case 40102: L(1, 2, 4); break;
-      case 40104: L(1, 4, 4); break;
-      case 40108: L(1, 8, 4); break;
-      case 40116: L(1, 16, 4); break;
-      case 40201: L(2, 1, 4); break;
-      case 40202: L(2, 2, 4); break;
-      case 40204: L(2, 4, 4); break;
-      case 40208: L(2, 8, 4); break;
-      case 40401: L(4, 1, 4); break;
-      case 40402: L(4, 2, 4); break;
-      case 40404: L(4, 4, 4); break;
-      case 40801: L(8, 1, 4); break;
-      case 40802: L(8, 2, 4); break;
-      case 41601: L(16, 1, 4); break;
-      case 81601: L(16, 1, 8); break;
-      default: return hipErrorInvalidValue;
-    }
-#undef L
-    return hipGetLastError();
-  }
+  if (n_groups == 1 && rows <= 8 && K <= kDecodeMaxK)
+    return launch_decode<false>(bb_codes, bb_meta, bb_scale, res_codes, res_scale, row_index, rows, act_rows, K, payload,
+                                wscale, D, Y, ldy, FusedPrep{}, s);
   if (n_groups == 1 && rows <= 64) {
     const int KS = K / 128;
     const int mt = (rows + 7) / 8;

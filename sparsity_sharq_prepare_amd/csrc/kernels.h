@@ -35,6 +35,15 @@ hipError_t launch_linear_mx(const uint8_t* bb_codes, const uint8_t* bb_meta, con
                             int act_rows, int K, const uint8_t* payload, const uint8_t* wscale, int D, int n_groups,
                             const int32_t* group_offsets, float* Y, int64_t ldy, hipStream_t s);
 
+// single-launch decode (T <= 8, K <= decode_max_k()): MXFP4 prepare of the T
+// rows and the plain dual-path linear on them in one kernel; sync: two
+// device counters, zero before the call and left zero
+int decode_max_k();
+hipError_t launch_prepare_linear_mx(const void* X, bool bf16, int T, int K, int64_t ldx, const float* gamma, float eps,
+                                    uint8_t* bb_codes, uint8_t* bb_meta, uint8_t* bb_scale, uint8_t* res_codes,
+                                    uint8_t* res_scale, const uint8_t* payload, const uint8_t* wscale, int D, float* Y,
+                                    int64_t ldy, uint32_t* sync, hipStream_t s);
+
 hipError_t launch_linear_nv(const uint8_t* bb_codes, const uint8_t* bb_meta, const uint8_t* bb_scale,
                             const uint8_t* res_codes, const uint8_t* res_scale, const float* a_ts,
                             const int32_t* row_index, int rows, int act_rows, int K, const uint8_t* payload,

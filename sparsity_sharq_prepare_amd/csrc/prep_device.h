@@ -1,0 +1,200 @@
+// Device-side pieces of the MXFP4 activation preparation (xllm-io paper
+// review §3.2-§3.5; kasblo explainer, method steps 1-4) shared by the
+// standalone prepare kernel and the single-launch decode kernel.
+#pragma once
+
+#include "common.h"
+
+namespace sharq {
+namespace {
+
+template <bool BF16>
+SHARQ_DEV void unpack_group(const uint4& a, const uint4& b, float x[8]) {
+  if (BF16) {
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y);
+    x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
+    x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y);
+    x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
+  }
+}
+
+// pairwise tree of the 8 squares of one group (no contraction)
+SHARQ_DEV float tree8_sq(const float x[8]) {
+  float q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = __fmul_rn(x[i], x[i]);
+  return __fadd_rn(__fadd_rn(__fadd_rn(q[0], q[1]), __fadd_rn(q[2], q[3])),
+                   __fadd_rn(__fadd_rn(q[4], q[5]), __fadd_rn(q[6], q[7])));
+}
+
+// MXFP4 quantization of group g (8 normalized values y, one lane) and its
+// stores.  Per group: pair scores, kept pairs, then per 32-value block (the 4
+// lanes of a quad) the backbone scale, the codes of all four pairs (the kept
+// two are compacted with one byte permute), the exact residual (y minus the
+// dequantized kept pairs, y itself on dropped pairs) and its codes.  Metadata
+// nibbles and scales of a block are gathered into the quad's first lane and
+// stored from there.  All 64 lanes of the wave must take part (wave ballots,
+// quad DPP); the output descriptors span one row, so stores of groups past
+// the row (and of absent rows: zero-size descriptors) are dropped.  AUX: the
+// stores' cache-policy bits.
+template <int AUX = 0>
+SHARQ_DEV void mx_quantize_store(const float y[8], uint32_t g, __amdgpu_buffer_rsrc_t o_bc,
+                                 __amdgpu_buffer_rsrc_t o_rc, __amdgpu_buffer_rsrc_t o_mt,
+                                 __amdgpu_buffer_rsrc_t o_sb, __amdgpu_buffer_rsrc_t o_sr) {
+  constexpr uint32_t kOut = 0x80000000u;
+  // ---- pair scores, kept pairs, backbone scale
+  const float s0 = fmaxf(fabsf(y[0]), fabsf(y[1]));
+  const float s1 = fmaxf(fabsf(y[2]), fabsf(y[3]));
+  const float s2 = fmaxf(fabsf(y[4]), fabsf(y[5]));
+  const float s3 = fmaxf(fabsf(y[6]), fabsf(y[7]));
+  uint64_t kp[4];
+  uint32_t i0, i1;
+  top2_lanes(s0, s1, s2, s3, kp, i0, i1);
+  const uint32_t eb = e8m0_code(quad_max(fmaxf(fmaxf(s0, s1), fmaxf(s2, s3))));
+  const float s_bb = exp2i((int)eb - 127);
+  uint32_t bw = 0;
+  bw = cvt_fp4x2<0>(bw, y[0], y[1], s_bb);
+  bw = cvt_fp4x2<1>(bw, y[2], y[3], s_bb);
+  bw = cvt_fp4x2<2>(bw, y[4], y[5], s_bb);
+  bw = cvt_fp4x2<3>(bw, y[6], y[7], s_bb);
+  // ---- residual R = y - X~_sp (exact), X~_sp = 0 on dropped pairs
+  float R[8];
+  {
+    const v2f d[4] = {dq_fp4x2<0>(bw, s_bb), dq_fp4x2<1>(bw, s_bb), dq_fp4x2<2>(bw, s_bb), dq_fp4x2<3>(bw, s_bb)};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const bool kept = lane_in(kp[p]);
+      R[2 * p] = __fsub_rn(y[2 * p], kept ? d[p].x : 0.0f);
+      R[2 * p + 1] = __fsub_rn(y[2 * p + 1], kept ? d[p].y : 0.0f);
+    }
+  }
+  const float rmax = fmaxf(fmaxf(fmaxf(fabsf(R[0]), fabsf(R[1])), fmaxf(fabsf(R[2]), fabsf(R[3]))),
+                           fmaxf(fmaxf(fabsf(R[4]), fabsf(R[5])), fmaxf(fabsf(R[6]), fabsf(R[7]))));
+  const uint32_t er = e8m0_code(quad_max(rmax));
+  const float s_r = exp2i((int)er - 127);
+  uint32_t rw = 0;
+  rw = cvt_fp4x2<0>(rw, R[0], R[1], s_r);
+  rw = cvt_fp4x2<1>(rw, R[2], R[3], s_r);
+  rw = cvt_fp4x2<2>(rw, R[4], R[5], s_r);
+  rw = cvt_fp4x2<3>(rw, R[6], R[7], s_r);
+  // ---- compacted kept pair bytes (byte permute; selector 0x0C reads zero)
+  const uint32_t kept2 = __builtin_amdgcn_perm(0u, bw, i0 | (i1 << 8) | 0x0C0C0000u);
+  // metadata of the quad's 4 groups as 16 bits in its first lane
+  const uint32_t nib = i0 | (i1 << 2);
+  const uint32_t b8 = nib | (dpp_u<kDppQuadXor1>(nib) << 4);
+  const uint32_t m16 = (b8 & 0xFFu) | (dpp_u<kDppQuadXor2>(b8) << 8);
+  // (block values only from the quad's first lane)
+  const uint32_t qo = (g & 3) == 0 ? 0u : kOut;
+  __builtin_amdgcn_raw_buffer_store_b16((uint16_t)kept2, o_bc, 2 * g, 0, AUX);
+  __builtin_amdgcn_raw_buffer_store_b32(rw, o_rc, 4 * g, 0, AUX);
+  __builtin_amdgcn_raw_buffer_store_b16((uint16_t)m16, o_mt, (g >> 1) | qo, 0, AUX);
+  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)eb, o_sb, (g >> 2) | qo, 0, AUX);
+  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)er, o_sr, (g >> 2) | qo, 0, AUX);
+}
+
+// raw buffer descriptor of `bytes` bytes at base + byte offset off (fields
+// made wave-uniform so that no waterfall loop is generated)
+SHARQ_DEV __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint64_t off, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base) + off;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// One activation row prepared by the NT threads of a workgroup, reading the
+// row twice (sum of squares, then quantization) chunk by chunk: the MXFP4
+// outputs of the standalone prepare kernel, bit for bit.  Chunk c holds
+// groups c NT .. c NT + NT - 1, so the sum of squares follows the same
+// pinned pairwise tree: group tree, wave butterfly (aligned 512-value
+// blocks), the chunk's waves in order, then the chunks as a tree (zero
+// padding to a power of two).  red: LDS scratch of at least
+// nch * NT / 64 + 2 * nch + 1 floats, nch = ceil(K / (8 NT)).  AUX: cache
+// policy of the output stores.  Ends with a workgroup barrier.
+template <int NT, int AUX>
+SHARQ_DEV void prepare_row_mx(const void* X, bool bf16, int K, int64_t row_elem_off, const float* gamma, float eps,
+                              int row, uint8_t* bb_codes, uint8_t* bb_meta, uint8_t* bb_scale, uint8_t* res_codes,
+                              uint8_t* res_scale, float* red) {
+  constexpr int WPR = NT / kWave;
+  const int t = threadIdx.x, l = t & (kWave - 1), w = t / kWave;
+  const int G = K >> 3;
+  const int nch = (G + NT - 1) / NT;
+  const uint32_t es = bf16 ? 2u : 4u;
+  const __amdgpu_buffer_rsrc_t rx = row_rsrc(X, (uint64_t)row_elem_off * es, (uint32_t)K * es);
+  auto load = [&](uint32_t g, float x[8]) {
+    if (bf16) {
+      const auto a = __builtin_amdgcn_raw_buffer_load_b128(rx, 16u * g, 0, 0);
+      unpack_group<true>(make_uint4(a[0], a[1], a[2], a[3]), make_uint4(0, 0, 0, 0), x);
+    } else {
+      const auto a = __builtin_amdgcn_raw_buffer_load_b128(rx, 32u * g, 0, 0);
+      const auto b = __builtin_amdgcn_raw_buffer_load_b128(rx, 32u * g + 16u, 0, 0);
+      unpack_group<false>(make_uint4(a[0], a[1], a[2], a[3]), make_uint4(b[0], b[1], b[2], b[3]), x);
+    }
+  };
+
+  float inv = 1.0f;
+  if (gamma) {
+    for (int c = 0; c < nch; ++c) {                 // uniform trip count: whole waves take part
+      float x[8];
+      load((uint32_t)(c * NT + t), x);               // groups past K read zeros
+      const float s = wave_tree_sum(tree8_sq(x));
+      if (l == 0) red[c * WPR + w] = s;
+    }
+    __syncthreads();
+    if (t == 0) {
+      int np = 1;
+      while (np < nch) np <<= 1;
+      float* part = red + nch * WPR;
+      for (int c = 0; c < np; ++c) {
+        float v[WPR];
+#pragma unroll
+        for (int i = 0; i < WPR; ++i) v[i] = c < nch ? red[c * WPR + i] : 0.0f;
+#pragma unroll
+        for (int n = WPR / 2; n >= 1; n >>= 1) {
+#pragma unroll
+          for (int i = 0; i < n; ++i) v[i] = __fadd_rn(v[2 * i], v[2 * i + 1]);
+        }
+        part[c] = v[0];
+      }
+      for (int n = np / 2; n >= 1; n >>= 1)
+        for (int i = 0; i < n; ++i) part[i] = __fadd_rn(part[2 * i], part[2 * i + 1]);
+      const float ms = __fdiv_rn(part[0], (float)K);
+      part[np] = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(ms, eps)));
+    }
+    __syncthreads();
+    int np = 1;
+    while (np < nch) np <<= 1;
+    inv = red[nch * WPR + np];
+  }
+
+  const __amdgpu_buffer_rsrc_t o_bc = row_rsrc(bb_codes, (uint64_t)row * (K >> 2), K >> 2);
+  const __amdgpu_buffer_rsrc_t o_rc = row_rsrc(res_codes, (uint64_t)row * (K >> 1), K >> 1);
+  const __amdgpu_buffer_rsrc_t o_mt = row_rsrc(bb_meta, (uint64_t)row * (K >> 4), K >> 4);
+  const __amdgpu_buffer_rsrc_t o_sb = row_rsrc(bb_scale, (uint64_t)row * (K >> 5), K >> 5);
+  const __amdgpu_buffer_rsrc_t o_sr = row_rsrc(res_scale, (uint64_t)row * (K >> 5), K >> 5);
+  for (int c = 0; c < nch; ++c) {
+    const uint32_t g = (uint32_t)(c * NT + t);
+    float y[8];
+    load(g, y);
+    if (gamma) {
+      const uint32_t k0 = g < (uint32_t)G ? 8u * g : 0u;   // lanes past K hold zeros
+      const float4 ga = *reinterpret_cast<const float4*>(gamma + k0);
+      const float4 gb = *reinterpret_cast<const float4*>(gamma + k0 + 4);
+      const float gm[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = __fmul_rn(__fmul_rn(y[i], inv), gm[i]);
+    }
+    mx_quantize_store<AUX>(y, g, o_bc, o_rc, o_mt, o_sb, o_sr);
+  }
+  __syncthreads();
+}
+
+}  // namespace
+}  // namespace sharq

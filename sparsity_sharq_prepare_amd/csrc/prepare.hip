@@ -16,35 +16,11 @@
 // Every fp32 operation rounds to nearest even, without contraction.
 #include "common.h"
 #include "kernels.h"
+#include "prep_device.h"
 
 namespace sharq {
 
 namespace {
-
-template <bool BF16>
-SHARQ_DEV void unpack_group(const uint4& a, const uint4& b, float x[8]) {
-  if (BF16) {
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __uint_as_float(w[i] << 16);
-      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-  } else {
-    x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y);
-    x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
-    x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y);
-    x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
-  }
-}
-
-SHARQ_DEV float tree8_sq(const float x[8]) {
-  float q[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = __fmul_rn(x[i], x[i]);
-  return __fadd_rn(__fadd_rn(__fadd_rn(q[0], q[1]), __fadd_rn(q[2], q[3])),
-                   __fadd_rn(__fadd_rn(q[4], q[5]), __fadd_rn(q[6], q[7])));
-}
 
 // Row-resident state of one thread: its raw groups.  Loads go through a raw
 // buffer descriptor spanning the row (no bytes for an absent row), so groups
@@ -153,12 +129,9 @@ SHARQ_DEV uint32_t select_kept(uint32_t word, uint32_t nib) {
 // ============================================================================
 // MXFP4: one pass
 // ============================================================================
-// Per group of 8 (one lane): normalize, pair scores, kept pair indices, then
-// per 32-value block (the 4 lanes of a quad) the backbone scale, the codes of
-// all four pairs (the kept two are compacted with one byte permute), the exact
-// residual (y minus the dequantized kept pairs, y itself on dropped pairs) and
-// its codes.  Metadata nibbles and scales of a block are gathered into the
-// quad's first lane and stored from there.
+// Per group of 8 (one lane): normalize, then mx_quantize_store (pair scores,
+// kept pairs, backbone and residual codes and scales of the quad's 32-value
+// block, metadata).
 //
 // Workgroups loop over blocks of RPW rows (block b, b + grid, ...).  gamma of
 // the thread's groups is read once, and the next block's rows are loaded while
@@ -207,7 +180,6 @@ struct MxRowPass {
     const __amdgpu_buffer_rsrc_t o_bc = orow(bb_codes, K >> 2), o_rc = orow(res_codes, K >> 1);
     const __amdgpu_buffer_rsrc_t o_mt = orow(bb_meta, K >> 4), o_sb = orow(bb_scale, K >> 5);
     const __amdgpu_buffer_rsrc_t o_sr = orow(res_scale, K >> 5);
-    constexpr uint32_t kOut = 0x80000000u;
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
       const uint32_t g = (uint32_t)(c * TPR + t);
@@ -229,56 +201,7 @@ struct MxRowPass {
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[i] = __fmul_rn(__fmul_rn(y[i], inv), gm[i]);
       }
-      // ---- pair scores, kept pairs, backbone scale
-      const float s0 = fmaxf(fabsf(y[0]), fabsf(y[1]));
-      const float s1 = fmaxf(fabsf(y[2]), fabsf(y[3]));
-      const float s2 = fmaxf(fabsf(y[4]), fabsf(y[5]));
-      const float s3 = fmaxf(fabsf(y[6]), fabsf(y[7]));
-      uint64_t kp[4];
-      uint32_t i0, i1;
-      top2_lanes(s0, s1, s2, s3, kp, i0, i1);
-      const uint32_t eb = e8m0_code(quad_max(fmaxf(fmaxf(s0, s1), fmaxf(s2, s3))));
-      const float s_bb = exp2i((int)eb - 127);
-      uint32_t bw = 0;
-      bw = cvt_fp4x2<0>(bw, y[0], y[1], s_bb);
-      bw = cvt_fp4x2<1>(bw, y[2], y[3], s_bb);
-      bw = cvt_fp4x2<2>(bw, y[4], y[5], s_bb);
-      bw = cvt_fp4x2<3>(bw, y[6], y[7], s_bb);
-      // ---- residual R = y - X~_sp (exact), X~_sp = 0 on dropped pairs
-      float R[8];
-      {
-        const v2f d[4] = {dq_fp4x2<0>(bw, s_bb), dq_fp4x2<1>(bw, s_bb), dq_fp4x2<2>(bw, s_bb),
-                          dq_fp4x2<3>(bw, s_bb)};
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const bool kept = lane_in(kp[p]);
-          R[2 * p] = __fsub_rn(y[2 * p], kept ? d[p].x : 0.0f);
-          R[2 * p + 1] = __fsub_rn(y[2 * p + 1], kept ? d[p].y : 0.0f);
-        }
-      }
-      const float rmax = fmaxf(fmaxf(fmaxf(fabsf(R[0]), fabsf(R[1])), fmaxf(fabsf(R[2]), fabsf(R[3]))),
-                               fmaxf(fmaxf(fabsf(R[4]), fabsf(R[5])), fmaxf(fabsf(R[6]), fabsf(R[7]))));
-      const uint32_t er = e8m0_code(quad_max(rmax));
-      const float s_r = exp2i((int)er - 127);
-      uint32_t rw = 0;
-      rw = cvt_fp4x2<0>(rw, R[0], R[1], s_r);
-      rw = cvt_fp4x2<1>(rw, R[2], R[3], s_r);
-      rw = cvt_fp4x2<2>(rw, R[4], R[5], s_r);
-      rw = cvt_fp4x2<3>(rw, R[6], R[7], s_r);
-      // ---- compacted kept pair bytes (byte permute; selector 0x0C reads zero)
-      const uint32_t kept2 = __builtin_amdgcn_perm(0u, bw, i0 | (i1 << 8) | 0x0C0C0000u);
-      // metadata of the quad's 4 groups as 16 bits in its first lane
-      const uint32_t nib = i0 | (i1 << 2);
-      const uint32_t b8 = nib | (dpp_u<kDppQuadXor1>(nib) << 4);
-      const uint32_t m16 = (b8 & 0xFFu) | (dpp_u<kDppQuadXor2>(b8) << 8);
-      // (groups past K have offsets past the row; block values only from the
-      // quad's first lane)
-      const uint32_t qo = (g & 3) == 0 ? 0u : kOut;
-      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)kept2, o_bc, 2 * g, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(rw, o_rc, 4 * g, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)m16, o_mt, (g >> 1) | qo, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)eb, o_sb, (g >> 2) | qo, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)er, o_sr, (g >> 2) | qo, 0, 0);
+      mx_quantize_store(y, g, o_bc, o_rc, o_mt, o_sb, o_sr);
     }
   }
 };

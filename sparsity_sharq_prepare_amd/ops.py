@@ -1,4 +1,5 @@
-"""Thin PyTorch binding of the SharQ C ABI (pack_weight, prepare, linear).
+"""Thin PyTorch binding of the SharQ C ABI (pack_weight, prepare, linear,
+prepare_linear).
 
 PyTorch provides device memory and the stream; each function allocates its
 outputs as torch tensors, fills the C structs with their device pointers and
@@ -152,3 +153,36 @@ def linear(act: PreparedAct, w: PackedWeight, group_offsets: Optional[torch.Tens
     L.check(L.lib().sharq_linear(act.struct(), w.struct(), _ptr(group_offsets), _ptr(row_index), total_rows,
                                  out.data_ptr(), out.stride(0), _stream_ptr(stream)))
     return out
+
+
+# per-device zeroed 16-byte workspaces of prepare_linear (its counters are
+# left zero by every call); calls on one device are stream-ordered here
+_PL_WS: dict = {}
+
+
+def _prepare_linear_ws(device: torch.device) -> torch.Tensor:
+    key = (device.type, device.index if device.index is not None else torch.cuda.current_device())
+    ws = _PL_WS.get(key)
+    if ws is None:
+        ws = torch.zeros(16, dtype=torch.uint8, device=device)
+        _PL_WS[key] = ws
+    return ws
+
+
+def prepare_linear(X: torch.Tensor, gamma: Optional[torch.Tensor], w: PackedWeight, eps: float = 1e-6,
+                   act: Optional[PreparedAct] = None, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    """Preparation of X and the plain MXFP4 linear on it, in one launch for
+    decode shapes (T <= 8); returns (prepared activations, Y fp32 T x D)."""
+    _dev_check(X, gamma, out, workspace)
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be a 2-D tensor contiguous along K")
+    T, K = X.shape
+    act = act or empty_act(w.fmt, T, K, X.device)
+    if out is None:
+        out = torch.empty((T, w.D), dtype=torch.float32, device=X.device)
+    ws = workspace if workspace is not None else _prepare_linear_ws(X.device)
+    L.check(L.lib().sharq_prepare_linear(X.data_ptr(), _dtype_code(X), T, K, X.stride(0), _ptr(gamma), eps,
+                                         act.struct(), w.struct(), out.data_ptr(), out.stride(0), ws.data_ptr(),
+                                         ws.numel(), _stream_ptr(stream)))
+    return act, out

@@ -28,10 +28,10 @@ from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SOURCES = {
-    "linear_mx_decode": ["gemm_mx.hip", "common.h"],
-    "linear_mx_tile": ["gemm_mx.hip", "common.h"],
+    "linear_mx_decode": ["gemm_mx.hip", "common.h", "prep_device.h"],
+    "linear_mx_tile": ["gemm_mx.hip", "common.h", "prep_device.h"],
     "linear_nv_tile": ["gemm_nv.hip", "common.h"],
-    "prepare_mx_kernel": ["prepare.hip", "common.h"],
+    "prepare_mx_kernel": ["prepare.hip", "common.h", "prep_device.h"],
 }
 
 

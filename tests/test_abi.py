@@ -137,3 +137,30 @@ def test_pack_validation_errors():
     nv_alias.scale_dn = nv_alias.scale_sp
     assert lib.sharq_pack_weight(W, 1, 256, 64, 1, 64, 0, nv_alias, 0x80000, 1 << 20, None) == \
         L.SHARQ_ERR_INVALID_ARGUMENT
+
+
+def test_prepare_linear_validation_errors():
+    lib = L.lib()
+    f = lib.sharq_prepare_linear
+    X, Y, ws = 0x50000, 0x30000, 0x90000
+    a, w = _fake_act(), _fake_weight()
+    # NVFP4 preparation needs tensor-wide reductions first: not offered here
+    assert f(X, 1, 8, 256, 256, None, 1e-6, _fake_act(fmt=1), _fake_weight(fmt=1), Y, 64, ws, 16, None) == \
+        L.SHARQ_ERR_INVALID_ARGUMENT
+    assert "MXFP4" in lib.sharq_last_error().decode()
+    # plain linear only
+    assert f(X, 1, 8, 256, 256, None, 1e-6, a, _fake_weight(G=2), Y, 64, ws, 16, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    # workspace missing, too small, misaligned
+    assert f(X, 1, 8, 256, 256, None, 1e-6, a, w, Y, 64, None, 0, None) == L.SHARQ_ERR_WORKSPACE_TOO_SMALL
+    assert f(X, 1, 8, 256, 256, None, 1e-6, a, w, Y, 64, ws, 4, None) == L.SHARQ_ERR_WORKSPACE_TOO_SMALL
+    assert f(X, 1, 8, 256, 256, None, 1e-6, a, w, Y, 64, ws + 4, 16, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    # activation / weight K differ; act describes other rows; K % 128 != 0
+    assert f(X, 1, 8, 256, 256, None, 1e-6, a, _fake_weight(K=512), Y, 64, ws, 16, None) == \
+        L.SHARQ_ERR_FORMAT_MISMATCH
+    assert f(X, 1, 4, 256, 256, None, 1e-6, a, w, Y, 64, ws, 16, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert f(X, 1, 8, 96, 96, None, 1e-6, _fake_act(K=96), _fake_weight(K=96), Y, 64, ws, 16, None) == \
+        L.SHARQ_ERR_UNSUPPORTED_SHAPE
+    # prepare-side checks: unknown dtype, ldx < K; linear-side: ldy < D
+    assert f(X, 7, 8, 256, 256, None, 1e-6, a, w, Y, 64, ws, 16, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert f(X, 1, 8, 256, 128, None, 1e-6, a, w, Y, 64, ws, 16, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert f(X, 1, 8, 256, 256, None, 1e-6, a, w, Y, 32, ws, 16, None) == L.SHARQ_ERR_INVALID_ARGUMENT

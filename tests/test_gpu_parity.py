@@ -309,3 +309,119 @@ def test_graph_replay_matches_eager():
         assert torch.equal(act.res_codes, codes_eager)
         ops.linear(act, w)             # eager work between replays
         torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ single-launch decode
+FUSED_SHAPES = [  # (T, K, D, dtype, gamma): one launch for T <= 8, K <= 16384 (every decode
+    # kernel geometry: 1..16 K-splits, 1..8 column groups, J = 4 and 8), else the two launches
+    (1, 256, 64, "bf16", True), (8, 512, 200, "bf16", True), (5, 1152, 72, "bf16", True),
+    (3, 384, 40, "f32", True), (8, 2048, 96, "bf16", False), (7, 16384, 48, "bf16", True),
+    (2, 14336, 130, "f32", True), (6, 768, 8200, "bf16", True), (8, 4096, 4100, "bf16", True),
+    (2, 256, 40000, "bf16", True),
+    (9, 512, 96, "bf16", True), (4, 16512, 64, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("T,K,D,dtype,gamma", FUSED_SHAPES)
+def test_prepare_linear_shapes(T, K, D, dtype, gamma):
+    case = synth.random_case(T * 11 + K + D, T, K, D, dtype=dtype, gamma=gamma)
+    X, g = dev_x(case), dev_gamma(case.gamma)
+    w = ops.pack_weight(dev_w(case.w, dtype))
+    act, Y = ops.prepare_linear(X, g, w)
+    ref = oracle_prepare(case)
+    compare_act(act, ref)
+    Yr, S = O.sharq_linear(ref, O.pack_weight(case.w_f32()))
+    assert_gemm_close(Y.cpu().numpy(), Yr, S)
+    # the same bytes and values as the two separate calls, and again on a
+    # second call (the workspace counters are back at zero)
+    act2 = ops.prepare(X, g, 1e-6)
+    Y2 = ops.linear(act2, w)
+    act3, Y3 = ops.prepare_linear(X, g, w)
+    torch.cuda.synchronize()
+    for k in ("bb_codes", "bb_meta", "bb_scale", "res_codes", "res_scale"):
+        assert torch.equal(getattr(act, k), getattr(act2, k)), k
+        assert torch.equal(getattr(act3, k), getattr(act2, k)), k
+    assert torch.equal(Y, Y2) and torch.equal(Y3, Y2)
+    ws = ops._prepare_linear_ws(X.device)
+    assert int(ws.view(torch.int32)[:2].abs().sum()) == 0
+
+
+@pytest.mark.parametrize("i", range(3), ids=DECODE_IDS)
+def test_prepare_linear_decode_full_sampled(i):
+    case = synth.decode_case(i)
+    X, g = dev_x(case), dev_gamma(case.gamma)
+    w = ops.pack_weight(dev_w(case.w, case.dtype))
+    act, Y = ops.prepare_linear(X, g, w)
+    ref = oracle_prepare(case)
+    compare_act(act, ref)
+    r, c = sample_pairs(case.T, case.D, 3000, seed=case.K + 1)
+    Yr, S = O.sharq_linear_sampled(ref, O.pack_weight(case.w_f32()), r, c)
+    assert_gemm_close(Y.cpu().numpy()[r, c], Yr, S)
+    Y2 = ops.linear(ops.prepare(X, g, 1e-6), w)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2)
+
+
+def test_prepare_linear_sequence_and_own_workspace():
+    # calls of different shapes back to back on one workspace, then on a
+    # caller-owned one; every output equals the two-launch result
+    ws = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    outs = []
+    for seed, (T, K, D) in enumerate([(8, 1024, 320), (1, 256, 64), (4, 2048, 1000), (8, 1024, 320)]):
+        case = synth.random_case(500 + seed, T, K, D)
+        X, g = dev_x(case), dev_gamma(case.gamma)
+        w = ops.pack_weight(dev_w(case.w, case.dtype))
+        for workspace in (None, ws):
+            act, Y = ops.prepare_linear(X, g, w, workspace=workspace)
+            outs.append((Y, ops.linear(ops.prepare(X, g, 1e-6), w)))
+    torch.cuda.synchronize()
+    for Y, Y2 in outs:
+        assert torch.equal(Y, Y2)
+    assert int(ws.abs().sum()) == 0
+
+
+def test_prepare_linear_graph_replay():
+    case = synth.random_case(91, 8, 2048, 700)
+    X, g = dev_x(case), dev_gamma(case.gamma)
+    w = ops.pack_weight(dev_w(case.w, case.dtype))
+    act = ops.empty_act("mxfp4", 8, 2048)
+    Y = torch.empty((8, 700), dtype=torch.float32, device="cuda")
+    ops.prepare_linear(X, g, w, act=act, out=Y)
+    torch.cuda.synchronize()
+    Y_eager, codes_eager = Y.clone(), act.bb_codes.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ops.prepare_linear(X, g, w, act=act, out=Y)
+    for _ in range(4):
+        Y.zero_()
+        act.bb_codes.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Y_eager)
+        assert torch.equal(act.bb_codes, codes_eager)
+        ops.prepare_linear(X, g, w)     # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_prepare_linear_same_buffers_new_data():
+    # consecutive calls write different activations into the same buffers
+    # (36-byte scale rows: neighbouring rows share cache lines); every call
+    # must see its own producers' bytes, never a cached copy of the last call's
+    T, K, D = 7, 1152, 600
+    cases = [synth.random_case(700 + i, T, K, D) for i in range(3)]
+    w = ops.pack_weight(dev_w(cases[0].w, cases[0].dtype))
+    refs = []
+    for c in cases:
+        X, g = dev_x(c), dev_gamma(c.gamma)
+        a2 = ops.prepare(X, g, 1e-6)
+        refs.append((X, g, a2, ops.linear(a2, w)))
+    act = ops.empty_act("mxfp4", T, K)
+    Y = torch.empty((T, D), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        for X, g, a2, Y2 in refs:
+            ops.prepare_linear(X, g, w, act=act, out=Y)
+            torch.cuda.synchronize()
+            assert torch.equal(Y, Y2)
+            for k in ("bb_codes", "bb_meta", "bb_scale", "res_codes", "res_scale"):
+                assert torch.equal(getattr(act, k), getattr(a2, k)), k
