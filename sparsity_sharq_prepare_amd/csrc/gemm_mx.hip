@@ -196,24 +196,26 @@ __global__ __launch_bounds__(MT >= 8 ? 512 : 1024) void linear_mx_skinny(
 // grid.x = ceil(D / 16 CG) (+ rows producer workgroups first when fused),
 // 64 NW threads, NW J >= K / 128.
 //
-// Fused (single-launch decode, rows <= 8): workgroups 0, 8, .., 8 (rows-1)
-// each prepare one activation row (prepare_row_mx: the standalone prepare's
-// outputs, bit for bit) into the activation buffers, write their L2 back
-// (agent-scope release) and increment sync[0].  Workgroups go to the 8 XCDs
-// round robin, so all producers share XCD 0 and its L2: every prepared byte
-// is written through one L2.  The other workgroups are the GEMM's: they issue
-// their weight loads first, then wait (one lane, bounded polling) until
-// sync[0] reaches rows, and only then load the prepared activations with
-// ordinary loads: on XCD 0 they hit the producers' L2, elsewhere the L2 holds
-// no line of these buffers (caches are invalidated at kernel start and
-// nothing reads them before the wait), so the first read fetches the
-// written-back bytes and later ones hit.  The weight stream overlaps the
-// preparation.  Workgroups are dispatched in index order on every XCD, so
-// the producers are resident before any waiting workgroup can hold their
-// place.  The last GEMM workgroup past the wait resets sync[0] and sync[1] to
-// zero for the next call.
+// Fused (single-launch decode, rows <= 8): GEMM workgroups 0, 8, .., 8 (rows-1)
+// also prepare one activation row each (RowPrep: the standalone prepare's
+// outputs, bit for bit): they load the row and gamma, then their weights,
+// quantize and store the row with write-through stores, wait until all of it
+// is done, and increment sync[0] at memory.  (A release that writes the L2
+// back costs microseconds; write-through stores need none.)  Workgroups go to
+// the 8 XCDs round robin, so all producers share XCD 0 and its L2.  Every GEMM workgroup issues its weight loads,
+// then waits (one lane, bounded polling) until sync[0] reaches rows, and only
+// then loads the prepared activations with ordinary loads: on XCD 0 they hit
+// the producers' L2, elsewhere the L2 holds no line of these buffers (caches
+// are invalidated at kernel start and nothing reads them before the wait), so
+// the first read fetches the written-back bytes and later ones hit.  The
+// weight stream overlaps the preparation.  Workgroups are dispatched in index
+// order on every XCD and the producers come first on XCD 0, so they are
+// resident before any waiting workgroup can hold their place.  The last GEMM
+// workgroup past the wait resets sync[0] and sync[1] to zero for the next
+// call.
 constexpr int kDecodeMaxK = 16384;                   // staged operand + reduction fit in LDS
 constexpr uint32_t kFusedSpinMax = 1u << 20;         // polls before giving up (the kernel always ends)
+constexpr int kAuxWriteThrough = 16;                 // store cache policy sc1: written through to memory
 
 struct FusedPrep {
   const void* X;               // activation rows (bf16 or fp32), row r at X + r * ldx elements
@@ -247,24 +249,18 @@ __global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
   };
 
   const int n_gemm = (D + 16 * CG - 1) / (16 * CG);
-  int bx = blockIdx.x;
+  const int bx = blockIdx.x;
+  // fused: workgroup bx (bx % 8 == 0) also prepares row bx / 8; its row and
+  // gamma loads go out first, ahead of the weight loads (K / (8 NT) <= J / 4
+  // groups per thread for every decode geometry)
+  constexpr int PMAXC = J / 4 > 0 ? J / 4 : 1;
+  RowPrep<NT, PMAXC, kAuxWriteThrough> rp;
+  bool producer = false;
   if constexpr (FUSED) {
-    const int b = blockIdx.x;
-    if ((b & 7) == 0 && (b >> 3) < rows) {         // producer of row b / 8 (uniform)
-      const int r = b >> 3;
-      prepare_row_mx<NT, 0>(fp.X, fp.bf16 != 0, K, (int64_t)r * fp.ldx, fp.gamma, fp.eps, r,
-                         const_cast<uint8_t*>(bb_codes), const_cast<uint8_t*>(bb_meta), const_cast<uint8_t*>(bb_scale),
-                         const_cast<uint8_t*>(res_codes), const_cast<uint8_t*>(res_scale),
-                         reinterpret_cast<float*>(dsm));
-      // every wave's stores have reached the L2, then one write-back of it
-      // (the release of the increment) publishes the whole row
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (tid == 0) __hip_atomic_fetch_add(&fp.sync[0], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      return;
-    }
-    bx = b - min(rows, (b + 7) >> 3);               // producers before b: 0, 8, ..
-    if (bx >= n_gemm) return;                        // padding (grid covers producer 8 (rows-1))
+    producer = (bx & 7) == 0 && (bx >> 3) < rows;   // uniform
+    if (producer) rp.load(fp.X, fp.bf16 != 0, K, (int64_t)(bx >> 3) * fp.ldx, fp.gamma);
+    else if (bx >= n_gemm) return;                   // padding (the grid covers producer 8 (rows-1))
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- activation loads (L2 hits): item i is block i >> 3 of token i & 7; a
@@ -331,6 +327,18 @@ __global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
   __builtin_amdgcn_sched_barrier(0);
 
   if constexpr (FUSED) {
+    if (producer) {
+      rp.finish(fp.bf16 != 0, K, fp.gamma, fp.eps, bx >> 3, const_cast<uint8_t*>(bb_codes),
+                const_cast<uint8_t*>(bb_meta), const_cast<uint8_t*>(bb_scale), const_cast<uint8_t*>(res_codes),
+                const_cast<uint8_t*>(res_scale), reinterpret_cast<float*>(dsm));
+      // every wave's loads and write-through stores are done (the row is in
+      // memory), then the increment, performed at memory (system scope: no
+      // L2 write-back is needed, and none is made)
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) __hip_atomic_fetch_add(&fp.sync[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      if (bx >= n_gemm) return;                      // producer only (tiny D)
+    }
     if (tid == 0) {
       for (uint32_t it = 0; it < kFusedSpinMax; ++it) {
         if (__hip_atomic_load(&fp.sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)rows) break;
@@ -1005,8 +1013,8 @@ hipError_t launch_decode(const uint8_t* bb_codes, const uint8_t* bb_meta, const 
   while (NK * CG * 2 <= 16 && (D + 16 * CG * 2 - 1) / (16 * CG * 2) >= 256) CG *= 2;
   const size_t lds = (size_t)(K / 32 + 1) * 17 * 16 + (size_t)NK * CG * 64 * 4 * sizeof(float);
   const int n_gemm = (D + 16 * CG - 1) / (16 * CG);
-  // fused: rows producers at workgroups 0, 8, .. among the GEMM workgroups
-  dim3 grid(FUSED ? std::max(n_gemm + rows, 8 * (rows - 1) + 1) : n_gemm), block(64 * NK * CG);
+  // fused: the producers are workgroups 0, 8, .., 8 (rows - 1)
+  dim3 grid(FUSED ? std::max(n_gemm, 8 * (rows - 1) + 1) : n_gemm), block(64 * NK * CG);
 #define L(NK_, CG_, J_)                                                                                                 \
   hipLaunchKernelGGL((linear_mx_decode<NK_, CG_, J_, FUSED>), grid, block, lds, s, bb_codes, bb_meta, bb_scale,         \
                      res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, Y, ldy, fp)

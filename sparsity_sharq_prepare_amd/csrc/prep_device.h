@@ -109,92 +109,118 @@ SHARQ_DEV __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint64_t off, uint32
                                            (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
-// One activation row prepared by the NT threads of a workgroup, reading the
-// row twice (sum of squares, then quantization) chunk by chunk: the MXFP4
-// outputs of the standalone prepare kernel, bit for bit.  Chunk c holds
-// groups c NT .. c NT + NT - 1, so the sum of squares follows the same
-// pinned pairwise tree: group tree, wave butterfly (aligned 512-value
-// blocks), the chunk's waves in order, then the chunks as a tree (zero
-// padding to a power of two).  red: LDS scratch of at least
-// nch * NT / 64 + 2 * nch + 1 floats, nch = ceil(K / (8 NT)).  AUX: cache
-// policy of the output stores.  Ends with a workgroup barrier.
-template <int NT, int AUX>
-SHARQ_DEV void prepare_row_mx(const void* X, bool bf16, int K, int64_t row_elem_off, const float* gamma, float eps,
-                              int row, uint8_t* bb_codes, uint8_t* bb_meta, uint8_t* bb_scale, uint8_t* res_codes,
-                              uint8_t* res_scale, float* red) {
-  constexpr int WPR = NT / kWave;
-  const int t = threadIdx.x, l = t & (kWave - 1), w = t / kWave;
-  const int G = K >> 3;
-  const int nch = (G + NT - 1) / NT;
-  const uint32_t es = bf16 ? 2u : 4u;
-  const __amdgpu_buffer_rsrc_t rx = row_rsrc(X, (uint64_t)row_elem_off * es, (uint32_t)K * es);
-  auto load = [&](uint32_t g, float x[8]) {
-    if (bf16) {
-      const auto a = __builtin_amdgcn_raw_buffer_load_b128(rx, 16u * g, 0, 0);
-      unpack_group<true>(make_uint4(a[0], a[1], a[2], a[3]), make_uint4(0, 0, 0, 0), x);
-    } else {
-      const auto a = __builtin_amdgcn_raw_buffer_load_b128(rx, 32u * g, 0, 0);
-      const auto b = __builtin_amdgcn_raw_buffer_load_b128(rx, 32u * g + 16u, 0, 0);
-      unpack_group<false>(make_uint4(a[0], a[1], a[2], a[3]), make_uint4(b[0], b[1], b[2], b[3]), x);
-    }
-  };
+// One activation row prepared by the NT threads of a workgroup, held in
+// registers (at most MAXC groups of 8 per thread): the MXFP4 outputs of the
+// standalone prepare kernel, bit for bit.  Chunk c holds groups
+// c NT .. c NT + NT - 1, so the sum of squares follows the same pinned
+// pairwise tree: group tree, wave butterfly (aligned 512-value blocks), the
+// chunk's waves in order, then the chunks as a tree (zero padding to a power
+// of two).  load() only issues the row's and gamma's loads, so the caller can
+// put other loads behind them; finish() computes and stores (cache policy
+// AUX).
+template <int NT, int MAXC, int AUX = 0>
+struct RowPrep {
+  static constexpr int WPR = NT / kWave;
+  uint4 xa[MAXC], xb[MAXC];    // the thread's groups (bf16: xa; fp32: xa, xb)
+  float4 ga[MAXC], gb[MAXC];   // their gamma
 
-  float inv = 1.0f;
-  if (gamma) {
-    for (int c = 0; c < nch; ++c) {                 // uniform trip count: whole waves take part
-      float x[8];
-      load((uint32_t)(c * NT + t), x);               // groups past K read zeros
-      const float s = wave_tree_sum(tree8_sq(x));
-      if (l == 0) red[c * WPR + w] = s;
-    }
-    __syncthreads();
-    if (t == 0) {
-      int np = 1;
-      while (np < nch) np <<= 1;
-      float* part = red + nch * WPR;
-      for (int c = 0; c < np; ++c) {
-        float v[WPR];
+  // row_elem_off: element offset of the row in X; K / (8 NT) <= MAXC
+  SHARQ_DEV void load(const void* X, bool bf16, int K, int64_t row_elem_off, const float* gamma) {
+    const int t = threadIdx.x, G = K >> 3;
+    const uint32_t es = bf16 ? 2u : 4u;
+    const __amdgpu_buffer_rsrc_t rx = row_rsrc(X, (uint64_t)row_elem_off * es, (uint32_t)K * es);
 #pragma unroll
-        for (int i = 0; i < WPR; ++i) v[i] = c < nch ? red[c * WPR + i] : 0.0f;
-#pragma unroll
-        for (int n = WPR / 2; n >= 1; n >>= 1) {
-#pragma unroll
-          for (int i = 0; i < n; ++i) v[i] = __fadd_rn(v[2 * i], v[2 * i + 1]);
-        }
-        part[c] = v[0];
+    for (int c = 0; c < MAXC; ++c) {
+      const uint32_t g = (uint32_t)(c * NT + t);     // groups past K read zeros
+      if (bf16) {
+        const auto a = __builtin_amdgcn_raw_buffer_load_b128(rx, 16u * g, 0, 0);
+        xa[c] = make_uint4(a[0], a[1], a[2], a[3]);
+        xb[c] = make_uint4(0, 0, 0, 0);
+      } else {
+        const auto a = __builtin_amdgcn_raw_buffer_load_b128(rx, 32u * g, 0, 0);
+        const auto b = __builtin_amdgcn_raw_buffer_load_b128(rx, 32u * g + 16u, 0, 0);
+        xa[c] = make_uint4(a[0], a[1], a[2], a[3]);
+        xb[c] = make_uint4(b[0], b[1], b[2], b[3]);
       }
-      for (int n = np / 2; n >= 1; n >>= 1)
-        for (int i = 0; i < n; ++i) part[i] = __fadd_rn(part[2 * i], part[2 * i + 1]);
-      const float ms = __fdiv_rn(part[0], (float)K);
-      part[np] = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(ms, eps)));
+      if (gamma) {
+        const uint32_t k0 = g < (uint32_t)G ? 8u * g : 0u;   // lanes past K hold zeros
+        ga[c] = *reinterpret_cast<const float4*>(gamma + k0);
+        gb[c] = *reinterpret_cast<const float4*>(gamma + k0 + 4);
+      }
     }
-    __syncthreads();
-    int np = 1;
-    while (np < nch) np <<= 1;
-    inv = red[nch * WPR + np];
   }
 
-  const __amdgpu_buffer_rsrc_t o_bc = row_rsrc(bb_codes, (uint64_t)row * (K >> 2), K >> 2);
-  const __amdgpu_buffer_rsrc_t o_rc = row_rsrc(res_codes, (uint64_t)row * (K >> 1), K >> 1);
-  const __amdgpu_buffer_rsrc_t o_mt = row_rsrc(bb_meta, (uint64_t)row * (K >> 4), K >> 4);
-  const __amdgpu_buffer_rsrc_t o_sb = row_rsrc(bb_scale, (uint64_t)row * (K >> 5), K >> 5);
-  const __amdgpu_buffer_rsrc_t o_sr = row_rsrc(res_scale, (uint64_t)row * (K >> 5), K >> 5);
-  for (int c = 0; c < nch; ++c) {
-    const uint32_t g = (uint32_t)(c * NT + t);
-    float y[8];
-    load(g, y);
-    if (gamma) {
-      const uint32_t k0 = g < (uint32_t)G ? 8u * g : 0u;   // lanes past K hold zeros
-      const float4 ga = *reinterpret_cast<const float4*>(gamma + k0);
-      const float4 gb = *reinterpret_cast<const float4*>(gamma + k0 + 4);
-      const float gm[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] = __fmul_rn(__fmul_rn(y[i], inv), gm[i]);
-    }
-    mx_quantize_store<AUX>(y, g, o_bc, o_rc, o_mt, o_sb, o_sr);
+  SHARQ_DEV void get(bool bf16, int c, float x[8]) const {
+    if (bf16) unpack_group<true>(xa[c], xb[c], x);
+    else unpack_group<false>(xa[c], xb[c], x);
   }
-  __syncthreads();
-}
+
+  // red: LDS scratch of at least MAXC * NT / 64 + 1 floats.  Ends with a
+  // workgroup barrier; stores are issued, not awaited.
+  SHARQ_DEV void finish(bool bf16, int K, const float* gamma, float eps, int row, uint8_t* bb_codes,
+                        uint8_t* bb_meta, uint8_t* bb_scale, uint8_t* res_codes, uint8_t* res_scale,
+                        float* red) const {
+    const int t = threadIdx.x, l = t & (kWave - 1), w = t / kWave;
+    float inv = 1.0f;
+    if (gamma) {
+      float part[MAXC];
+#pragma unroll
+      for (int c = 0; c < MAXC; ++c) {
+        float x[8];
+        get(bf16, c, x);
+        part[c] = wave_tree_sum(tree8_sq(x));      // chunks past K contribute +0
+      }
+      if (l == 0) {
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) red[c * WPR + w] = part[c];
+      }
+      __syncthreads();
+      if (t == 0) {
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+          float v[WPR];
+#pragma unroll
+          for (int i = 0; i < WPR; ++i) v[i] = red[c * WPR + i];
+#pragma unroll
+          for (int n = WPR / 2; n >= 1; n >>= 1) {
+#pragma unroll
+            for (int i = 0; i < n; ++i) v[i] = __fadd_rn(v[2 * i], v[2 * i + 1]);
+          }
+          part[c] = v[0];
+        }
+#pragma unroll
+        for (int n = MAXC / 2; n >= 1; n >>= 1) {
+#pragma unroll
+          for (int i = 0; i < n; ++i) part[i] = __fadd_rn(part[2 * i], part[2 * i + 1]);
+        }
+        const float ms = __fdiv_rn(part[0], (float)K);
+        red[MAXC * WPR] = __fdiv_rn(1.0f, sqrt_rn(__fadd_rn(ms, eps)));
+      }
+      __syncthreads();
+      inv = red[MAXC * WPR];
+    }
+    const __amdgpu_buffer_rsrc_t o_bc = row_rsrc(bb_codes, (uint64_t)row * (K >> 2), K >> 2);
+    const __amdgpu_buffer_rsrc_t o_rc = row_rsrc(res_codes, (uint64_t)row * (K >> 1), K >> 1);
+    const __amdgpu_buffer_rsrc_t o_mt = row_rsrc(bb_meta, (uint64_t)row * (K >> 4), K >> 4);
+    const __amdgpu_buffer_rsrc_t o_sb = row_rsrc(bb_scale, (uint64_t)row * (K >> 5), K >> 5);
+    const __amdgpu_buffer_rsrc_t o_sr = row_rsrc(res_scale, (uint64_t)row * (K >> 5), K >> 5);
+    const int nch = ((K >> 3) + NT - 1) / NT;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      if (c >= nch) break;                           // whole chunk past K (uniform)
+      const uint32_t g = (uint32_t)(c * NT + t);
+      float y[8];
+      get(bf16, c, y);
+      if (gamma) {
+        const float gm[8] = {ga[c].x, ga[c].y, ga[c].z, ga[c].w, gb[c].x, gb[c].y, gb[c].z, gb[c].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = __fmul_rn(__fmul_rn(y[i], inv), gm[i]);
+      }
+      mx_quantize_store<AUX>(y, g, o_bc, o_rc, o_mt, o_sb, o_sr);
+    }
+    __syncthreads();
+  }
+};
 
 }  // namespace
 }  // namespace sharq
