@@ -1,4 +1,5 @@
-"""HBM traffic of a kernel from rocprofv3 counter passes.
+"""HBM traffic of a kernel from rocprofv3 counter passes, and kernel-trace
+summaries.
 
 Two `rocprofv3 --pmc` passes of the same command, one collecting FETCH_SIZE
 and one WRITE_SIZE (KiB per dispatch), give the bytes a kernel moved between
@@ -17,6 +18,12 @@ it is the largest copyBuffer dispatch of the run.
 The summary records traffic_bytes_per_launch (the kernel's average over its
 dispatches) and source_sha256, a hash of the kernel sources, so that bench.py
 ignores it once the kernel has changed.
+
+    python -m sparsity_sharq_prepare_amd.profiling trace \
+        --stats <rocprofv3 --kernel-trace --stats run_kernel_stats.csv> \
+        --title "..." --out profiles/<kernel>_<workload>_kernel_trace.txt --command "..."
+
+writes the per-kernel call count and average / min / max duration table.
 """
 from __future__ import annotations
 
@@ -24,6 +31,7 @@ import argparse
 import csv
 import hashlib
 import os
+import sys
 from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -32,6 +40,14 @@ SOURCES = {
     "linear_mx_tile": ["gemm_mx.hip", "common.h", "prep_device.h"],
     "linear_nv_tile": ["gemm_nv.hip", "common.h"],
     "prepare_mx_kernel": ["prepare.hip", "common.h", "prep_device.h"],
+}
+# dispatch names a kernel's counters are averaged over (all substrings must
+# match): the decode step's GEMM is the two-launch form (template flag false)
+MATCH = {
+    "linear_mx_decode": ("linear_mx_decode<", ", false>"),
+    "linear_mx_tile": ("linear_mx_tile",),
+    "linear_nv_tile": ("linear_nv_tile",),
+    "prepare_mx_kernel": ("prepare_mx_kernel",),
 }
 
 
@@ -63,13 +79,39 @@ def kernel_bytes(path: str, counter: str, kernel: str, copy_bytes: int):
     if not copies:
         raise SystemExit(f"{path}: no copyBuffer dispatch for the calibration")
     factor = copy_bytes / (max(copies) * 1024.0)
-    ks = [v for n, v in disp.values() if kernel in n]
+    ks = [v for n, v in disp.values() if all(m in n for m in MATCH[kernel])]
     if not ks:
         raise SystemExit(f"{path}: no dispatch of {kernel}")
     return sum(ks) / len(ks) * 1024.0 * factor, factor, len(ks)
 
 
+def trace_main(argv):
+    ap = argparse.ArgumentParser(description="kernel-trace summary from rocprofv3 --stats")
+    ap.add_argument("--stats", required=True)
+    ap.add_argument("--title", required=True)
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--command", default="")
+    ap.add_argument("--note", default="")
+    a = ap.parse_args(argv)
+    rows = list(csv.DictReader(open(a.stats, newline="")))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    with open(a.out, "w") as fh:
+        fh.write(f"# rocprofv3 kernel trace summary: {a.title}\n")
+        if a.command:
+            fh.write(f"# command: {a.command}\n")
+        if a.note:
+            fh.write(f"# {a.note}\n")
+        fh.write(f"{'kernel':<72s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}\n")
+        for r in rows:
+            name = r["Name"].split("(")[0][:72]
+            fh.write(f"{name:<72s} {int(r['Calls']):>6d} {float(r['AverageNs']) / 1e3:>9.2f} "
+                     f"{float(r['MinNs']) / 1e3:>9.2f} {float(r['MaxNs']) / 1e3:>9.2f} {float(r['Percentage']):>6.2f}\n")
+    print(open(a.out).read())
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "trace":
+        return trace_main(sys.argv[2:])
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--fetch", required=True)
     ap.add_argument("--write", required=True)
