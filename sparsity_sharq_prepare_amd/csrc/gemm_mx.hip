@@ -997,20 +997,23 @@ int num_cus_gemm() {
   return cached[dev];
 }
 
-// decode geometry: J = 4 K-steps per wave while 16 K-splits suffice, else 8;
-// column groups of 16 per workgroup while at least 256 workgroups remain and
-// the workgroup stays within 16 waves.  Fused: rows producer workgroups first.
+// decode geometry: J = 4 K-steps per wave up to K = 2048, 8 beyond (at most
+// 16 K-splits); column groups of 16 per workgroup while at least 200
+// workgroups remain and the workgroup stays within 16 waves.  Every
+// workgroup stages the whole activation, so fewer, wider workgroups read
+// less of it (measured: 4096 x 14336 with 224 workgroups of 4 column groups
+// 9.6 us, with 448 of 2 10.6 us; 16 steps per wave at K = 14336 is slower).
 template <bool FUSED>
 hipError_t launch_decode(const uint8_t* bb_codes, const uint8_t* bb_meta, const uint8_t* bb_scale,
                          const uint8_t* res_codes, const uint8_t* res_scale, const int32_t* row_index, int rows,
                          int act_rows, int K, const uint8_t* payload, const uint8_t* wscale, int D, float* Y, int64_t ldy,
                          FusedPrep fp, hipStream_t s) {
   const int KS = K / 128;
-  const int J = KS <= 64 ? 4 : 8;
+  const int J = KS <= 16 ? 4 : 8;
   int NK = 1;
   while (NK * J < KS) NK *= 2;
   int CG = 1;
-  while (NK * CG * 2 <= 16 && (D + 16 * CG * 2 - 1) / (16 * CG * 2) >= 256) CG *= 2;
+  while (NK * CG * 2 <= 16 && (D + 16 * CG * 2 - 1) / (16 * CG * 2) >= 200) CG *= 2;
   const size_t lds = (size_t)(K / 32 + 1) * 17 * 16 + (size_t)NK * CG * 64 * 4 * sizeof(float);
   const int n_gemm = (D + 16 * CG - 1) / (16 * CG);
   // fused: the producers are workgroups 0, 8, .., 8 (rows - 1)
@@ -1031,9 +1034,11 @@ hipError_t launch_decode(const uint8_t* bb_codes, const uint8_t* bb_meta, const 
     case 40401: L(4, 1, 4); break;
     case 40402: L(4, 2, 4); break;
     case 40404: L(4, 4, 4); break;
-    case 40801: L(8, 1, 4); break;
-    case 40802: L(8, 2, 4); break;
-    case 41601: L(16, 1, 4); break;
+    case 80401: L(4, 1, 8); break;
+    case 80402: L(4, 2, 8); break;
+    case 80404: L(4, 4, 8); break;
+    case 80801: L(8, 1, 8); break;
+    case 80802: L(8, 2, 8); break;
     case 81601: L(16, 1, 8); break;
     default: return hipErrorInvalidValue;
   }
