@@ -498,9 +498,12 @@ PrepGeom prep_geometry_mx(int T, int K) {
   g.threads = tpr > 256 ? tpr : 256;
   g.rpw = g.threads / tpr;
   const int nblk = (T + g.rpw - 1) / g.rpw;
+  // short rows (at most 2 groups per thread, few registers): one workgroup
+  // per row block, so that many waves per SIMD hide the latencies; long rows:
   // two workgroups of four waves per CU (two waves per SIMD), each looping
-  // over row blocks
-  g.blocks = nblk < 2 * num_cus() ? nblk : 2 * num_cus();
+  // over row blocks with the next rows prefetched (measured: 32768 x 768
+  // 23.6 vs 29.8 us; 4096 x 4096 16.6 vs 18.6 us the other way round)
+  g.blocks = (maxc <= 2 || nblk < 2 * num_cus()) ? nblk : 2 * num_cus();
   return g;
 }
 
