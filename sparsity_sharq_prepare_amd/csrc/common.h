@@ -65,9 +65,12 @@ SHARQ_DEV uint32_t e4m3_encode(float u) {
 }
 
 SHARQ_DEV float e4m3_decode(uint32_t code) {
-  uint32_t E = (code >> 3) & 15u, M = code & 7u;
-  if (E == 0) return __builtin_amdgcn_ldexpf((float)M, -9);
-  return __builtin_amdgcn_ldexpf((float)(8u + M), (int)E - 10);
+  const uint32_t E = (code >> 3) & 15u, M = code & 7u;
+  // subnormal (E = 0): M * 2^-9; normal: (8 + M) * 2^(E - 10); selects, not
+  // a branch, so that callers' loops stay one basic block
+  const uint32_t m = E == 0 ? M : 8u + M;
+  const int e = E == 0 ? -9 : (int)E - 10;
+  return __builtin_amdgcn_ldexpf((float)m, e);
 }
 
 // ---------------------------------------------------------------- E2M1 value
