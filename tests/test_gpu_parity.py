@@ -134,6 +134,8 @@ LINEAR_SHAPES = [  # skinny (T <= 64) and tile paths, ragged rows and columns
     # decode path (<= 8 rows): uneven steps per wave, the largest staged K, and
     # a K beyond it (general skinny path)
     (5, 1152, 72), (7, 16384, 48), (2, 18944, 40),
+    # degenerate widths: one output column, the smallest GEMM K
+    (3, 256, 1), (70, 512, 1), (1, 128, 16),
 ]
 
 
@@ -425,3 +427,52 @@ def test_prepare_linear_same_buffers_new_data():
             assert torch.equal(Y, Y2)
             for k in ("bb_codes", "bb_meta", "bb_scale", "res_codes", "res_scale"):
                 assert torch.equal(getattr(act, k), getattr(a2, k)), k
+
+
+# ------------------------------------------------------------------ edge cases
+def test_linear_zero_rows_and_empty_experts():
+    # a gathered linear of zero rows enqueues nothing (Y keeps its contents);
+    # a grouped linear whose first, a middle and the last expert have no rows
+    case = synth.random_case(31, 16, 512, 96)
+    act = ops.prepare(dev_x(case), dev_gamma(case.gamma), 1e-6)
+    w = ops.pack_weight(dev_w(case.w, case.dtype))
+    Y = torch.full((4, 96), 7.0, device="cuda")
+    ops.linear(act, w, row_index=torch.zeros(0, dtype=torch.int32, device="cuda"), total_rows=0, out=Y)
+    torch.cuda.synchronize()
+    assert bool(torch.all(Y == 7.0))
+    rng = np.random.default_rng(12)
+    E, K, D = 6, 256, 130
+    go = np.concatenate([[0], np.cumsum([0, 37, 0, 64, 5, 0])]).astype(np.int32)
+    case2 = synth.random_case(40, int(go[-1]), K, 1)
+    W = synth.f32_to_bf16_bits(rng.standard_normal((E, K, D)).astype(np.float32) * 0.02)
+    act2 = ops.prepare(dev_x(case2), dev_gamma(case2.gamma), 1e-6)
+    w2 = ops.pack_weight(dev_w(W, "bf16"))
+    Y2 = ops.linear(act2, w2, group_offsets=torch.from_numpy(go).cuda())
+    ref = oracle_prepare(case2)
+    wps = [O.pack_weight(synth.bf16_bits_to_f32(W[e])) for e in range(E)]
+    Yr, S = O.grouped_linear(ref, wps, go)
+    assert_gemm_close(Y2.cpu().numpy(), Yr, S)
+
+
+@pytest.mark.parametrize("T", [5, 40, 300])
+def test_strided_input_and_output(T):
+    # X rows further apart than K (a column slice of a wider buffer) and Y rows
+    # further apart than D: the same bytes and values as the contiguous call,
+    # and Y's padding columns untouched (decode, skinny and tile paths)
+    K, D = 512, 200
+    case = synth.random_case(51 + T, T, K, D)
+    X, g = dev_x(case), dev_gamma(case.gamma)
+    Xw = torch.zeros((T, K + 64), dtype=X.dtype, device="cuda")
+    Xw[:, 64:] = X
+    act_s = ops.prepare(Xw[:, 64:], g, 1e-6)
+    act = ops.prepare(X, g, 1e-6)
+    w = ops.pack_weight(dev_w(case.w, case.dtype))
+    Yw = torch.full((T, 256), -3.0, device="cuda")
+    ops.linear(act_s, w, out=Yw[:, :D])
+    Y = ops.linear(act, w)
+    torch.cuda.synchronize()
+    for k in ("bb_codes", "bb_meta", "bb_scale", "res_codes", "res_scale"):
+        assert torch.equal(getattr(act_s, k), getattr(act, k)), k
+    assert torch.equal(Yw[:, :D], Y)
+    assert bool(torch.all(Yw[:, D:] == -3.0))
+    compare_act(act, oracle_prepare(case))
