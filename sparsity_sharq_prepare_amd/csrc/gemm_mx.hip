@@ -530,7 +530,9 @@ __global__ __launch_bounds__(256 * WN, 1) void linear_mx_tile(
     const int nt = tiles_m * tiles_n;
     int b = blockIdx.x;
     if ((nt & 7) == 0) b = (b & 7) * (nt >> 3) + (b >> 3);   // consecutive tiles on one XCD
-    const int tm = b % tiles_m, tn = b / tiles_m;
+    // bands of 4 row tiles sweeping the columns, as in linear_mx_tile8
+    const int band = b / (4 * tiles_n), band_m = min(4, tiles_m - band * 4), in_band = b - band * 4 * tiles_n;
+    const int tm = band * 4 + in_band % band_m, tn = in_band / band_m;
     m0 = tm * BM;
     row_end = rows;
     n0 = tn * kBN;
@@ -819,12 +821,20 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int wq = w & 3;
 
-  // ---- tile -> (first row, first column); consecutive tiles on one XCD
+  // ---- tile -> (first row, first column). Tiles are ordered in bands of
+  // kBand row tiles that sweep all column tiles (row fastest inside a band),
+  // and each XCD takes one contiguous stretch of that order: the workgroups
+  // that run together on one XCD then share a few activation and weight
+  // tiles through its L2 instead of all 16 row tiles of the activations
+  // (measured at 4096 x 4096 x 14336: 269 -> 243 us)
   const int tiles_n = (D + BNE - 1) / BNE, tiles_m = (rows + BM - 1) / BM;
   const int nt = tiles_m * tiles_n;
   int bi = blockIdx.x;
   if ((nt & 7) == 0) bi = (bi & 7) * (nt >> 3) + (bi >> 3);
-  const int m0 = (bi % tiles_m) * BM, n0 = (bi / tiles_m) * BNE;
+  constexpr int kBand = 4;
+  const int band = bi / (kBand * tiles_n), band_m = min(kBand, tiles_m - band * kBand);
+  const int in_band = bi - band * kBand * tiles_n;
+  const int m0 = (band * kBand + in_band % band_m) * BM, n0 = (in_band / band_m) * BNE;
 
   const int KS = K >> 7, G = KS >> 2;
   const uint32_t kA = K >> 2, kM = K >> 4, kS = K >> 5, kR = K >> 1;
