@@ -192,6 +192,40 @@ sharq_status sharq_prepare_linear(const void *X, int32_t dtype, int32_t T, int32
                                   const sharq_weight *w, float *Y, int64_t ldy, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/* ---- Plain baseline (the unfused pipeline the fused preparation replaces,
+ * xllm-io paper review §5 kernel latency breakdown): RMSNorm, plain MXFP4
+ * quantization and a dense one-operand MXFP4 GEMM as three launches, for
+ * timing and error comparisons against the SharQ path. ---- */
+
+/* RMSNorm of T rows into fp32 y, with the fused preparation's pinned order
+ * (so y is bit-identical to the y that sharq_prepare quantizes).
+ * X: (device) T x K of `dtype`, row t at X + t * ldx; gamma: (device) K fp32
+ * or NULL (y = x); Y: (device) fp32 T x K, row t at Y + t * ldy (ldy >= K,
+ * rows 16-byte aligned).  K % 32 == 0, K <= the sharq_prepare maximum.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, HIP. */
+sharq_status sharq_rmsnorm(const void *X, int32_t dtype, int32_t T, int32_t K, int64_t ldx,
+                           const float *gamma, float eps, float *Y, int64_t ldy, void *stream);
+
+/* Plain MXFP4 quantization of fp32 rows (review §3.1 block scale rounded up
+ * to a power of two, §5.3): per 32-block e = the smallest integer with
+ * amax <= 6 * 2^e (E8M0 code e + 127), codes = E2M1 RNE of y / 2^e.
+ * Y: (device) fp32 T x K, row t at Y + t * ldy (rows 16-byte aligned);
+ * codes: (device) T x K/2 (two codes per byte, even K index in the low
+ * nibble); scales: (device) T x K/32.  K % 32 == 0.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, HIP. */
+sharq_status sharq_quantize_mx(const float *Y, int32_t T, int32_t K, int64_t ldy, uint8_t *codes,
+                               uint8_t *scales, void *stream);
+
+/* Dense one-operand MXFP4 GEMM Y = X~ W~ (fp32 accumulation) on the prefill
+ * tile kernel: the plain FP4 linear the dual-path GEMM is compared with.
+ * codes, scales: (device) plain MXFP4 activations as sharq_quantize_mx
+ * writes them (T rows); w: (host) MXFP4 weight, n_groups == 1, its dense
+ * scale view is used; Y: (device) fp32 T x D, row t at Y + t * ldy.
+ * w->K % 512 == 0; the size limits of sharq_linear apply.
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, FORMAT_MISMATCH, HIP. */
+sharq_status sharq_linear_dense(const uint8_t *codes, const uint8_t *scales, int32_t T,
+                                const sharq_weight *w, float *Y, int64_t ldy, void *stream);
+
 /* Static string naming a status code. */
 const char *sharq_status_string(sharq_status s);
 

@@ -439,6 +439,36 @@ def plain_quantized(y: np.ndarray, fmt: str = "mxfp4") -> np.ndarray:
     return nv_dequant_f64(c, sc, 16, s)
 
 
+def plain_prepare_mx(x: np.ndarray, gamma, eps: float = 1e-6) -> dict:
+    """The unfused pipeline that the fused preparation replaces (review §5,
+    kernel latency breakdown): RMSNorm (the pinned order of ``rmsnorm``), then
+    plain MXFP4 of y per 32-block (review §3.1, scale rounded up to a power of
+    two).  Returns y, the packed codes (T x K/2) and the E8M0 scale bytes
+    (T x K/32)."""
+    y = rmsnorm(x, gamma, eps)
+    c, e = mx_quantize(y)
+    return {"y": y, "codes": pack_nibbles(c), "scales": e8m0_encode_exponent(e)}
+
+
+def plain_linear_mx(codes: np.ndarray, scales: np.ndarray, wp: dict):
+    """Plain FP4 GEMM Y = X~ W~ in fp64 from the exact dequantized operand and
+    the weight's dense scale view, with the tolerance scale sum_k |x~_k w~_k|."""
+    Xt = mx_dequant_f64(unpack_nibbles(codes), e8m0_decode_exponent(scales))
+    W = weight_dequant(wp, "dn")
+    return Xt @ W, np.abs(Xt) @ np.abs(W)
+
+
+def plain_linear_mx_sampled(codes: np.ndarray, scales: np.ndarray, wp: dict, out_rows, out_cols):
+    """Y[out_rows[n], out_cols[n]] of ``plain_linear_mx`` for large shapes."""
+    ur, ir = np.unique(np.asarray(out_rows), return_inverse=True)
+    uc, ic = np.unique(np.asarray(out_cols), return_inverse=True)
+    Xt = mx_dequant_f64(unpack_nibbles(codes[ur]), e8m0_decode_exponent(scales[ur]))
+    W = weight_dequant(weight_cols(wp, uc), "dn")
+    Y = np.einsum("nk,kn->n", Xt[ir], W[:, ic])
+    S = np.einsum("nk,kn->n", np.abs(Xt[ir]), np.abs(W[:, ic]))
+    return Y, S
+
+
 def rel_frobenius(Y_hat: np.ndarray, Y_ref: np.ndarray) -> float:
     return float(np.linalg.norm(Y_hat - Y_ref) / np.linalg.norm(Y_ref))
 

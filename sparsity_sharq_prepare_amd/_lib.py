@@ -28,7 +28,8 @@ FORMATS = {"mxfp4": SHARQ_MXFP4, "nvfp4": SHARQ_NVFP4_EMU}
 
 # every entry point include/sharq.h declares
 EXPORTS = ("sharq_weight_sizes", "sharq_act_sizes", "sharq_pack_weight", "sharq_prepare", "sharq_linear",
-           "sharq_prepare_linear", "sharq_status_string", "sharq_last_error")
+           "sharq_prepare_linear", "sharq_rmsnorm", "sharq_quantize_mx", "sharq_linear_dense",
+           "sharq_status_string", "sharq_last_error")
 
 
 class SharqWeight(ctypes.Structure):
@@ -70,8 +71,13 @@ def lib() -> ctypes.CDLL:
         L.sharq_prepare_linear.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_int64, c_void_p, c_float,
                                            POINTER(SharqAct), POINTER(SharqWeight), c_void_p, c_int64, c_void_p,
                                            c_size_t, c_void_p]
+        L.sharq_rmsnorm.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_int64, c_void_p, c_float, c_void_p,
+                                    c_int64, c_void_p]
+        L.sharq_quantize_mx.argtypes = [c_void_p, c_int32, c_int32, c_int64, c_void_p, c_void_p, c_void_p]
+        L.sharq_linear_dense.argtypes = [c_void_p, c_void_p, c_int32, POINTER(SharqWeight), c_void_p, c_int64,
+                                         c_void_p]
         for name in ("sharq_weight_sizes", "sharq_act_sizes", "sharq_pack_weight", "sharq_prepare", "sharq_linear",
-                     "sharq_prepare_linear"):
+                     "sharq_prepare_linear", "sharq_rmsnorm", "sharq_quantize_mx", "sharq_linear_dense"):
             getattr(L, name).restype = c_int32
         L.sharq_status_string.argtypes = [c_int32]
         L.sharq_status_string.restype = c_char_p

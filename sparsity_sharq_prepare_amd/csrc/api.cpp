@@ -261,4 +261,59 @@ sharq_status sharq_prepare_linear(const void* X, int32_t dtype, int32_t T, int32
                   "sharq_prepare_linear launch");
 }
 
+sharq_status sharq_rmsnorm(const void* X, int32_t dtype, int32_t T, int32_t K, int64_t ldx, const float* gamma,
+                           float eps, float* Y, int64_t ldy, void* stream) {
+  if (!X || !Y) return fail(SHARQ_ERR_INVALID_ARGUMENT, "X and Y must not be NULL");
+  if (!valid_dtype(dtype)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  if (sharq_status st = check_k(K, 32)) return st;
+  if (T < 1) return fail(SHARQ_ERR_UNSUPPORTED_SHAPE, "T must be >= 1");
+  if (K > sharq::prepare_max_k())
+    return fail(SHARQ_ERR_UNSUPPORTED_SHAPE, "K = %d exceeds the supported maximum %d", K, sharq::prepare_max_k());
+  if (ldx < K || ldy < K) return fail(SHARQ_ERR_INVALID_ARGUMENT, "ldx and ldy must be >= K = %d", K);
+  if (!aligned16(X) || ((size_t)ldx * dtype_size(dtype)) % 16 != 0)
+    return fail(SHARQ_ERR_INVALID_ARGUMENT, "X rows must start 16-byte aligned");
+  if (!aligned16(Y) || ldy % 4 != 0) return fail(SHARQ_ERR_INVALID_ARGUMENT, "Y rows must start 16-byte aligned");
+  if (gamma && !aligned16(gamma)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "gamma must be 16-byte aligned");
+  if (!(eps >= 0.0f)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "eps must be >= 0");
+  return from_hip(sharq::launch_rmsnorm(X, dtype == SHARQ_BF16, T, K, ldx, gamma, eps, Y, ldy,
+                                        static_cast<hipStream_t>(stream)),
+                  "sharq_rmsnorm launch");
+}
+
+sharq_status sharq_quantize_mx(const float* Y, int32_t T, int32_t K, int64_t ldy, uint8_t* codes, uint8_t* scales,
+                               void* stream) {
+  if (!Y || !codes || !scales) return fail(SHARQ_ERR_INVALID_ARGUMENT, "Y, codes and scales must not be NULL");
+  if (sharq_status st = check_k(K, 32)) return st;
+  if (T < 1) return fail(SHARQ_ERR_UNSUPPORTED_SHAPE, "T must be >= 1");
+  if (ldy < K) return fail(SHARQ_ERR_INVALID_ARGUMENT, "ldy = %lld < K = %d", (long long)ldy, K);
+  if (!aligned16(Y) || ldy % 4 != 0) return fail(SHARQ_ERR_INVALID_ARGUMENT, "Y rows must start 16-byte aligned");
+  if (!aligned16(codes) || !aligned16(scales))
+    return fail(SHARQ_ERR_INVALID_ARGUMENT, "codes and scales must be 16-byte aligned");
+  return from_hip(sharq::launch_quantize_mx(Y, T, K, ldy, codes, scales, static_cast<hipStream_t>(stream)),
+                  "sharq_quantize_mx launch");
+}
+
+sharq_status sharq_linear_dense(const uint8_t* codes, const uint8_t* scales, int32_t T, const sharq_weight* w,
+                                float* Y, int64_t ldy, void* stream) {
+  if (!codes || !scales || !w || !Y) return fail(SHARQ_ERR_INVALID_ARGUMENT, "codes, scales, w and Y must not be NULL");
+  if (w->fmt != SHARQ_MXFP4) return fail(SHARQ_ERR_FORMAT_MISMATCH, "sharq_linear_dense takes an MXFP4 weight");
+  if (w->n_groups != 1) return fail(SHARQ_ERR_INVALID_ARGUMENT, "sharq_linear_dense is a plain linear (n_groups = 1)");
+  if (sharq_status st = check_k(w->K, 512)) return st;
+  if (T < 1 || w->D < 1) return fail(SHARQ_ERR_UNSUPPORTED_SHAPE, "T and D must be >= 1");
+  if (ldy < w->D) return fail(SHARQ_ERR_INVALID_ARGUMENT, "ldy = %lld < D = %d", (long long)ldy, w->D);
+  if (!aligned16(Y)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "Y must be 16-byte aligned");
+  const uint8_t* bufs[4] = {codes, scales, w->payload, w->scale_dn};
+  for (const uint8_t* p : bufs) {
+    if (!p) return fail(SHARQ_ERR_INVALID_ARGUMENT, "activation / weight buffers must not be NULL");
+    if (!aligned16(p)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "activation / weight buffers must be 16-byte aligned");
+  }
+  if ((int64_t)T * w->D > kMaxElems) return fail(SHARQ_ERR_UNSUPPORTED_SHAPE, "output too large");
+  if ((int64_t)T * (w->K / 2) > kMaxDescBytes || (int64_t)w->D * (w->K / 2) > kMaxDescBytes)
+    return fail(SHARQ_ERR_UNSUPPORTED_SHAPE, "activation codes (T*K/2) or weight payload (D*K/2) over %lld bytes",
+                (long long)kMaxDescBytes);
+  return from_hip(sharq::launch_linear_dense_mx(codes, scales, T, w->K, w->payload, w->scale_dn, w->D, Y, ldy,
+                                                static_cast<hipStream_t>(stream)),
+                  "sharq_linear_dense launch");
+}
+
 }  // extern "C"

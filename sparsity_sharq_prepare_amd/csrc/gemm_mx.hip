@@ -803,7 +803,7 @@ struct Tile8Side {             // four steps
 
 }  // namespace
 
-template <int WROWS, int BNE>
+template <int WROWS, int BNE, bool DENSE = false>
 __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
     const uint8_t* __restrict__ bb_codes, const uint8_t* __restrict__ bb_meta, const uint8_t* __restrict__ bb_scale,
     const uint8_t* __restrict__ res_codes, const uint8_t* __restrict__ res_scale, const int32_t* __restrict__ row_index,
@@ -812,8 +812,13 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
   // WROWS = 4: waves 4 (rows) x 2 (columns), 64 x 128 each; WROWS = 8: 8 x 1,
   // 32 x 256 each (every backbone fragment expanded by one wave only)
   // BNE: columns the tile computes (256, or 224 so that more shapes give a
-  // whole number of rounds over the CUs); staging stays 256 columns wide
+  // whole number of rounds over the CUs); staging stays 256 columns wide.
+  // DENSE: the plain MXFP4 GEMM of the comparison baseline, one operand
+  // (res_codes / res_scale hold plain codes and scales; no backbone)
   static_assert(BNE == kBN || WROWS == 8, "narrow tiles only with the 8 x 1 layout");
+  // DMA instructions per wave: per step (residual, weight, backbone codes) and
+  // per side group (metadata, activation scales, weight scales)
+  constexpr int NMAIN = DENSE ? 4 : 5, NSIDE = DENSE ? 2 : 3;
   constexpr int BM = 256, WM = BM / WROWS, WNC = BNE * WROWS / 8, FM = WM / 32, FN = WNC / 32;
   __shared__ Tile8Main lds[kNS];
   __shared__ Tile8Side side[2];
@@ -880,11 +885,15 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
     for (int j = 0; j < 2; ++j) dma16(r_dn, o_dn[j], s64, lds_addr(&st.a_dn[64 * (w + 8 * j)]));
 #pragma unroll
     for (int j = 0; j < 2; ++j) dma16(r_b, o_b[j], s64, lds_addr(&st.b[64 * (w + 8 * j)]));
-    dma16(r_sp, o_sp, s32, lds_addr(&st.a_sp[64 * w]));
+    if constexpr (!DENSE) dma16(r_sp, o_sp, s32, lds_addr(&st.a_sp[64 * w]));
   };
   auto issue_side = [&](int g, Tile8Side& sd) {
-    dma16(r_mt, o_mt, 32u * g, lds_addr(&sd.meta[64 * w]));
-    dma16(r_sa, o_sa, 16u * g, lds_addr(w < 4 ? &sd.s_sp[64 * wq] : &sd.s_dn[64 * wq]));
+    if constexpr (DENSE) {
+      dma16(r_sdn, o_sa, 16u * g, lds_addr(&sd.s_dn[64 * wq]));   // waves w and w + 4: same bytes
+    } else {
+      dma16(r_mt, o_mt, 32u * g, lds_addr(&sd.meta[64 * w]));
+      dma16(r_sa, o_sa, 16u * g, lds_addr(w < 4 ? &sd.s_sp[64 * wq] : &sd.s_dn[64 * wq]));
+    }
     dma16(r_sb, o_sw, 16u * g, lds_addr(&sd.s_b[64 * wq]));   // waves w and w + 4: same bytes
   };
 
@@ -910,9 +919,11 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
 #pragma unroll
     for (int f = 0; f < FM; ++f) {
       const int r = wm0 + 32 * f + lr;
-      S.sp[f] = st.a_sp[slot_sp(r, kh)];
-      S.mt[f] = meta[8 * r + 2 * p + kh];
-      S.ssp[f] = s_sp[8 * r + 2 * p + kh];
+      if constexpr (!DENSE) {
+        S.sp[f] = st.a_sp[slot_sp(r, kh)];
+        S.mt[f] = meta[8 * r + 2 * p + kh];
+        S.ssp[f] = s_sp[8 * r + 2 * p + kh];
+      }
       S.sdn[f] = s_dn[8 * r + 2 * p + kh];
     }
   };
@@ -934,10 +945,12 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
     constexpr int J = decltype(jc)::value;
 #pragma unroll
     for (int f = 0; f < FM; ++f) {
-      const uint4 asp = J == 0 ? expand4_fast(S.sp[f].x, S.sp[f].y, S.mt[f] & 0xFFFFu)
-                               : expand4_fast(S.sp[f].z, S.sp[f].w, S.mt[f] >> 16);
+      if constexpr (!DENSE) {
+        const uint4 asp = J == 0 ? expand4_fast(S.sp[f].x, S.sp[f].y, S.mt[f] & 0xFFFFu)
+                                 : expand4_fast(S.sp[f].z, S.sp[f].w, S.mt[f] >> 16);
 #pragma unroll
-      for (int n = 0; n < FN; ++n) acc[f][n] = mfma32_fp4_sel<J>(asp, H.b[n], acc[f][n], S.ssp[f], S.bs[n]);
+        for (int n = 0; n < FN; ++n) acc[f][n] = mfma32_fp4_sel<J>(asp, H.b[n], acc[f][n], S.ssp[f], S.bs[n]);
+      }
 #pragma unroll
       for (int n = 0; n < FN; ++n) acc[f][n] = mfma32_fp4_sel<J>(H.dn[f], H.b[n], acc[f][n], S.sdn[f], S.bs[n]);
     }
@@ -958,8 +971,8 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
       // stage s (and at p = 0 side group g) landed; stage s+1 (and after
       // p = 2 side group g+1) may still be in flight.  After the barrier every
       // wave is past its reads of step s-1, whose buffer stage s+2 reuses.
-      if (p == 3) wait_vm_lgkm0<8>();
-      else wait_vm_lgkm0<5>();
+      if (p == 3) wait_vm_lgkm0<NMAIN + NSIDE>();
+      else wait_vm_lgkm0<NMAIN>();
       __builtin_amdgcn_s_barrier();
       issue_main(min(s + 2, KS - 1), lds[(s + 2) % kNS]);
       // side group g+1 replaces group g-1, last read at step 4 g - 1
@@ -1128,6 +1141,25 @@ hipError_t launch_linear_mx(const uint8_t* bb_codes, const uint8_t* bb_meta, con
                        res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, n_groups, group_offsets, Y,
                        ldy);
   }
+  return hipGetLastError();
+}
+
+// plain dense MXFP4 GEMM of the comparison baseline: Y = X~ W~ with one
+// operand (codes T x K/2, E8M0 scales T x K/32), on the prefill tile
+hipError_t launch_linear_dense_mx(const uint8_t* codes, const uint8_t* scales, int rows, int K, const uint8_t* payload,
+                                  const uint8_t* wscale, int D, float* Y, int64_t ldy, hipStream_t s) {
+  if (rows <= 0 || D <= 0) return hipSuccess;
+  if (K % 512 != 0) return hipErrorInvalidValue;
+  const int tiles_m = (rows + 255) / 256;
+  const int ncu = num_cus_gemm();
+  const int t256 = tiles_m * ((D + 255) / 256), t224 = tiles_m * ((D + 223) / 224);
+  const bool narrow = (int64_t)((t224 + ncu - 1) / ncu) * 224 < (int64_t)((t256 + ncu - 1) / ncu) * 256;
+  if (narrow)
+    hipLaunchKernelGGL((linear_mx_tile8<8, 224, true>), dim3(t224), dim3(512), 0, s, nullptr, nullptr, nullptr, codes,
+                       scales, nullptr, rows, rows, K, payload, wscale, D, Y, ldy);
+  else
+    hipLaunchKernelGGL((linear_mx_tile8<8, 256, true>), dim3(t256), dim3(512), 0, s, nullptr, nullptr, nullptr, codes,
+                       scales, nullptr, rows, rows, K, payload, wscale, D, Y, ldy);
   return hipGetLastError();
 }
 

@@ -26,6 +26,15 @@ hipError_t launch_prepare_nv(const void* X, bool bf16, int T, int K, int64_t ldx
                              uint8_t* bb_codes, uint8_t* bb_meta, uint8_t* bb_scale, uint8_t* res_codes,
                              uint8_t* res_scale, float* tensor_scales, void* workspace, hipStream_t s);
 
+// plain baseline: RMSNorm to fp32 rows (the fused preparation's pinned
+// order), MXFP4 quantization of fp32 rows, dense MXFP4 GEMM (K % 512 == 0)
+hipError_t launch_rmsnorm(const void* X, bool bf16, int T, int K, int64_t ldx, const float* gamma, float eps, float* Y,
+                          int64_t ldy, hipStream_t s);
+hipError_t launch_quantize_mx(const float* Y, int T, int K, int64_t ldy, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s);
+hipError_t launch_linear_dense_mx(const uint8_t* codes, const uint8_t* scales, int rows, int K, const uint8_t* payload,
+                                  const uint8_t* wscale, int D, float* Y, int64_t ldy, hipStream_t s);
+
 hipError_t launch_pack(const void* W, bool bf16, bool nv, int K, int D, int n_groups, int64_t ldw, int64_t gstride,
                        uint8_t* payload, uint8_t* scale_sp, uint8_t* scale_dn, float* tscale, void* workspace,
                        hipStream_t s);

@@ -260,6 +260,81 @@ __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void prepare_mx_kernel(const
 }
 
 // ============================================================================
+// Plain baseline: RMSNorm and MXFP4 quantization as two separate kernels,
+// the unfused pipeline that the fused preparation replaces (xllm-io paper
+// review, kernel latency breakdown of §5).  y goes through HBM in fp32, the
+// precision the fused path keeps it in.
+// ============================================================================
+template <int TPR, int MAXC, bool BF16, bool NORM>
+__global__ __launch_bounds__(TPR > 256 ? TPR : 256) void rmsnorm_kernel(const void* __restrict__ X, int T, int K,
+                                                                        int64_t ldx, const float* __restrict__ gamma,
+                                                                        float eps, float* __restrict__ Y, int64_t ldy) {
+  constexpr int WGT = TPR > 256 ? TPR : 256, RPW = WGT / TPR, WPR = TPR / kWave;
+  __shared__ float red[RPW * MAXC * WPR];
+  const int tid = threadIdx.x;
+  const int rsub = __builtin_amdgcn_readfirstlane(tid / TPR);
+  const int t = tid % TPR, G = K >> 3;
+  const int nblk = (T + RPW - 1) / RPW;
+  for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const int row = blk * RPW + rsub;
+    const bool ok = row < T;
+    RowRegs<TPR, MAXC, BF16> rr;
+    rr.load(X, (int64_t)(ok ? row : 0) * ldx, G, t, ok);
+    // the same pinned 1/rms and y = (x * inv) * gamma as the fused preparation
+    const float inv = NORM ? row_inv_rms<TPR, MAXC, BF16>(rr, K, eps, t, rsub, red) : 1.0f;
+    float* yr = Y + (int64_t)(ok ? row : 0) * ldy;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      if (c * TPR >= G) break;                        // whole chunk beyond the row (uniform)
+      const int g = c * TPR + t;
+      float y[8];
+      rr.get(c, y);
+      if (NORM) normalize(y, inv, gamma, 8 * (int64_t)(g < G ? g : 0));
+      if (ok && g < G) {
+        float4* o = reinterpret_cast<float4*>(yr + 8 * (int64_t)g);
+        o[0] = make_float4(y[0], y[1], y[2], y[3]);
+        o[1] = make_float4(y[4], y[5], y[6], y[7]);
+      }
+    }
+    __syncthreads();                                  // red is reused by the next block's rows
+  }
+}
+
+// Plain MXFP4 of fp32 rows (review §3.1 block scale, rounded up to a power of
+// two): one group of 8 per thread, the 4 groups of a 32-block in one quad;
+// the block scale comes from the quad's max and is stored by its first lane.
+__global__ __launch_bounds__(256) void quantize_mx_kernel(const float* __restrict__ Y, int T, int K, int64_t ldy,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+  const int G = K >> 3;
+  const int g = blockIdx.x * 256 + threadIdx.x;
+  const bool ok = g < G;                              // uniform per quad: G % 4 == 0
+  for (int row = blockIdx.y; row < T; row += gridDim.y) {
+    float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (ok) {
+      const float4* src = reinterpret_cast<const float4*>(Y + (int64_t)row * ldy + 8 * (int64_t)g);
+      const float4 a = src[0], b = src[1];
+      y[0] = a.x; y[1] = a.y; y[2] = a.z; y[3] = a.w;
+      y[4] = b.x; y[5] = b.y; y[6] = b.z; y[7] = b.w;
+    }
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(y[i]));
+    const uint32_t e = e8m0_code(quad_max(am));
+    const float sc = exp2i((int)e - 127);
+    uint32_t w = 0;
+    w = cvt_fp4x2<0>(w, y[0], y[1], sc);
+    w = cvt_fp4x2<1>(w, y[2], y[3], sc);
+    w = cvt_fp4x2<2>(w, y[4], y[5], sc);
+    w = cvt_fp4x2<3>(w, y[6], y[7], sc);
+    if (ok) {
+      reinterpret_cast<uint32_t*>(codes + (int64_t)row * (K >> 1))[g] = w;
+      if ((g & 3) == 0) scales[(int64_t)row * (K >> 5) + (g >> 2)] = (uint8_t)e;
+    }
+  }
+}
+
+// ============================================================================
 // NVFP4 (emulated): phase 1 = RMSNorm + amax(y); phase 2 = mask, backbone
 // (E4M3 per 32 logical positions under s_sp), amax(R); phase 3 = residual
 // (E4M3 per 16 under s_dn).  Phases 2 and 3 recompute y from X with the
@@ -552,6 +627,34 @@ hipError_t launch_prepare_mx(const void* X, bool bf16, int T, int K, int64_t ldx
   SHARQ_PREP_MX_DISPATCH(L)
 #undef L
 #undef L2
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const void* X, bool bf16, int T, int K, int64_t ldx, const float* gamma, float eps, float* Y,
+                          int64_t ldy, hipStream_t s) {
+  const PrepGeom g = prep_geometry_mx(T, K);
+#define L2(TPR, MAXC, B, N)                                                                                 \
+  hipLaunchKernelGGL((rmsnorm_kernel<TPR, MAXC, B, N>), dim3(g.blocks), dim3(g.threads), 0, s, X, T, K, ldx, \
+                     gamma, eps, Y, ldy)
+#define L(TPR, MAXC)                                   \
+  if (bf16) {                                          \
+    if (gamma) L2(TPR, MAXC, true, true);              \
+    else L2(TPR, MAXC, true, false);                   \
+  } else {                                             \
+    if (gamma) L2(TPR, MAXC, false, true);             \
+    else L2(TPR, MAXC, false, false);                  \
+  }
+  SHARQ_PREP_MX_DISPATCH(L)
+#undef L
+#undef L2
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mx(const float* Y, int T, int K, int64_t ldy, uint8_t* codes, uint8_t* scales,
+                              hipStream_t s) {
+  const int G = K / 8;
+  dim3 grid((G + 255) / 256, T < 65535 ? T : 65535);
+  hipLaunchKernelGGL(quantize_mx_kernel, grid, dim3(256), 0, s, Y, T, K, ldy, codes, scales);
   return hipGetLastError();
 }
 

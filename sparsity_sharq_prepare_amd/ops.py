@@ -1,5 +1,5 @@
 """Thin PyTorch binding of the SharQ C ABI (pack_weight, prepare, linear,
-prepare_linear).
+prepare_linear, and the plain baseline rmsnorm, quantize_mx, linear_dense).
 
 PyTorch provides device memory and the stream; each function allocates its
 outputs as torch tensors, fills the C structs with their device pointers and
@@ -186,3 +186,49 @@ def prepare_linear(X: torch.Tensor, gamma: Optional[torch.Tensor], w: PackedWeig
                                          act.struct(), w.struct(), out.data_ptr(), out.stride(0), ws.data_ptr(),
                                          ws.numel(), _stream_ptr(stream)))
     return act, out
+
+
+# ----------------------------------------------------------------------------
+# plain baseline: RMSNorm, plain MXFP4 quantization, dense MXFP4 GEMM
+# ----------------------------------------------------------------------------
+def rmsnorm(X: torch.Tensor, gamma: Optional[torch.Tensor], eps: float = 1e-6,
+            out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """RMSNorm of X (T x K, fp32 or bf16) into fp32 y (T x K), the fused
+    preparation's pinned order."""
+    _dev_check(X, gamma, out)
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be a 2-D tensor contiguous along K")
+    T, K = X.shape
+    if out is None:
+        out = torch.empty((T, K), dtype=torch.float32, device=X.device)
+    L.check(L.lib().sharq_rmsnorm(X.data_ptr(), _dtype_code(X), T, K, X.stride(0), _ptr(gamma), eps,
+                                  out.data_ptr(), out.stride(0), _stream_ptr(stream)))
+    return out
+
+
+def quantize_mx(Y: torch.Tensor, codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,
+                stream=None):
+    """Plain MXFP4 quantization of fp32 rows: (codes T x K/2, E8M0 scales T x K/32)."""
+    _dev_check(Y, codes, scales)
+    if Y.dim() != 2 or Y.stride(1) != 1 or Y.dtype != torch.float32:
+        raise ValueError("Y must be a 2-D float32 tensor contiguous along K")
+    T, K = Y.shape
+    if codes is None:
+        codes = torch.empty((T, K // 2), dtype=torch.uint8, device=Y.device)
+    if scales is None:
+        scales = torch.empty((T, K // 32), dtype=torch.uint8, device=Y.device)
+    L.check(L.lib().sharq_quantize_mx(Y.data_ptr(), T, K, Y.stride(0), codes.data_ptr(), scales.data_ptr(),
+                                      _stream_ptr(stream)))
+    return codes, scales
+
+
+def linear_dense(codes: torch.Tensor, scales: torch.Tensor, w: PackedWeight, out: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    """Dense one-operand MXFP4 GEMM Y = X~ W~ (fp32, T x D)."""
+    _dev_check(codes, scales, out)
+    T = codes.shape[0]
+    if out is None:
+        out = torch.empty((T, w.D), dtype=torch.float32, device=codes.device)
+    L.check(L.lib().sharq_linear_dense(codes.data_ptr(), scales.data_ptr(), T, w.struct(), out.data_ptr(),
+                                       out.stride(0), _stream_ptr(stream)))
+    return out

@@ -164,3 +164,29 @@ def test_prepare_linear_validation_errors():
     assert f(X, 7, 8, 256, 256, None, 1e-6, a, w, Y, 64, ws, 16, None) == L.SHARQ_ERR_INVALID_ARGUMENT
     assert f(X, 1, 8, 256, 128, None, 1e-6, a, w, Y, 64, ws, 16, None) == L.SHARQ_ERR_INVALID_ARGUMENT
     assert f(X, 1, 8, 256, 256, None, 1e-6, a, w, Y, 32, ws, 16, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+
+
+def test_plain_baseline_validation_errors():
+    lib = L.lib()
+    X, Y, c, s = 0x50000, 0x30000, 0x60000, 0x70000
+    # rmsnorm: unknown dtype, K % 32, ldy < K, misaligned Y rows, NULL
+    assert lib.sharq_rmsnorm(X, 7, 8, 256, 256, None, 1e-6, Y, 256, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert lib.sharq_rmsnorm(X, 1, 8, 48, 48, None, 1e-6, Y, 48, None) == L.SHARQ_ERR_UNSUPPORTED_SHAPE
+    assert lib.sharq_rmsnorm(X, 1, 8, 256, 256, None, 1e-6, Y, 128, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert lib.sharq_rmsnorm(X, 1, 8, 256, 256, None, 1e-6, Y, 258, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert lib.sharq_rmsnorm(None, 1, 8, 256, 256, None, 1e-6, Y, 256, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert lib.sharq_rmsnorm(X, 1, 0, 256, 256, None, 1e-6, Y, 256, None) == L.SHARQ_ERR_UNSUPPORTED_SHAPE
+    # quantize: K % 32, ldy < K, misaligned outputs
+    assert lib.sharq_quantize_mx(Y, 8, 48, 48, c, s, None) == L.SHARQ_ERR_UNSUPPORTED_SHAPE
+    assert lib.sharq_quantize_mx(Y, 8, 256, 128, c, s, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert lib.sharq_quantize_mx(Y, 8, 256, 256, c + 8, s, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert lib.sharq_quantize_mx(Y, 8, 256, 256, None, s, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    # dense GEMM: K % 512, NVFP4 weight, grouped weight, ldy < D
+    f = lib.sharq_linear_dense
+    assert f(c, s, 8, _fake_weight(K=256), Y, 64, None) == L.SHARQ_ERR_UNSUPPORTED_SHAPE
+    assert "512" in lib.sharq_last_error().decode()
+    assert f(c, s, 8, _fake_weight(fmt=1, K=512), Y, 64, None) == L.SHARQ_ERR_FORMAT_MISMATCH
+    assert f(c, s, 8, _fake_weight(K=512, G=2), Y, 64, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert f(c, s, 8, _fake_weight(K=512), Y, 32, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert f(c, s, 0, _fake_weight(K=512), Y, 64, None) == L.SHARQ_ERR_UNSUPPORTED_SHAPE
+    assert f(None, s, 8, _fake_weight(K=512), Y, 64, None) == L.SHARQ_ERR_INVALID_ARGUMENT

@@ -9,8 +9,8 @@ import torch
 from oracle import sharq as O
 from sparsity_sharq_prepare_amd import ops, synth
 
-from gpu_util import (assert_gemm_close, compare_act, compare_weight, dev_gamma, dev_w, dev_x, run_case,
-                      sample_pairs)
+from gpu_util import (assert_bytes_equal, assert_gemm_close, compare_act, compare_weight, dev_gamma, dev_w, dev_x,
+                      run_case, sample_pairs)
 
 pytestmark = pytest.mark.gpu
 
@@ -476,3 +476,84 @@ def test_strided_input_and_output(T):
     assert torch.equal(Yw[:, :D], Y)
     assert bool(torch.all(Yw[:, D:] == -3.0))
     compare_act(act, oracle_prepare(case))
+
+
+# ------------------------------------------------------------------ plain baseline (unfused pipeline)
+BASE_SHAPES = [  # (T, K, dtype, gamma): the prepare geometries (64..1024 threads per row, 1..16 chunks)
+    (37, 256, "bf16", True), (5, 768, "bf16", False), (3, 32, "f32", True), (300, 4096, "bf16", True),
+    (4099, 2048, "bf16", True), (17, 14336, "bf16", True), (2100, 4096, "f32", True), (9, 18944, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("T,K,dtype,gamma", BASE_SHAPES)
+def test_plain_rmsnorm_quantize(T, K, dtype, gamma):
+    case = synth.random_case(7 * T + K, T, K, 8, dtype=dtype, gamma=gamma)
+    y = ops.rmsnorm(dev_x(case), dev_gamma(case.gamma), 1e-6)
+    codes, scales = ops.quantize_mx(y)
+    ref = O.plain_prepare_mx(case.x_f32(), case.gamma)
+    torch.cuda.synchronize()
+    assert_bytes_equal("y bits", y.cpu().numpy().view(np.uint32), ref["y"].view(np.uint32))
+    assert_bytes_equal("codes", codes.cpu().numpy(), ref["codes"])
+    assert_bytes_equal("scales", scales.cpu().numpy(), ref["scales"])
+
+
+def test_plain_quantize_edge_values_and_strided_rows():
+    rng = np.random.default_rng(11)
+    K = 128
+    y = np.zeros((6, K), np.float32)
+    y[0, 1::2] = -0.0                                          # signed zeros, all-zero blocks
+    y[1] = rng.standard_normal(K).astype(np.float32) * np.float32(1e-40)   # subnormal blocks
+    mags = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)   # E2M1 ties
+    y[2] = mags[rng.integers(0, 7, K)] * np.where(rng.random(K) < 0.5, -1, 1).astype(np.float32)
+    y[2, 0::32] = 6.0
+    y[3] = rng.standard_normal(K).astype(np.float32) * np.float32(3e37)    # near the top of fp32
+    y[4] = np.float32(1.0)
+    y[4, 7] = np.float32(6.0000005)                            # amax just above 6: next scale
+    y[5] = rng.standard_normal(K).astype(np.float32)
+    wide = torch.zeros((6, K + 36), dtype=torch.float32, device="cuda")
+    wide[:, :K] = torch.from_numpy(y).cuda()
+    codes, scales = ops.quantize_mx(wide[:, :K])               # ldy = K + 36
+    c, e = O.mx_quantize(y)
+    torch.cuda.synchronize()
+    assert_bytes_equal("codes", codes.cpu().numpy(), O.pack_nibbles(c))
+    from oracle import formats as F
+    assert_bytes_equal("scales", scales.cpu().numpy(), F.e8m0_encode_exponent(e))
+
+
+DENSE_SHAPES = [  # (T, K, D): one and many row tiles, ragged rows and columns, both tile widths
+    (1, 512, 200), (70, 512, 1), (300, 1024, 520), (257, 1536, 250), (4000, 512, 3000), (512, 2048, 4096),
+]
+
+
+@pytest.mark.parametrize("T,K,D", DENSE_SHAPES)
+def test_plain_linear_dense(T, K, D):
+    case = synth.random_case(T + 5 * K + D, T, K, D)
+    y = ops.rmsnorm(dev_x(case), dev_gamma(case.gamma), 1e-6)
+    codes, scales = ops.quantize_mx(y)
+    w = ops.pack_weight(dev_w(case.w, "bf16"))
+    Y = ops.linear_dense(codes, scales, w)
+    ref = O.plain_prepare_mx(case.x_f32(), case.gamma)
+    Yr, S = O.plain_linear_mx(ref["codes"], ref["scales"], O.pack_weight(case.w_f32()))
+    assert_gemm_close(Y.cpu().numpy(), Yr, S)
+
+
+def test_plain_linear_dense_prefill_sampled():
+    case = synth.prefill_case()
+    y = ops.rmsnorm(dev_x(case), dev_gamma(case.gamma), 1e-6)
+    codes, scales = ops.quantize_mx(y)
+    w = ops.pack_weight(dev_w(case.w, "bf16"))
+    Y = ops.linear_dense(codes, scales, w)
+    Y2 = ops.linear_dense(codes, scales, w)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2)
+    ref_c, ref_s = codes.cpu().numpy(), scales.cpu().numpy()
+    r, c = sample_pairs(case.T, case.D, 2000, seed=3)
+    # the codes themselves are checked against the oracle on the sampled rows
+    rows = np.unique(r)
+    refp = O.plain_prepare_mx(case.x_f32()[rows], case.gamma)
+    assert_bytes_equal("codes", ref_c[rows], refp["codes"])
+    assert_bytes_equal("scales", ref_s[rows], refp["scales"])
+    cols = np.unique(c)
+    wref = O.pack_weight(case.w_f32()[:, cols])
+    Yr, S = O.plain_linear_mx_sampled(ref_c, ref_s, wref, r, np.searchsorted(cols, c))
+    assert_gemm_close(Y.cpu().numpy()[r, c], Yr, S)

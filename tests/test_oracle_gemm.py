@@ -131,3 +131,54 @@ def test_sharq_beats_plain_fp4_on_outliers(fmt):
     Y, _ = O.sharq_linear(act, wp)
     plain = O.plain_quantized(act["y"], fmt) @ W
     assert O.rel_frobenius(Y, ref) < 0.5 * O.rel_frobenius(plain, ref)
+
+
+# ------------------------------------------------------------ plain baseline
+def test_plain_pipeline_worked_example():
+    g = {r[0]: r[1:] for r in read_golden("worked_example_block.txt")}
+    x = np.full((1, 32), F32(0.2), dtype=F32)
+    x[0, 5] = 12.0
+    p = O.plain_prepare_mx(x, None)
+    assert np.array_equal(p["y"], x)
+    assert p["codes"][0].tolist() == [int(b, 16) for b in g["plain_codes"]]
+    assert p["scales"][0].tolist() == [int(b, 16) for b in g["plain_scale"]]
+    ones = O.pack_weight(np.ones((32, 1), F32), "mxfp4")
+    Y, S = O.plain_linear_mx(p["codes"], p["scales"], ones)
+    assert Y[0, 0] == float(g["plain_y_ones"][0]) and S[0, 0] == 12.0
+    alt = O.pack_weight(np.array([[(-1.0) ** k] for k in range(32)], F32), "mxfp4")
+    Y2, _ = O.plain_linear_mx(p["codes"], p["scales"], alt)
+    assert Y2[0, 0] == float(g["plain_y_alt"][0])
+    # the dual path keeps what the plain path loses (same block, same weights)
+    Yd, _ = O.sharq_linear(worked_example_act(), ones)
+    assert Yd[0, 0] == float(g["y_ones"][0]) > Y[0, 0]
+
+
+def test_plain_permutation_weight_and_grid_values():
+    # W = 2 x permutation -> W~ = W exactly, Y[:, pi(k)] = 2 x~[:, k]
+    case = synth.random_case(31, 5, 512, 512)
+    p = O.plain_prepare_mx(case.x_f32(), case.gamma)
+    pi = np.random.default_rng(4).permutation(512)
+    W = np.zeros((512, 512), F32)
+    W[np.arange(512), pi] = 2.0
+    Y, _ = O.plain_linear_mx(p["codes"], p["scales"], O.pack_weight(W, "mxfp4"))
+    Xt = O.mx_dequant_f64(O.unpack_nibbles(p["codes"]), F.e8m0_decode_exponent(p["scales"]))
+    assert np.array_equal(Y[:, pi], 2.0 * Xt)
+    # values already on the FP4 grid of their block scale come back exactly
+    rng = np.random.default_rng(5)
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], F32)
+    v = mags[rng.integers(0, 8, (3, 64))] * np.where(rng.random((3, 64)) < 0.5, -1, 1).astype(F32)
+    v[:, 0::32] = 6.0                               # every block reaches 6 -> scale 2^0
+    v = v * F32(0.25)                               # ... then 2^-2, exactly
+    q = O.plain_prepare_mx(v, None)
+    back = O.mx_dequant_f64(O.unpack_nibbles(q["codes"]), F.e8m0_decode_exponent(q["scales"]))
+    assert np.array_equal(back, v.astype(np.float64))
+    assert np.all(q["scales"] == 125)
+
+
+def test_plain_zero_rows_and_rmsnorm_consistency():
+    z = np.zeros((2, 64), F32)
+    q = O.plain_prepare_mx(z, np.ones(64, F32))
+    assert np.all(q["codes"] == 0) and np.all(q["scales"] == 0)   # e = -127
+    case = synth.random_case(7, 9, 256, 8)
+    assert np.array_equal(O.plain_prepare_mx(case.x_f32(), case.gamma)["y"],
+                          O.prepare(case.x_f32(), case.gamma, 1e-6)["y"])
