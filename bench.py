@@ -73,7 +73,7 @@ class Job:
         self.fused = fmt == "mxfp4" and self.groups == 1 and rows is None and T <= 8
         self.step_fused = False          # the step uses it when it is the faster form
 
-    # algorithmic work (SURVEY-defined units)
+    # algorithmic work of one launch
     def gemm_flops_nominal(self):
         return 2.0 * self.rows * self.K * self.D
 
@@ -268,6 +268,60 @@ def kernel_times(jobs, R, reps=3):
     return prep_ms, gemm_ms, fused_ms
 
 
+def plain_breakdown(jobs, prep_ms, gemm_ms, R, reps=3):
+    """MI355X analogue of the pages' prefill kernel-latency breakdown (xllm-io
+    paper review §5): the unfused plain MXFP4 pipeline (RMSNorm kernel,
+    quantize kernel, dense one-operand MXFP4 GEMM) against SharQ's fused
+    prepare and dual-path GEMM on the same inputs and weights.  Each kernel is
+    timed like kernel_times: R back-to-back launches in a HIP graph."""
+    import torch
+    from sparsity_sharq_prepare_amd import ops
+    out = {}
+    for job, pm, gm in zip(jobs, prep_ms, gemm_ms):
+        T, K = job.X.shape
+        y = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        codes = torch.empty((T, K // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((T, K // 32), dtype=torch.uint8, device="cuda")
+        Yd = torch.empty((T, job.D), dtype=torch.float32, device="cuda")
+        ops.rmsnorm(job.Xs[0], job.gamma, 1e-6, out=y)
+        ops.quantize_mx(y, codes, scales)
+        torch.cuda.synchronize()
+        graphs = []
+        for kind in ("rmsnorm", "quantize", "dense"):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(R):
+                    if kind == "rmsnorm":
+                        ops.rmsnorm(job.Xs[i % len(job.Xs)], job.gamma, 1e-6, out=y)
+                    elif kind == "quantize":
+                        ops.quantize_mx(y, codes, scales)
+                    else:
+                        ops.linear_dense(codes, scales, job.weights[i % len(job.weights)], out=Yd)
+            graphs.append(g)
+        res = []
+        for g in graphs:
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            res.append(e0.elapsed_time(e1) / (reps * R) * 1e3)
+        rms, qnt, dense = res
+        sp, sg = pm * 1e3, gm * 1e3
+        out[job.name] = {
+            "plain": {"rmsnorm_us": round(rms, 2), "quantize_us": round(qnt, 2), "dense_gemm_us": round(dense, 2),
+                      "total_us": round(rms + qnt + dense, 2)},
+            "sharq": {"prepare_us": round(sp, 2), "dual_gemm_us": round(sg, 2), "total_us": round(sp + sg, 2)},
+            "prepare_over_rmsnorm_plus_quantize": round(sp / (rms + qnt), 3),
+            "dual_over_dense_gemm": round(sg / dense, 3),
+            "sharq_over_plain_total": round((sp + sg) / (rms + qnt + dense), 3),
+        }
+    return out
+
+
 # ----------------------------------------------------------------------------
 # CPU oracle baseline
 # ----------------------------------------------------------------------------
@@ -451,6 +505,8 @@ def main():
         "kernels": kernels,
         "pack_us": round(pack_us, 1),
     }
+    if args.workload == "prefill":
+        out["breakdown"] = plain_breakdown(jobs, prep_ms, gemm_ms, len(jobs[0].weights))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cases, args.workload, args.cpu_seconds)
         if args.workload != "moe":

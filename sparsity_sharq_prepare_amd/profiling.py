@@ -49,6 +49,10 @@ MATCH = {
     "linear_nv_tile": ("linear_nv_tile",),
     "prepare_mx_kernel": ("prepare_mx_kernel",),
 }
+# ... and none of these: the plain baseline's dense tile (template flag true)
+EXCLUDE = {
+    "linear_mx_tile": ("linear_mx_tile8<8, 224, true>", "linear_mx_tile8<8, 256, true>"),
+}
 
 
 def source_hash(files) -> str:
@@ -79,7 +83,8 @@ def kernel_bytes(path: str, counter: str, kernel: str, copy_bytes: int):
     if not copies:
         raise SystemExit(f"{path}: no copyBuffer dispatch for the calibration")
     factor = copy_bytes / (max(copies) * 1024.0)
-    ks = [v for n, v in disp.values() if all(m in n for m in MATCH[kernel])]
+    ks = [v for n, v in disp.values()
+          if all(m in n for m in MATCH[kernel]) and not any(x in n for x in EXCLUDE.get(kernel, ()))]
     if not ks:
         raise SystemExit(f"{path}: no dispatch of {kernel}")
     return sum(ks) / len(ks) * 1024.0 * factor, factor, len(ks)
