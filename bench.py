@@ -396,26 +396,56 @@ def read_traffic(name, sources):
         return None
 
 
-def oracle_errors(cases, y_gpu, workload):
+def gpu_error_outputs(jobs, rows):
+    """GPU outputs on the first ``rows`` rows of each linear for the error
+    report: the plain MXFP4 pipeline (RMSNorm, quantize, dense GEMM; K % 512
+    == 0) and the sparse backbone alone (the dual GEMM with the residual codes
+    zeroed).  MXFP4 linears only."""
+    from sparsity_sharq_prepare_amd import ops
+    out = []
+    for j, r in zip(jobs, rows):
+        e = {}
+        if j.fmt == "mxfp4" and j.groups == 1:
+            X = j.X[:r]
+            if j.K % 512 == 0:
+                y = ops.rmsnorm(X, j.gamma, 1e-6)
+                codes, scales = ops.quantize_mx(y)
+                e["plain"] = ops.linear_dense(codes, scales, j.weights[0])
+            act = ops.prepare(X, j.gamma, 1e-6, "mxfp4")
+            act.res_codes.zero_()
+            e["sparse_only"] = ops.linear(act, j.weights[0])
+        out.append({k: v.float().cpu().numpy() for k, v in e.items()})
+    return out
+
+
+def oracle_errors(cases, y_gpu, extra_gpu, workload):
     """Relative Frobenius error against the unquantized product y W (fp64),
-    y = RMSNorm(x), for the GPU's SharQ output and for plain FP4 of the same
-    activations and packed weights (oracle), on the rows the CPU baseline
-    samples: all rows at decode, the first 64 otherwise (MoE: not reported)."""
+    y = RMSNorm(x), on the rows the CPU baseline samples (all rows at decode,
+    the first 64 otherwise; MoE: not reported):
+    - the GPU's SharQ output, and GPU plain MXFP4 / sparse-only outputs;
+    - the oracle's operator-level analogue of the review's Table 5
+      (sparse only, sparse + sparse, dense + dense, SharQ, plain FP4) with
+      the packed FP4 weights, and with unquantized weights
+      (activation error alone)."""
     import numpy as np
     from oracle import sharq as O
     if workload == "moe":
         return None
     out = {}
-    for c, Yg in zip(cases, y_gpu):
+    for c, Yg, ex in zip(cases, y_gpu, extra_gpu):
         rows = Yg.shape[0]
-        prep = O.prepare(c.x_f32()[:rows], c.gamma, 1e-6, c.fmt)
-        y = prep["y"].astype(np.float64)
-        W = c.w_f32().astype(np.float64)
-        ref = y @ W
+        x = c.x_f32()[:rows]
+        prep = O.prepare(x, c.gamma, 1e-6, c.fmt)
+        ref = prep["y"].astype(np.float64) @ c.w_f32().astype(np.float64)
         wp = O.pack_weight(c.w_f32(), c.fmt)
-        plain = O.plain_quantized(prep["y"], c.fmt) @ O.weight_dequant(wp, "dn")
-        out[c.name] = {"rows": rows, "sharq": round(O.rel_frobenius(Yg.astype(np.float64), ref), 6),
-                       f"plain_{c.fmt}": round(O.rel_frobenius(plain, ref), 6)}
+        st = O.decomposition_study(x, c.gamma, c.w_f32(), c.fmt, wp=wp)
+        e = {"rows": rows, "sharq": round(O.rel_frobenius(Yg.astype(np.float64), ref), 6),
+             f"plain_{c.fmt}": round(st["weights_fp4"]["plain"], 6)}
+        for k, v in ex.items():
+            e[f"{k}_gpu"] = round(O.rel_frobenius(v.astype(np.float64), ref), 6)
+        e["table5"] = {k: round(v, 6) for k, v in st["weights_fp4"].items()}
+        e["table5_activation_only"] = {k: round(v, 6) for k, v in st["activation_only"].items()}
+        out[c.name] = e
     return out
 
 
@@ -510,8 +540,9 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cases, args.workload, args.cpu_seconds)
         if args.workload != "moe":
-            y_gpu = [j.Y[: (j.rows if args.workload == "decode" else 64)].float().cpu().numpy() for j in jobs]
-            out["errors"] = oracle_errors(cases, y_gpu, args.workload)
+            rows = [j.rows if args.workload == "decode" else 64 for j in jobs]
+            y_gpu = [j.Y[:r].float().cpu().numpy() for j, r in zip(jobs, rows)]
+            out["errors"] = oracle_errors(cases, y_gpu, gpu_error_outputs(jobs, rows), args.workload)
     print(json.dumps(out))
 
 

@@ -469,6 +469,72 @@ def plain_linear_mx_sampled(codes: np.ndarray, scales: np.ndarray, wp: dict, out
     return Y, S
 
 
+def _sparse_quantized(v: np.ndarray, fmt: str, f64: bool = False) -> np.ndarray:
+    """4:8 in-pairs sparsification of ``v`` (the pair-top-2 rule of
+    ``pair_top2``) and backbone-style quantization of the kept values
+    (MXFP4 per 32; NVFP4 E4M3 per 32 logical positions under the tensor scale
+    of amax(v)), dequantized (fp32 as the preparation rounds it, or the exact
+    fp64 value the GEMM multiplies) with zeros at dropped positions."""
+    i0, i1 = pair_top2(v)
+    M = mask_from_pairs(i0, i1)
+    vs = np.where(M, v, F32(0.0))
+    if fmt == "mxfp4":
+        c, e = mx_quantize(vs)
+        q = mx_dequant_f64(c, e) if f64 else mx_dequant_f32(c, e)
+    else:
+        s = nv_tensor_scale(np.abs(v).max() if v.size else 0.0)
+        c, sc = nv_quantize(vs, NV_BB_BLOCK, s)
+        q = nv_dequant_f64(c, sc, NV_BB_BLOCK, s) if f64 else nv_dequant_f32(c, sc, NV_BB_BLOCK, s)
+    return np.where(M, q, 0.0)
+
+
+def _dense_quantized(v: np.ndarray, fmt: str, f64: bool = False) -> np.ndarray:
+    """Dense quantization of ``v`` as the residual path does it (MXFP4 per 32;
+    NVFP4 E4M3 per 16 under the tensor scale of amax(v)), dequantized in fp32
+    or exactly in fp64."""
+    if fmt == "mxfp4":
+        c, e = mx_quantize(v)
+        return mx_dequant_f64(c, e) if f64 else mx_dequant_f32(c, e)
+    s = nv_tensor_scale(np.abs(v).max() if v.size else 0.0)
+    c, sc = nv_quantize(v, NV_RES_BLOCK, s)
+    return nv_dequant_f64(c, sc, NV_RES_BLOCK, s) if f64 else nv_dequant_f32(c, sc, NV_RES_BLOCK, s)
+
+
+def decomposition_study(x: np.ndarray, gamma, w: np.ndarray, fmt: str = "mxfp4", eps: float = 1e-6,
+                        wp: dict = None) -> dict:
+    """Operator-level analogue of the review's Table 5 (sparse / dense path
+    combinations): relative Frobenius error against the unquantized y W
+    (fp64) of X^ W~ (packed FP4 weights, "weights_fp4") and of X^ W
+    ("activation_only") for the activation approximations
+      sparse_only   X~_sp                    (the residual dropped)
+      sparse_sparse X~_sp + Q_sp(M'(R) ⊙ R)  (the residual also 4:8-sparse)
+      dense_dense   Q(y) + Q(y - Q(y))       (both paths dense)
+      sharq         X~_sp + Q_dn(R)          (sparse backbone, dense residual)
+      plain         Q(y)                     (one dense FP4 path)
+    where y = RMSNorm(x), X~_sp and R are those of ``prepare``, W~ is the
+    packed weight, M' is the pair-top-2 mask chosen on R, and each residual
+    is taken against the quantized first path (review §3.3).  Every
+    residual here is exact in fp32 (Sterbenz, as for R).  ``wp``: W already
+    packed (``pack_weight(w, fmt)``), to skip packing it again."""
+    prep = prepare(x, gamma, eps, fmt)
+    y = prep["y"]
+    W = weight_dequant(wp if wp is not None else pack_weight(w, fmt), "dn")
+    ref = y.astype(np.float64) @ np.asarray(w, dtype=np.float64)
+    Xt_sp = _sparse_quantized(y, fmt, f64=True)        # exact values of the backbone
+    R = prep["R"]
+    q1 = _dense_quantized(y, fmt)                       # fp32, the residual's reference
+    approx = {
+        "sparse_only": Xt_sp,
+        "sparse_sparse": Xt_sp + _sparse_quantized(R, fmt, f64=True),
+        "dense_dense": _dense_quantized(y, fmt, f64=True) + _dense_quantized(y - q1, fmt, f64=True),
+        "sharq": Xt_sp + _dense_quantized(R, fmt, f64=True),
+        "plain": plain_quantized(y, fmt),
+    }
+    Wf = np.asarray(w, dtype=np.float64)
+    return {"weights_fp4": {k: rel_frobenius(v @ W, ref) for k, v in approx.items()},
+            "activation_only": {k: rel_frobenius(v @ Wf, ref) for k, v in approx.items()}}
+
+
 def rel_frobenius(Y_hat: np.ndarray, Y_ref: np.ndarray) -> float:
     return float(np.linalg.norm(Y_hat - Y_ref) / np.linalg.norm(Y_ref))
 

@@ -182,3 +182,58 @@ def test_plain_zero_rows_and_rmsnorm_consistency():
     case = synth.random_case(7, 9, 256, 8)
     assert np.array_equal(O.plain_prepare_mx(case.x_f32(), case.gamma)["y"],
                           O.prepare(case.x_f32(), case.gamma, 1e-6)["y"])
+
+
+# ------------------------------------------------------------ Table-5 analogue
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_study_pieces_are_the_prepare_steps(fmt):
+    case = synth.random_case(21, 6, 512, 8, fmt=fmt)
+    prep = O.prepare(case.x_f32(), case.gamma, 1e-6, fmt)
+    # the sparse quantizer applied to y is the backbone of the preparation
+    assert np.array_equal(O._sparse_quantized(prep["y"], fmt).view(np.uint32), prep["Xt_sp"].view(np.uint32))
+    # a dense residual against a dense first path is exact in fp32 (Sterbenz)
+    y = prep["y"]
+    q1 = O._dense_quantized(y, fmt)
+    assert np.array_equal(q1 + (y - q1), y)
+    # the exact values are the dual GEMM's operands (act_dequant)
+    Xt, Rt = O.act_dequant(prep)
+    assert np.array_equal(O._sparse_quantized(prep["y"], fmt, f64=True), Xt)
+    assert np.array_equal(O._dense_quantized(prep["R"], fmt, f64=True), Rt)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_study_ordering(fmt, seed):
+    # the review's Table 5 ordering (qualitative; the pages give perplexities,
+    # not operator errors): sparse only fails, the sparse residual is worse
+    # than the dense one, SharQ is close to dense + dense and far below plain FP4
+    spec = synth.LLAMA_OUTLIERS if fmt == "mxfp4" else synth.QWEN_OUTLIERS
+    case = synth.random_case(seed, 16, 1024, 64, fmt=fmt, spec=spec)
+    r = O.decomposition_study(case.x_f32(), case.gamma, case.w_f32(), fmt)
+    a, w = r["activation_only"], r["weights_fp4"]
+    assert a["dense_dense"] < a["sharq"] < a["sparse_sparse"] < a["plain"] < a["sparse_only"]
+    # with FP4 weights their error dominates: SharQ and dense + dense agree
+    # to within noise (either may be lower), the rest keeps its order
+    assert abs(w["sharq"] - w["dense_dense"]) <= 0.02 * w["dense_dense"]
+    assert w["sharq"] < w["sparse_sparse"] < w["plain"] < w["sparse_only"]
+    assert a["sharq"] < 0.5 * a["plain"]
+
+
+def test_study_grid_input_has_no_residual():
+    # y on the FP4 grid inside the mask and 0 outside: R = 0, so SharQ, the
+    # sparse-only and the sparse + sparse forms coincide and are exact
+    rng = np.random.default_rng(3)
+    mags = np.array([0.5, 1, 1.5, 2, 3, 4, 6], F32)
+    x = np.zeros((4, 64), F32)
+    for t in range(4):
+        for g in range(8):
+            # two nonzero pairs per group; groups 0 and 4 keep pair 0, which
+            # holds its 32-block's max 6 (scale 2^0, so every value is on the grid)
+            pairs = [0, 1 + rng.integers(0, 3)] if g % 4 == 0 else rng.choice(4, 2, replace=False)
+            for p in pairs:
+                x[t, 8 * g + 2 * p: 8 * g + 2 * p + 2] = mags[rng.integers(0, 7, 2)]
+            if g % 4 == 0:
+                x[t, 8 * g] = 6.0
+    w = (np.random.default_rng(4).standard_normal((64, 8)) * 0.02).astype(F32)
+    r = O.decomposition_study(x, None, w, "mxfp4")["activation_only"]
+    assert r["sharq"] == r["sparse_only"] == r["sparse_sparse"] == 0.0
