@@ -238,9 +238,13 @@ __global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
   constexpr uint32_t kOut = 0x80000000u;             // offset past every buffer here: reads zero
   constexpr int NT = NW * 64;
   const int KB = K >> 5, KS = K >> 7;
+  // scale rows: MFMA row r (0-7 backbone, 8-15 residual of token r & 7) at
+  // s_sm + r * KBP; KBP / 4 odd, so the 16 rows of one step's reads fall on
+  // distinct banks; a spare 16-byte slot follows them
+  const int KBP = ((KB + 15) & ~15) + 4;
   uint4* const a_sm = dsm;                                            // [KB + 1][16]
-  uint8_t* const s_sm = reinterpret_cast<uint8_t*>(dsm + (KB + 1) * 16);   // [KB + 1][16]
-  float* const red = reinterpret_cast<float*>(dsm + (KB + 1) * 17);   // [NW][64][4]
+  uint8_t* const s_sm = reinterpret_cast<uint8_t*>(dsm + (KB + 1) * 16);   // [16][KBP] + 16
+  float* const red = reinterpret_cast<float*>(dsm + (KB + 1) * 16 + (16 * KBP + 16) / 16);   // [NW][64][4]
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   auto rsrc = [](const uint8_t* base, int64_t bytes) {
@@ -263,19 +267,30 @@ __global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- activation loads (L2 hits): item i is block i >> 3 of token i & 7; a
-  // thread always serves token tid & 7 and at most IPT = J / (2 CG) items
-  // (NK J >= K / 128 gives 8 K / 32 <= 64 NW IPT).  Issued before the weight
-  // loads (the LDS writes then wait only for them), except when fused: there
-  // the activations exist only once the producers are done.
+  // ---- activation loads (L2 hits), as coalesced 16-byte pieces of the
+  // token rows: residual piece i = block i % KB of token i / KB; backbone
+  // piece i = blocks 2 (i % (KB / 2)) and + 1 of token i / (KB / 2), with
+  // its 4 metadata bytes; scale piece i = 16 scale bytes of one row (backbone
+  // rows first).  Wide loads keep the address unit's work per byte low (one
+  // load per 16 bytes instead of five loads per 32-value block).  Pieces past
+  // the end (and of absent tokens) read zeros and land in spare LDS slots.
+  // Issued before the weight loads (the LDS writes then wait only for them),
+  // except when fused: there the activations exist only once the producers
+  // are done.  NK J >= K / 128 gives 8 KB <= NT IPT.
   constexpr int IPT = (J / (2 * CG)) > 0 ? J / (2 * CG) : 1;
-  const int t = tid & 7;
-  const bool t_ok = t < rows;
-  const uint32_t ar = t_ok ? (uint32_t)gather_row(row_index, t, act_rows) : 0u;
-  const int n_item = 8 * KB;
-  uint4 sv[IPT];
-  uint2 sc[IPT];
-  uint32_t srs[IPT], sm[IPT], sbs[IPT];
+  constexpr int BPT = (IPT + 1) / 2;                  // backbone pieces per thread
+  const int KBh = KB >> 1, KB16 = (KB + 15) >> 4;
+  const int n_res = 8 * KB, n_bb = 8 * KBh, n_sc = 16 * KB16;
+  // piece index -> row by a float reciprocal instead of an integer division:
+  // (i + 1/2) / n is at least 1 / (2 n) >= 2^-11 away from an integer, far
+  // beyond the rounding of these small operands
+  const float rKB = 1.0f / (float)KB, rKBh = 1.0f / (float)KBh, rKB16 = 1.0f / (float)KB16;
+  auto qdiv = [](int i, float r) { return (int)(((float)i + 0.5f) * r); };
+  auto act_row = [&](int t) -> uint32_t {
+    return t < rows ? (uint32_t)gather_row(row_index, t, act_rows) : 0u;
+  };
+  uint4 rv[IPT], bv[BPT], sv[2];
+  uint32_t mv[BPT];
   auto load_act = [&]() {
     const int an = __builtin_amdgcn_readfirstlane(act_rows);
     const __amdgpu_buffer_rsrc_t r_rc = rsrc(res_codes, (int64_t)an * (K >> 1));
@@ -285,15 +300,29 @@ __global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
     const __amdgpu_buffer_rsrc_t r_bs = rsrc(bb_scale, (int64_t)an * (K >> 5));
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
-      const int i = tid + NT * j, kb = i >> 3;
-      const uint32_t out = i < n_item && t_ok ? 0u : kOut;
-      const auto cr = __builtin_amdgcn_raw_buffer_load_b128(r_rc, (ar * (uint32_t)(K >> 1) + 16u * kb) | out, 0, 0);
-      sv[j] = make_uint4(cr[0], cr[1], cr[2], cr[3]);
-      srs[j] = __builtin_amdgcn_raw_buffer_load_b8(r_rs, (ar * (uint32_t)(K >> 5) + kb) | out, 0, 0);
-      const auto cb = __builtin_amdgcn_raw_buffer_load_b64(r_bc, (ar * (uint32_t)(K >> 2) + 8u * kb) | out, 0, 0);
-      sc[j] = make_uint2(cb[0], cb[1]);
-      sm[j] = __builtin_amdgcn_raw_buffer_load_b16(r_bm, (ar * (uint32_t)(K >> 4) + 2u * kb) | out, 0, 0);
-      sbs[j] = __builtin_amdgcn_raw_buffer_load_b8(r_bs, (ar * (uint32_t)(K >> 5) + kb) | out, 0, 0);
+      const int i = tid + NT * j, t = qdiv(i, rKB), kb = i - t * KB;
+      const uint32_t off = i < n_res && t < rows ? act_row(t) * (uint32_t)(K >> 1) + 16u * kb : kOut;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(r_rc, off, 0, 0);
+      rv[j] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      const int i = tid + NT * j, t = qdiv(i, rKBh), kp = i - t * KBh;
+      const bool ok = i < n_bb && t < rows;
+      const uint32_t ar = ok ? act_row(t) : 0u;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(r_bc, ok ? ar * (uint32_t)(K >> 2) + 16u * kp : kOut, 0, 0);
+      bv[j] = make_uint4(v[0], v[1], v[2], v[3]);
+      mv[j] = __builtin_amdgcn_raw_buffer_load_b32(r_bm, ok ? ar * (uint32_t)(K >> 4) + 4u * kp : kOut, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = tid + NT * j, r = qdiv(i, rKB16), p = i - r * KB16, t = r & 7;
+      const bool ok = i < n_sc && t < rows;
+      // bytes past a row's K / 32 belong to the next row (or read zero past
+      // the buffer); they land in the row's padding
+      const uint32_t off = ok ? act_row(t) * (uint32_t)(K >> 5) + 16u * p : kOut;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(r < 8 ? r_bs : r_rs, off, 0, 0);
+      sv[j] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   };
   if (!FUSED) load_act();
@@ -356,16 +385,30 @@ __global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
   }
 
   // ---- activation operand into LDS (waits only for the activation loads,
-  // which were issued first)
-  // (unconditional: items past the end go to the spare block row KB, so no
-  // load is sunk behind the weight loads into a conditional block)
+  // which were issued first): residual blocks as they are, backbone blocks
+  // expanded to operand form, scale rows as they are.  Pieces past the end
+  // write the spare block row KB or the spare scale slot, so no load is sunk
+  // behind the weight loads into a conditional block.
 #pragma unroll
   for (int j = 0; j < IPT; ++j) {
-    const int i = tid + NT * j, kb = i < n_item ? i >> 3 : KB;
-    a_sm[16 * kb + 8 + t] = sv[j];
-    s_sm[16 * kb + 8 + t] = (uint8_t)srs[j];
-    a_sm[16 * kb + t] = expand4_fast(sc[j].x, sc[j].y, sm[j]);
-    s_sm[16 * kb + t] = (uint8_t)sbs[j];
+    const int i = tid + NT * j, t = qdiv(i, rKB), kb = i - t * KB;
+    a_sm[i < n_res ? 16 * kb + 8 + t : 16 * KB] = rv[j];
+  }
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    const int i = tid + NT * j, t = qdiv(i, rKBh), kp = i - t * KBh;
+    const bool ok = i < n_bb;
+    a_sm[ok ? 16 * (2 * kp) + t : 16 * KB + 1] = expand4_fast(bv[j].x, bv[j].y, mv[j] & 0xFFFFu);
+    a_sm[ok ? 16 * (2 * kp + 1) + t : 16 * KB + 2] = expand4_fast(bv[j].z, bv[j].w, mv[j] >> 16);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = tid + NT * j, r = qdiv(i, rKB16), p = i - r * KB16;
+    // row r of the scale table: backbone token r (r < 8) is MFMA row r,
+    // residual token r - 8 is MFMA row r as well
+    // (4-byte stores: KBP is a multiple of 4, not of 16)
+    uint32_t* dst = reinterpret_cast<uint32_t*>(s_sm + (i < n_sc ? r * KBP + 16 * p : 16 * KBP));
+    dst[0] = sv[j].x; dst[1] = sv[j].y; dst[2] = sv[j].z; dst[3] = sv[j].w;
   }
   __syncthreads();
 
@@ -375,7 +418,7 @@ __global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
   for (int j = 0; j < J; ++j) {
     const int s = s0 + j < KS ? s0 + j : KS - 1;
     const int e = 64 * s + l;                        // = 16 (4 s + kq) + (l & 15)
-    acc = mfma_fp4(a_sm[e], wv[j], acc, s_sm[e], (wsd[j] >> (8 * kq)) & 0xFFu);
+    acc = mfma_fp4(a_sm[e], wv[j], acc, s_sm[(l & 15) * KBP + 4 * s + kq], (wsd[j] >> (8 * kq)) & 0xFFu);
   }
 
   // ---- fixed-order reduction over the waves; backbone row + residual row
@@ -1037,7 +1080,9 @@ hipError_t launch_decode(const uint8_t* bb_codes, const uint8_t* bb_meta, const 
   while (NK * J < KS) NK *= 2;
   int CG = 1;
   while (NK * CG * 2 <= 16 && (D + 16 * CG * 2 - 1) / (16 * CG * 2) >= 200) CG *= 2;
-  const size_t lds = (size_t)(K / 32 + 1) * 17 * 16 + (size_t)NK * CG * 64 * 4 * sizeof(float);
+  const int KBP = ((K / 32 + 15) & ~15) + 4;           // as in the kernel
+  const size_t lds = (size_t)(K / 32 + 1) * 16 * 16 + (size_t)(16 * KBP + 16) / 16 * 16 +
+                     (size_t)NK * CG * 64 * 4 * sizeof(float);
   const int n_gemm = (D + 16 * CG - 1) / (16 * CG);
   // fused: the producers are workgroups 0, 8, .., 8 (rows - 1)
   dim3 grid(FUSED ? std::max(n_gemm, 8 * (rows - 1) + 1) : n_gemm), block(64 * NK * CG);
