@@ -72,7 +72,14 @@ typedef enum {
   SHARQ_ERR_HIP = 5                 /* a HIP runtime call or kernel launch failed */
 } sharq_status;
 
-typedef enum { SHARQ_MXFP4 = 0, SHARQ_NVFP4_EMU = 1 } sharq_format;
+/* SHARQ_MXFP4_24: MXFP4 activations whose backbone uses the 2:4 element-wise
+ * mask (review §3.2 general N:M mask; the pattern the pages pair with MXFP4)
+ * instead of 4:8 in pairs: per group of 4 K-values the 2 largest |y| are
+ * kept (ties to the lower index); bb_codes holds one byte per group of 4 (the
+ * kept codes, lower index in the low nibble), bb_meta one nibble per group
+ * of 4 (i0 | i1 << 2, even group in the low nibble: T x K/8 bytes).  An
+ * activation format only: it multiplies SHARQ_MXFP4 weights. */
+typedef enum { SHARQ_MXFP4 = 0, SHARQ_NVFP4_EMU = 1, SHARQ_MXFP4_24 = 2 } sharq_format;
 typedef enum { SHARQ_F32 = 0, SHARQ_BF16 = 1 } sharq_dtype;
 
 /* Packed weight: n_groups stacked matrices (n_groups experts; 1 for a plain
@@ -102,7 +109,7 @@ typedef struct {
   int32_t fmt;           /* sharq_format */
   int32_t T, K;
   uint8_t *bb_codes;     /* (device) T x K/4                                   */
-  uint8_t *bb_meta;      /* (device) T x K/16                                  */
+  uint8_t *bb_meta;      /* (device) T x K/16 (2:4: T x K/8)                    */
   uint8_t *bb_scale;     /* (device) T x K/32                                  */
   uint8_t *res_codes;    /* (device) T x K/2                                   */
   uint8_t *res_scale;    /* (device) T x K/32 (MXFP4) | T x K/16 (NVFP4)       */

@@ -133,6 +133,50 @@ def mask_from_pairs(i0: np.ndarray, i1: np.ndarray) -> np.ndarray:
     return np.repeat(keep, 2, axis=-1).reshape(T, G * 8)
 
 
+def nm_keep(y: np.ndarray, N: int, M: int, unit: int = 1) -> np.ndarray:
+    """Element mask of the general N:M rule (review §3.2, input-adaptive N:M
+    mask; explainer, 4:8 in-pairs section): each group of M contiguous values
+    is cut into M / unit units of ``unit`` contiguous values, a unit scores
+    the max |y| of its values, and the N / unit highest-scoring units are
+    kept, ties to the lower unit index.  unit = 2 with 4:8 is the in-pairs
+    pattern of ``pair_top2``; unit = 1 with 2:4 is the element-wise pattern
+    the pages pair with MXFP4."""
+    T, K = y.shape
+    U, n = M // unit, N // unit
+    s = np.abs(y.reshape(T, K // M, U, unit)).max(axis=-1)          # (T, G, U)
+    sp, sq = s[..., :, None], s[..., None, :]
+    idx = np.arange(U)
+    beats = (sq > sp) | ((sq == sp) & (idx[None, :] < idx[:, None]))
+    kept = beats.sum(axis=-1) < n
+    return np.repeat(kept, unit, axis=-1).reshape(T, K)
+
+
+def top2_of4_indices(M: np.ndarray):
+    """Kept positions i0 < i1 of every group of 4 of a 2:4 mask (T x K)."""
+    T, K = M.shape
+    order = np.argsort(~M.reshape(T, K // 4, 4), axis=-1, kind="stable")
+    return order[..., 0].astype(np.uint8), order[..., 1].astype(np.uint8)
+
+
+def compact_24(codes: np.ndarray, i0: np.ndarray, i1: np.ndarray) -> np.ndarray:
+    """2:4 backbone bytes (T x K/4): per group of 4 the codes at i0 (low
+    nibble) and i1 (high nibble)."""
+    T, K = codes.shape
+    c = codes.reshape(T, K // 4, 4)
+    t, g = np.indices(i0.shape)
+    return (c[t, g, i0] | (c[t, g, i1] << 4)).astype(np.uint8)
+
+
+def expand_24(bb_codes: np.ndarray, i0: np.ndarray, i1: np.ndarray) -> np.ndarray:
+    """Inverse of compact_24: element codes (T x K) with 0 at dropped positions."""
+    T, G = i0.shape
+    c = np.zeros((T, G, 4), dtype=np.uint8)
+    t, g = np.indices((T, G))
+    c[t, g, i0] = bb_codes & 0xF
+    c[t, g, i1] = bb_codes >> 4
+    return c.reshape(T, G * 4)
+
+
 def meta_bytes(i0: np.ndarray, i1: np.ndarray) -> np.ndarray:
     nib = (i0.astype(np.uint8) | (i1.astype(np.uint8) << 2))
     return (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
@@ -261,7 +305,7 @@ def nv_dequant_f64(codes, sc, block: int, s_T) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # prepare: the fused activation preparation (review §3.2-§3.5)
 # ----------------------------------------------------------------------------
-def prepare(x: np.ndarray, gamma, eps: float = 1e-6, fmt: str = "mxfp4") -> dict:
+def prepare(x: np.ndarray, gamma, eps: float = 1e-6, fmt: str = "mxfp4", mask: str = "4:8") -> dict:
     """Online sparse-dense decomposition of the activation rows ``x`` (T x K,
     fp32 values of the stored inputs).
 
@@ -271,13 +315,22 @@ def prepare(x: np.ndarray, gamma, eps: float = 1e-6, fmt: str = "mxfp4") -> dict
        X~_sp = D_sp(Q_sp(X_sp)).
     4. R = y - X~_sp (fp32; zero-cost at dropped positions where R = y).
     5. Q_dn quantizes R per block.
+    ``mask``: "4:8" (in pairs, groups of 8: metadata nibble = kept pair
+    indices) or "2:4" (element-wise, MXFP4 only, groups of 4: metadata nibble
+    = kept element indices, backbone byte = their two codes).
     Returns the layouts of the GPU library plus the fp32 intermediates."""
     y = rmsnorm(x, gamma, eps)
     T, K = y.shape
-    i0, i1 = pair_top2(y)
-    M = mask_from_pairs(i0, i1)
+    if mask == "4:8":
+        i0, i1 = pair_top2(y)
+        M = mask_from_pairs(i0, i1)
+    elif mask == "2:4" and fmt == "mxfp4":
+        M = nm_keep(y, 2, 4)
+        i0, i1 = top2_of4_indices(M)
+    else:
+        raise ValueError(f"mask {mask} with {fmt}")
     X_sp = np.where(M, y, F32(0.0))
-    out = {"y": y, "mask": M, "i0": i0, "i1": i1, "fmt": fmt, "T": T, "K": K}
+    out = {"y": y, "mask": M, "i0": i0, "i1": i1, "fmt": fmt, "T": T, "K": K, "mask_kind": mask}
     if fmt == "mxfp4":
         sp_codes, sp_e = mx_quantize(X_sp)
         Xt_sp = np.where(M, mx_dequant_f32(sp_codes, sp_e), F32(0.0))
@@ -295,8 +348,9 @@ def prepare(x: np.ndarray, gamma, eps: float = 1e-6, fmt: str = "mxfp4") -> dict
         out.update(bb_scale=sp_sc, res_scale=res_sc, tensor_scales=np.array([s_sp, s_dn], dtype=F32))
     else:
         raise ValueError(fmt)
+    bb = compact_pairs(sp_codes, i0, i1) if mask == "4:8" else compact_24(sp_codes, i0, i1)
     out.update(X_sp=X_sp, Xt_sp=Xt_sp, R=R,
-               bb_codes=compact_pairs(sp_codes, i0, i1), bb_meta=meta_bytes(i0, i1),
+               bb_codes=bb, bb_meta=meta_bytes(i0, i1),
                res_codes=pack_nibbles(res_codes), sp_codes_full=sp_codes, res_codes_full=res_codes)
     return out
 
@@ -334,7 +388,16 @@ def act_dequant(act: dict):
     """(X~_sp, R~) as exact fp64 values from the stored layouts."""
     fmt = act["fmt"]
     i0, i1 = meta_unpack(act["bb_meta"])
-    sp_codes = expand_pairs(act["bb_codes"], i0, i1)
+    if act.get("mask_kind", "4:8") == "2:4":
+        sp_codes = expand_24(act["bb_codes"], i0, i1)
+        t, g = np.indices(i0.shape)
+        keep = np.zeros(i0.shape + (4,), dtype=bool)
+        keep[t, g, i0] = True
+        keep[t, g, i1] = True
+        M = keep.reshape(i0.shape[0], -1)
+    else:
+        sp_codes = expand_pairs(act["bb_codes"], i0, i1)
+        M = mask_from_pairs(i0, i1)
     res_codes = unpack_nibbles(act["res_codes"])
     if fmt == "mxfp4":
         Xt = mx_dequant_f64(sp_codes, e8m0_decode_exponent(act["bb_scale"]))
@@ -343,7 +406,6 @@ def act_dequant(act: dict):
         s_sp, s_dn = act["tensor_scales"]
         Xt = nv_dequant_f64(sp_codes, act["bb_scale"], NV_BB_BLOCK, s_sp)
         Rt = nv_dequant_f64(res_codes, act["res_scale"], NV_RES_BLOCK, s_dn)
-    M = mask_from_pairs(i0, i1)
     return np.where(M, Xt, 0.0), Rt
 
 
@@ -469,14 +531,13 @@ def plain_linear_mx_sampled(codes: np.ndarray, scales: np.ndarray, wp: dict, out
     return Y, S
 
 
-def _sparse_quantized(v: np.ndarray, fmt: str, f64: bool = False) -> np.ndarray:
+def _sparse_quantized(v: np.ndarray, fmt: str, f64: bool = False, mask: str = "4:8") -> np.ndarray:
     """4:8 in-pairs sparsification of ``v`` (the pair-top-2 rule of
     ``pair_top2``) and backbone-style quantization of the kept values
     (MXFP4 per 32; NVFP4 E4M3 per 32 logical positions under the tensor scale
     of amax(v)), dequantized (fp32 as the preparation rounds it, or the exact
     fp64 value the GEMM multiplies) with zeros at dropped positions."""
-    i0, i1 = pair_top2(v)
-    M = mask_from_pairs(i0, i1)
+    M = mask_from_pairs(*pair_top2(v)) if mask == "4:8" else nm_keep(v, 2, 4)
     vs = np.where(M, v, F32(0.0))
     if fmt == "mxfp4":
         c, e = mx_quantize(vs)
@@ -511,6 +572,8 @@ def decomposition_study(x: np.ndarray, gamma, w: np.ndarray, fmt: str = "mxfp4",
       dense_dense   Q(y) + Q(y - Q(y))       (both paths dense)
       sharq         X~_sp + Q_dn(R)          (sparse backbone, dense residual)
       plain         Q(y)                     (one dense FP4 path)
+    and, for MXFP4, sparse_only_2:4 and sharq_2:4 with a 2:4 element-wise
+    backbone mask instead of 4:8 in pairs
     where y = RMSNorm(x), X~_sp and R are those of ``prepare``, W~ is the
     packed weight, M' is the pair-top-2 mask chosen on R, and each residual
     is taken against the quantized first path (review §3.3).  Every
@@ -530,6 +593,10 @@ def decomposition_study(x: np.ndarray, gamma, w: np.ndarray, fmt: str = "mxfp4",
         "sharq": Xt_sp + _dense_quantized(R, fmt, f64=True),
         "plain": plain_quantized(y, fmt),
     }
+    if fmt == "mxfp4":                                  # the pages' MXFP4 pattern, 2:4 element-wise
+        sp24 = _sparse_quantized(y, fmt, mask="2:4")
+        approx["sparse_only_2:4"] = _sparse_quantized(y, fmt, f64=True, mask="2:4")
+        approx["sharq_2:4"] = approx["sparse_only_2:4"] + _dense_quantized(y - sp24, fmt, f64=True)
     Wf = np.asarray(w, dtype=np.float64)
     return {"weights_fp4": {k: rel_frobenius(v @ W, ref) for k, v in approx.items()},
             "activation_only": {k: rel_frobenius(v @ Wf, ref) for k, v in approx.items()}}

@@ -21,10 +21,11 @@ SHARQ_ERR_HIP = 5
 
 SHARQ_MXFP4 = 0
 SHARQ_NVFP4_EMU = 1
+SHARQ_MXFP4_24 = 2          # activations only: MXFP4 with the 2:4 element-wise backbone
 SHARQ_F32 = 0
 SHARQ_BF16 = 1
 
-FORMATS = {"mxfp4": SHARQ_MXFP4, "nvfp4": SHARQ_NVFP4_EMU}
+FORMATS = {"mxfp4": SHARQ_MXFP4, "nvfp4": SHARQ_NVFP4_EMU, "mxfp4_24": SHARQ_MXFP4_24}
 
 # every entry point include/sharq.h declares
 EXPORTS = ("sharq_weight_sizes", "sharq_act_sizes", "sharq_pack_weight", "sharq_prepare", "sharq_linear",

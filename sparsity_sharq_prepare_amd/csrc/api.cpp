@@ -38,7 +38,10 @@ sharq_status from_hip(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-bool valid_fmt(int32_t f) { return f == SHARQ_MXFP4 || f == SHARQ_NVFP4_EMU; }
+bool valid_fmt(int32_t f) { return f == SHARQ_MXFP4 || f == SHARQ_NVFP4_EMU; }   // weights
+bool valid_act_fmt(int32_t f) { return valid_fmt(f) || f == SHARQ_MXFP4_24; }
+// the weight format an activation format multiplies with (2:4 backbones use MXFP4 weights)
+int32_t weight_fmt_of(int32_t act_fmt) { return act_fmt == SHARQ_MXFP4_24 ? SHARQ_MXFP4 : act_fmt; }
 bool valid_dtype(int32_t d) { return d == SHARQ_F32 || d == SHARQ_BF16; }
 size_t dtype_size(int32_t d) { return d == SHARQ_F32 ? 4 : 2; }
 
@@ -84,9 +87,9 @@ sharq_status prepare_checks(const void* X, int32_t dtype, int32_t T, int32_t K, 
 sharq_status linear_checks(const sharq_act* a, const sharq_weight* w, const int32_t* group_offsets,
                            const int32_t* row_index, int32_t total_rows, float* Y, int64_t ldy) {
   if (!a || !w || !Y) return fail(SHARQ_ERR_INVALID_ARGUMENT, "a, w and Y must not be NULL");
-  if (!valid_fmt(a->fmt) || !valid_fmt(w->fmt)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "unknown format");
-  if (a->fmt != w->fmt)
-    return fail(SHARQ_ERR_FORMAT_MISMATCH, "activation format %d != weight format %d", a->fmt, w->fmt);
+  if (!valid_act_fmt(a->fmt) || !valid_fmt(w->fmt)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "unknown format");
+  if (weight_fmt_of(a->fmt) != w->fmt)
+    return fail(SHARQ_ERR_FORMAT_MISMATCH, "activation format %d does not multiply weight format %d", a->fmt, w->fmt);
   if (a->K != w->K) return fail(SHARQ_ERR_FORMAT_MISMATCH, "activation K = %d != weight K = %d", a->K, w->K);
   if (sharq_status s = check_k(a->K, 128)) return s;
   if (a->T < 1 || w->D < 1 || w->n_groups < 1)
@@ -156,18 +159,19 @@ sharq_status sharq_weight_sizes(int32_t fmt, int32_t K, int32_t D, int32_t n_gro
 
 sharq_status sharq_act_sizes(int32_t fmt, int32_t T, int32_t K, size_t bytes_out[7]) {
   if (!bytes_out) return fail(SHARQ_ERR_INVALID_ARGUMENT, "bytes_out is NULL");
-  if (!valid_fmt(fmt)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "unknown format %d", fmt);
+  if (!valid_act_fmt(fmt)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "unknown format %d", fmt);
   if (sharq_status s = check_k(K, 32)) return s;
   if (T < 1) return fail(SHARQ_ERR_UNSUPPORTED_SHAPE, "T = %d must be >= 1", T);
   if ((int64_t)T * K > kMaxElems) return fail(SHARQ_ERR_UNSUPPORTED_SHAPE, "activation too large");
   const int64_t t = T;
   bytes_out[0] = (size_t)(t * (K / 4));
-  bytes_out[1] = (size_t)(t * (K / 16));
+  const bool nv = fmt == SHARQ_NVFP4_EMU;
+  bytes_out[1] = (size_t)(t * (fmt == SHARQ_MXFP4_24 ? K / 8 : K / 16));
   bytes_out[2] = (size_t)(t * (K / 32));
   bytes_out[3] = (size_t)(t * (K / 2));
-  bytes_out[4] = (size_t)(t * (fmt == SHARQ_MXFP4 ? K / 32 : K / 16));
-  bytes_out[5] = fmt == SHARQ_MXFP4 ? 0 : 2 * sizeof(float);
-  bytes_out[6] = fmt == SHARQ_MXFP4 ? 0 : sharq::prepare_nv_workspace(T, K);
+  bytes_out[4] = (size_t)(t * (nv ? K / 16 : K / 32));
+  bytes_out[5] = nv ? 2 * sizeof(float) : 0;
+  bytes_out[6] = nv ? sharq::prepare_nv_workspace(T, K) : 0;
   return ok();
 }
 
@@ -206,9 +210,10 @@ sharq_status sharq_prepare(const void* X, int32_t dtype, int32_t T, int32_t K, i
                            float eps, const sharq_act* out, void* workspace, size_t workspace_bytes, void* stream) {
   if (sharq_status st = prepare_checks(X, dtype, T, K, ldx, gamma, eps, out, workspace, workspace_bytes)) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (out->fmt == SHARQ_MXFP4) {
+  if (out->fmt != SHARQ_NVFP4_EMU) {
     return from_hip(sharq::launch_prepare_mx(X, dtype == SHARQ_BF16, T, K, ldx, gamma, eps, out->bb_codes,
-                                             out->bb_meta, out->bb_scale, out->res_codes, out->res_scale, s),
+                                             out->bb_meta, out->bb_scale, out->res_codes, out->res_scale, s,
+                                             out->fmt == SHARQ_MXFP4_24),
                     "sharq_prepare launch");
   }
   return from_hip(sharq::launch_prepare_nv(X, dtype == SHARQ_BF16, T, K, ldx, gamma, eps, out->bb_codes,
@@ -221,10 +226,10 @@ sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, const int32
                           const int32_t* row_index, int32_t total_rows, float* Y, int64_t ldy, void* stream) {
   if (sharq_status st = linear_checks(a, w, group_offsets, row_index, total_rows, Y, ldy)) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (a->fmt == SHARQ_MXFP4) {
+  if (a->fmt != SHARQ_NVFP4_EMU) {
     return from_hip(sharq::launch_linear_mx(a->bb_codes, a->bb_meta, a->bb_scale, a->res_codes, a->res_scale,
                                             row_index, total_rows, a->T, a->K, w->payload, w->scale_sp, w->D, w->n_groups,
-                                            group_offsets, Y, ldy, s),
+                                            group_offsets, Y, ldy, s, a->fmt == SHARQ_MXFP4_24),
                     "sharq_linear launch");
   }
   return from_hip(sharq::launch_linear_nv(a->bb_codes, a->bb_meta, a->bb_scale, a->res_codes, a->res_scale,

@@ -73,6 +73,25 @@ SHARQ_DEV uint4 expand4_fast(uint32_t c_lo, uint32_t c_hi, uint32_t meta16) {
   return r;
 }
 
+// 2:4 backbone: one 32-value block (8 groups of 4) from its 8 compacted bytes
+// (c_lo, c_hi: the kept codes of group g in byte g, lower index in the low
+// nibble) and its 8 metadata nibbles m32 (i0 | i1 << 2) -> 16 bytes, the kept
+// codes at nibbles 4 g + i0 and 4 g + i1, zeros elsewhere
+SHARQ_DEV uint32_t expand_24_pair(uint32_t b2, uint32_t m8) {
+  // two groups: kept bytes b2 (bits 0-15), nibbles m8 (bits 0-7) -> 32 bits
+  const uint32_t lo = ((b2 & 15u) << (4u * (m8 & 3u))) | (((b2 >> 4) & 15u) << (4u * ((m8 >> 2) & 3u)));
+  const uint32_t hi = (((b2 >> 8) & 15u) << (4u * ((m8 >> 4) & 3u))) | (((b2 >> 12) & 15u) << (4u * ((m8 >> 6) & 3u)));
+  return lo | (hi << 16);
+}
+SHARQ_DEV uint4 expand_24(uint32_t c_lo, uint32_t c_hi, uint32_t m32) {
+  uint4 r;
+  r.x = expand_24_pair(c_lo & 0xFFFFu, m32 & 0xFFu);
+  r.y = expand_24_pair(c_lo >> 16, (m32 >> 8) & 0xFFu);
+  r.z = expand_24_pair(c_hi & 0xFFFFu, (m32 >> 16) & 0xFFu);
+  r.w = expand_24_pair(c_hi >> 16, m32 >> 24);
+  return r;
+}
+
 }  // namespace
 
 // ============================================================================
@@ -80,7 +99,7 @@ SHARQ_DEV uint4 expand4_fast(uint32_t c_lo, uint32_t c_hi, uint32_t meta16) {
 // ============================================================================
 // grid.x = ceil(D / 16); blockDim = 64 * NW.  Wave w takes K-steps
 // w, w + NW, ... in batches of J whose loads are all issued before the MFMAs.
-template <int MT, int J>
+template <int MT, int J, bool M24 = false>
 __global__ __launch_bounds__(MT >= 8 ? 512 : 1024) void linear_mx_skinny(
     const uint8_t* __restrict__ bb_codes, const uint8_t* __restrict__ bb_meta, const uint8_t* __restrict__ bb_scale,
     const uint8_t* __restrict__ res_codes, const uint8_t* __restrict__ res_scale, const int32_t* __restrict__ row_index,
@@ -135,7 +154,8 @@ __global__ __launch_bounds__(MT >= 8 ? 512 : 1024) void linear_mx_skinny(
             const uint2 c = *reinterpret_cast<const uint2*>(bb_codes + arow[m] * (K >> 2) + 8 * (int64_t)kb);
             av[m][j].x = c.x;
             av[m][j].y = c.y;
-            av[m][j].z = *reinterpret_cast<const uint16_t*>(bb_meta + arow[m] * (K >> 4) + 2 * (int64_t)kb);
+            if (M24) av[m][j].z = *reinterpret_cast<const uint32_t*>(bb_meta + arow[m] * (K >> 3) + 4 * (int64_t)kb);
+            else av[m][j].z = *reinterpret_cast<const uint16_t*>(bb_meta + arow[m] * (K >> 4) + 2 * (int64_t)kb);
             as[m][j] = bb_scale[arow[m] * (K >> 5) + kb];
           }
         }
@@ -146,7 +166,7 @@ __global__ __launch_bounds__(MT >= 8 ? 512 : 1024) void linear_mx_skinny(
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         uint4 a = av[m][j];
-        if (!dn) a = expand4(a.x, a.y, a.z);
+        if (!dn) a = M24 ? expand_24(a.x, a.y, a.z) : expand4(a.x, a.y, a.z);
         acc[m] = mfma_fp4(a, wv[j], acc[m], as[m][j], ws[j]);
       }
     }
@@ -226,7 +246,7 @@ struct FusedPrep {
   uint32_t* sync;              // [2] counters, zero between calls
 };
 
-template <int NK, int CG, int J, bool FUSED>
+template <int NK, int CG, int J, bool FUSED, bool M24 = false>
 __global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
     const uint8_t* bb_codes, const uint8_t* bb_meta, const uint8_t* bb_scale, const uint8_t* res_codes,
     const uint8_t* res_scale, const int32_t* __restrict__ row_index, int rows, int act_rows, int K,
@@ -290,13 +310,13 @@ __global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
     return t < rows ? (uint32_t)gather_row(row_index, t, act_rows) : 0u;
   };
   uint4 rv[IPT], bv[BPT], sv[2];
-  uint32_t mv[BPT];
+  uint2 mv[BPT];                                      // metadata of the pair of blocks (2:4: 8 bytes)
   auto load_act = [&]() {
     const int an = __builtin_amdgcn_readfirstlane(act_rows);
     const __amdgpu_buffer_rsrc_t r_rc = rsrc(res_codes, (int64_t)an * (K >> 1));
     const __amdgpu_buffer_rsrc_t r_rs = rsrc(res_scale, (int64_t)an * (K >> 5));
     const __amdgpu_buffer_rsrc_t r_bc = rsrc(bb_codes, (int64_t)an * (K >> 2));
-    const __amdgpu_buffer_rsrc_t r_bm = rsrc(bb_meta, (int64_t)an * (K >> 4));
+    const __amdgpu_buffer_rsrc_t r_bm = rsrc(bb_meta, (int64_t)an * (K >> (M24 ? 3 : 4)));
     const __amdgpu_buffer_rsrc_t r_bs = rsrc(bb_scale, (int64_t)an * (K >> 5));
 #pragma unroll
     for (int j = 0; j < IPT; ++j) {
@@ -312,7 +332,12 @@ __global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
       const uint32_t ar = ok ? act_row(t) : 0u;
       const auto v = __builtin_amdgcn_raw_buffer_load_b128(r_bc, ok ? ar * (uint32_t)(K >> 2) + 16u * kp : kOut, 0, 0);
       bv[j] = make_uint4(v[0], v[1], v[2], v[3]);
-      mv[j] = __builtin_amdgcn_raw_buffer_load_b32(r_bm, ok ? ar * (uint32_t)(K >> 4) + 4u * kp : kOut, 0, 0);
+      if constexpr (M24) {
+        const auto m = __builtin_amdgcn_raw_buffer_load_b64(r_bm, ok ? ar * (uint32_t)(K >> 3) + 8u * kp : kOut, 0, 0);
+        mv[j] = make_uint2(m[0], m[1]);
+      } else {
+        mv[j] = make_uint2(__builtin_amdgcn_raw_buffer_load_b32(r_bm, ok ? ar * (uint32_t)(K >> 4) + 4u * kp : kOut, 0, 0), 0u);
+      }
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -398,8 +423,13 @@ __global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
   for (int j = 0; j < BPT; ++j) {
     const int i = tid + NT * j, t = qdiv(i, rKBh), kp = i - t * KBh;
     const bool ok = i < n_bb;
-    a_sm[ok ? 16 * (2 * kp) + t : 16 * KB + 1] = expand4_fast(bv[j].x, bv[j].y, mv[j] & 0xFFFFu);
-    a_sm[ok ? 16 * (2 * kp + 1) + t : 16 * KB + 2] = expand4_fast(bv[j].z, bv[j].w, mv[j] >> 16);
+    if constexpr (M24) {
+      a_sm[ok ? 16 * (2 * kp) + t : 16 * KB + 1] = expand_24(bv[j].x, bv[j].y, mv[j].x);
+      a_sm[ok ? 16 * (2 * kp + 1) + t : 16 * KB + 2] = expand_24(bv[j].z, bv[j].w, mv[j].y);
+    } else {
+      a_sm[ok ? 16 * (2 * kp) + t : 16 * KB + 1] = expand4_fast(bv[j].x, bv[j].y, mv[j].x & 0xFFFFu);
+      a_sm[ok ? 16 * (2 * kp + 1) + t : 16 * KB + 2] = expand4_fast(bv[j].z, bv[j].w, mv[j].x >> 16);
+    }
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -486,12 +516,12 @@ SHARQ_DEV int slot(int row, int q) { return row * 4 + (q ^ swz(row)); }
 // 16-byte half h of a 32-byte compacted-backbone row
 SHARQ_DEV int slot_sp(int row, int h) { return row * 2 + (h ^ ((row >> 3) & 1)); }
 
-template <int BM>
+template <int BM, bool M24 = false>
 struct TileStage {
   uint4 a_dn[BM * 4];          // residual codes, 64 B per row (swizzled 16 B slots)
   uint4 b[kBN * 4];            // weight payload, 64 B per column
   uint4 a_sp[BM * 2];          // compacted backbone, 32 B per row
-  uint32_t meta[BM * 2];       // backbone metadata, 8 B per row
+  uint32_t meta[BM * (M24 ? 4 : 2)];   // backbone metadata, 8 B per row (2:4: 16 B)
   uint32_t s_sp[BM];           // 4 scale bytes per row / column
   uint32_t s_dn[BM];
   uint32_t s_b[kBN];
@@ -544,13 +574,13 @@ struct TileFrag {
 
 }  // namespace
 
-template <int BM, bool GROUPED, int WN>
+template <int BM, bool GROUPED, int WN, bool M24 = false>
 __global__ __launch_bounds__(256 * WN, 1) void linear_mx_tile(
     const uint8_t* __restrict__ bb_codes, const uint8_t* __restrict__ bb_meta, const uint8_t* __restrict__ bb_scale,
     const uint8_t* __restrict__ res_codes, const uint8_t* __restrict__ res_scale, const int32_t* __restrict__ row_index,
     int rows, int act_rows, int K, const uint8_t* __restrict__ payload, const uint8_t* __restrict__ wscale, int D,
     int n_groups, const int32_t* __restrict__ group_offsets, float* __restrict__ Y, int64_t ldy) {
-  using Stage = TileStage<BM>;
+  using Stage = TileStage<BM, M24>;
   // 4 x WN waves: wave w covers rows (w & 3) * WM .. and columns (w >> 2) * WNC ..
   constexpr int NW = 4 * WN;
   constexpr int WM = BM / 4, WNC = kBN / WN, FM = WM / 32, FN = WNC / 32;
@@ -559,7 +589,7 @@ __global__ __launch_bounds__(256 * WN, 1) void linear_mx_tile(
   // DMA instructions per wave and stage: A_dn, B, A_sp, meta, scale rows
   // (WN = 1: s_sp, s_dn, s_b; WN = 2: waves 0-3 s_sp and s_dn, waves 4-7 s_b
   // twice, so every wave issues the same number and one wait count fits all)
-  constexpr int N_DN = BM / (16 * NW), N_B = 16 / NW, N_SP = BM / (32 * NW), N_MT = BM / (32 * NW);
+  constexpr int N_DN = BM / (16 * NW), N_B = 16 / NW, N_SP = BM / (32 * NW), N_MT = BM / ((M24 ? 16 : 32) * NW);
   constexpr int NDMA = N_DN + N_B + N_SP + N_MT + (WN == 1 ? 3 : 2);
   __shared__ Stage lds[kNS];
   const int tid = threadIdx.x, l = tid & 63;
@@ -624,7 +654,7 @@ __global__ __launch_bounds__(256 * WN, 1) void linear_mx_tile(
   }
 
   const int KS = K >> 7;
-  const uint32_t kA = K >> 2, kM = K >> 4, kS = K >> 5, kR = K >> 1;
+  const uint32_t kA = K >> 2, kM = K >> (M24 ? 3 : 4), kS = K >> 5, kR = K >> 1;
   const int4v r_dn = make_rsrc(res_codes, (uint32_t)act_rows * kR);
   const int4v r_sp = make_rsrc(bb_codes, (uint32_t)act_rows * kA);
   const int4v r_mt = make_rsrc(bb_meta, (uint32_t)act_rows * kM);
@@ -660,8 +690,8 @@ __global__ __launch_bounds__(256 * WN, 1) void linear_mx_tile(
     o_sp[j] = act_row(row) * kA + 16 * h;
   }
 #pragma unroll
-  for (int j = 0; j < N_MT; ++j) {                      // dword slots: 2 per row
-    const int sl = 64 * (w + NW * j) + l, row = sl >> 1, h = sl & 1;
+  for (int j = 0; j < N_MT; ++j) {                      // dword slots: 2 per row (2:4: 4)
+    const int sl = 64 * (w + NW * j) + l, row = M24 ? sl >> 2 : sl >> 1, h = M24 ? sl & 3 : sl & 1;
     o_mt[j] = act_row(row) * kM + 4 * h;
   }
   // scale rows: one dword (4 blocks) per row; for BM = 128 waves 2, 3 repeat
@@ -673,7 +703,7 @@ __global__ __launch_bounds__(256 * WN, 1) void linear_mx_tile(
   const int sdst = 64 * (wq & (BM / 64 - 1));
 
   auto issue = [&](int s, Stage& st) {
-    const uint32_t s64 = 64u * s, s32 = 32u * s, s8 = 8u * s, s4 = 4u * s;
+    const uint32_t s64 = 64u * s, s32 = 32u * s, s8 = (M24 ? 16u : 8u) * s, s4 = 4u * s;
 #pragma unroll
     for (int j = 0; j < N_DN; ++j) dma16(r_dn, o_dn[j], s64, lds_addr(&st.a_dn[64 * (w + NW * j)]));
 #pragma unroll
@@ -704,6 +734,7 @@ __global__ __launch_bounds__(256 * WN, 1) void linear_mx_tile(
     const uint16_t* s_dn = reinterpret_cast<const uint16_t*>(st.s_dn);
     const uint2* a_sp = reinterpret_cast<const uint2*>(st.a_sp);
     const uint16_t* meta = reinterpret_cast<const uint16_t*>(st.meta);
+    const uint32_t* meta32 = st.meta;
 #pragma unroll
     for (int n = 0; n < FN; ++n) {
       const int c = wn0 + 32 * n + lr;
@@ -715,7 +746,7 @@ __global__ __launch_bounds__(256 * WN, 1) void linear_mx_tile(
       const int r = wm0 + 32 * f + lr;
       F.dn[f] = st.a_dn[slot(r, 2 * kh + J)];
       F.sp[f] = a_sp[2 * slot_sp(r, kh) + J];
-      F.mt[f] = meta[4 * r + 2 * kh + J];
+      F.mt[f] = M24 ? meta32[4 * r + 2 * kh + J] : meta[4 * r + 2 * kh + J];
       F.ssp[f] = s_sp[2 * r + kh];
       F.sdn[f] = s_dn[2 * r + kh];
     }
@@ -731,7 +762,7 @@ __global__ __launch_bounds__(256 * WN, 1) void linear_mx_tile(
     constexpr int J = decltype(jc)::value;
 #pragma unroll
     for (int f = 0; f < FM; ++f) {
-      const uint4 asp = expand4_fast(F.sp[f].x, F.sp[f].y, F.mt[f]);
+      const uint4 asp = M24 ? expand_24(F.sp[f].x, F.sp[f].y, F.mt[f]) : expand4_fast(F.sp[f].x, F.sp[f].y, F.mt[f]);
 #pragma unroll
       for (int n = 0; n < FN; ++n) acc[f][n] = mfma32_fp4_sel<J>(asp, F.b[n], acc[f][n], F.ssp[f], F.bs[n]);
 #pragma unroll
@@ -1069,7 +1100,7 @@ int num_cus_gemm() {
 // workgroup stages the whole activation, so fewer, wider workgroups read
 // less of it (measured: 4096 x 14336 with 224 workgroups of 4 column groups
 // 9.6 us, with 448 of 2 10.6 us; 16 steps per wave at K = 14336 is slower).
-template <bool FUSED>
+template <bool FUSED, bool M24 = false>
 hipError_t launch_decode(const uint8_t* bb_codes, const uint8_t* bb_meta, const uint8_t* bb_scale,
                          const uint8_t* res_codes, const uint8_t* res_scale, const int32_t* row_index, int rows,
                          int act_rows, int K, const uint8_t* payload, const uint8_t* wscale, int D, float* Y, int64_t ldy,
@@ -1087,7 +1118,7 @@ hipError_t launch_decode(const uint8_t* bb_codes, const uint8_t* bb_meta, const 
   // fused: the producers are workgroups 0, 8, .., 8 (rows - 1)
   dim3 grid(FUSED ? std::max(n_gemm, 8 * (rows - 1) + 1) : n_gemm), block(64 * NK * CG);
 #define L(NK_, CG_, J_)                                                                                                 \
-  hipLaunchKernelGGL((linear_mx_decode<NK_, CG_, J_, FUSED>), grid, block, lds, s, bb_codes, bb_meta, bb_scale,         \
+  hipLaunchKernelGGL((linear_mx_decode<NK_, CG_, J_, FUSED, M24>), grid, block, lds, s, bb_codes, bb_meta, bb_scale,    \
                      res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, Y, ldy, fp)
   switch (J * 10000 + NK * 100 + CG) {
     case 40101: L(1, 1, 4); break;
@@ -1127,13 +1158,15 @@ hipError_t launch_prepare_linear_mx(const void* X, bool bf16, int T, int K, int6
                              ldy, fp, s);
 }
 
-hipError_t launch_linear_mx(const uint8_t* bb_codes, const uint8_t* bb_meta, const uint8_t* bb_scale,
-                            const uint8_t* res_codes, const uint8_t* res_scale, const int32_t* row_index, int rows,
-                            int act_rows, int K, const uint8_t* payload, const uint8_t* wscale, int D, int n_groups,
-                            const int32_t* group_offsets, float* Y, int64_t ldy, hipStream_t s) {
+namespace {
+template <bool M24>
+hipError_t launch_linear_mx_impl(const uint8_t* bb_codes, const uint8_t* bb_meta, const uint8_t* bb_scale,
+                                 const uint8_t* res_codes, const uint8_t* res_scale, const int32_t* row_index, int rows,
+                                 int act_rows, int K, const uint8_t* payload, const uint8_t* wscale, int D, int n_groups,
+                                 const int32_t* group_offsets, float* Y, int64_t ldy, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   if (n_groups == 1 && rows <= 8 && K <= kDecodeMaxK)
-    return launch_decode<false>(bb_codes, bb_meta, bb_scale, res_codes, res_scale, row_index, rows, act_rows, K, payload,
+    return launch_decode<false, M24>(bb_codes, bb_meta, bb_scale, res_codes, res_scale, row_index, rows, act_rows, K, payload,
                                 wscale, D, Y, ldy, FusedPrep{}, s);
   if (n_groups == 1 && rows <= 64) {
     const int KS = K / 128;
@@ -1147,7 +1180,7 @@ hipError_t launch_linear_mx(const uint8_t* bb_codes, const uint8_t* bb_meta, con
     const size_t lds = (size_t)NW * MT * 64 * 4 * sizeof(float);
     dim3 grid((D + 15) / 16), block(64 * NW);
 #define L(MT_, J_)                                                                                             \
-  hipLaunchKernelGGL((linear_mx_skinny<MT_, J_>), grid, block, lds, s, bb_codes, bb_meta, bb_scale, res_codes, \
+  hipLaunchKernelGGL((linear_mx_skinny<MT_, J_, M24>), grid, block, lds, s, bb_codes, bb_meta, bb_scale, res_codes, \
                      res_scale, row_index, rows, act_rows, K, payload, wscale, D, Y, ldy)
     switch (MT) {
       case 1: L(1, 8); break;
@@ -1161,7 +1194,9 @@ hipError_t launch_linear_mx(const uint8_t* bb_codes, const uint8_t* bb_meta, con
   const int tiles_n = (D + kBN - 1) / kBN;
   if (n_groups == 1) {
     const int tiles_m = (rows + 255) / 256;
-    if (K % 512 == 0) {
+    // (the 2:4 backbone's larger metadata does not fit the eight-wave tile's
+    // LDS ring; it takes the general tile below)
+    if (K % 512 == 0 && !M24) {
       // tile width 256 or 224: the one with fewer rounds x width over the CUs
       const int ncu = num_cus_gemm();
       const int t256 = tiles_m * ((D + 255) / 256), t224 = tiles_m * ((D + 223) / 224);
@@ -1174,7 +1209,7 @@ hipError_t launch_linear_mx(const uint8_t* bb_codes, const uint8_t* bb_meta, con
                            res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, Y, ldy);
       return hipGetLastError();
     }
-    hipLaunchKernelGGL((linear_mx_tile<256, false, 2>), dim3(tiles_m * tiles_n), dim3(512), 0, s, bb_codes, bb_meta,
+    hipLaunchKernelGGL((linear_mx_tile<256, false, 2, M24>), dim3(tiles_m * tiles_n), dim3(512), 0, s, bb_codes, bb_meta,
                        bb_scale, res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, 1, group_offsets, Y,
                        ldy);
   } else {
@@ -1182,11 +1217,22 @@ hipError_t launch_linear_mx(const uint8_t* bb_codes, const uint8_t* bb_meta, con
     // shapes faster than 128 x 256 with four (down 157 vs 199 us, up 146 vs
     // 149 us) despite the emptier last row tile of each expert
     const int bound = ((rows + 255) / 256 + n_groups) * tiles_n;
-    hipLaunchKernelGGL((linear_mx_tile<256, true, 2>), dim3(bound), dim3(512), 0, s, bb_codes, bb_meta, bb_scale,
+    hipLaunchKernelGGL((linear_mx_tile<256, true, 2, M24>), dim3(bound), dim3(512), 0, s, bb_codes, bb_meta, bb_scale,
                        res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, n_groups, group_offsets, Y,
                        ldy);
   }
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_linear_mx(const uint8_t* bb_codes, const uint8_t* bb_meta, const uint8_t* bb_scale,
+                            const uint8_t* res_codes, const uint8_t* res_scale, const int32_t* row_index, int rows,
+                            int act_rows, int K, const uint8_t* payload, const uint8_t* wscale, int D, int n_groups,
+                            const int32_t* group_offsets, float* Y, int64_t ldy, hipStream_t s, bool m24) {
+  return m24 ? launch_linear_mx_impl<true>(bb_codes, bb_meta, bb_scale, res_codes, res_scale, row_index, rows, act_rows,
+                                           K, payload, wscale, D, n_groups, group_offsets, Y, ldy, s)
+             : launch_linear_mx_impl<false>(bb_codes, bb_meta, bb_scale, res_codes, res_scale, row_index, rows,
+                                            act_rows, K, payload, wscale, D, n_groups, group_offsets, Y, ldy, s);
 }
 
 // plain dense MXFP4 GEMM of the comparison baseline: Y = X~ W~ with one

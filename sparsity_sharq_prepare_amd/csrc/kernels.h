@@ -18,9 +18,10 @@ int prepare_max_k();
 size_t prepare_nv_workspace(int T, int K);
 size_t pack_nv_workspace(int K, int D, int n_groups);
 
+// m24: the 2:4 element-wise backbone (metadata K/8 bytes per row) instead of 4:8 in pairs
 hipError_t launch_prepare_mx(const void* X, bool bf16, int T, int K, int64_t ldx, const float* gamma, float eps,
                              uint8_t* bb_codes, uint8_t* bb_meta, uint8_t* bb_scale, uint8_t* res_codes,
-                             uint8_t* res_scale, hipStream_t s);
+                             uint8_t* res_scale, hipStream_t s, bool m24 = false);
 
 hipError_t launch_prepare_nv(const void* X, bool bf16, int T, int K, int64_t ldx, const float* gamma, float eps,
                              uint8_t* bb_codes, uint8_t* bb_meta, uint8_t* bb_scale, uint8_t* res_codes,
@@ -39,10 +40,11 @@ hipError_t launch_pack(const void* W, bool bf16, bool nv, int K, int D, int n_gr
                        uint8_t* payload, uint8_t* scale_sp, uint8_t* scale_dn, float* tscale, void* workspace,
                        hipStream_t s);
 
+// m24: activations with the 2:4 element-wise backbone (metadata K/8 bytes per row)
 hipError_t launch_linear_mx(const uint8_t* bb_codes, const uint8_t* bb_meta, const uint8_t* bb_scale,
                             const uint8_t* res_codes, const uint8_t* res_scale, const int32_t* row_index, int rows,
                             int act_rows, int K, const uint8_t* payload, const uint8_t* wscale, int D, int n_groups,
-                            const int32_t* group_offsets, float* Y, int64_t ldy, hipStream_t s);
+                            const int32_t* group_offsets, float* Y, int64_t ldy, hipStream_t s, bool m24 = false);
 
 // single-launch decode (T <= 8, K <= decode_max_k()): MXFP4 prepare of the T
 // rows and the plain dual-path linear on them in one kernel; sync: two

@@ -44,19 +44,33 @@ SHARQ_DEV float tree8_sq(const float x[8]) {
 // quad DPP); the output descriptors span one row, so stores of groups past
 // the row (and of absent rows: zero-size descriptors) are dropped.  AUX: the
 // stores' cache-policy bits.
-template <int AUX = 0>
+// M24: the 2:4 element-wise backbone instead (review §3.2 general N:M mask;
+// the pattern the pages pair with MXFP4): each half of the group (4 values)
+// keeps its 2 largest |y|, ties to the lower index; the backbone byte of a
+// half holds the kept codes (lower index in the low nibble), its metadata
+// nibble their indices i0 | i1 << 2, one metadata byte per group of 8.
+template <int AUX = 0, bool M24 = false>
 SHARQ_DEV void mx_quantize_store(const float y[8], uint32_t g, __amdgpu_buffer_rsrc_t o_bc,
                                  __amdgpu_buffer_rsrc_t o_rc, __amdgpu_buffer_rsrc_t o_mt,
                                  __amdgpu_buffer_rsrc_t o_sb, __amdgpu_buffer_rsrc_t o_sr) {
   constexpr uint32_t kOut = 0x80000000u;
-  // ---- pair scores, kept pairs, backbone scale
-  const float s0 = fmaxf(fabsf(y[0]), fabsf(y[1]));
-  const float s1 = fmaxf(fabsf(y[2]), fabsf(y[3]));
-  const float s2 = fmaxf(fabsf(y[4]), fabsf(y[5]));
-  const float s3 = fmaxf(fabsf(y[6]), fabsf(y[7]));
-  uint64_t kp[4];
-  uint32_t i0, i1;
-  top2_lanes(s0, s1, s2, s3, kp, i0, i1);
+  // ---- scores, kept units (pairs, or values of each half), backbone scale
+  // (the kept units hold the group's max, so the block amax is that of y)
+  float sc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sc[i] = fabsf(y[i]);
+  const float s0 = fmaxf(sc[0], sc[1]);
+  const float s1 = fmaxf(sc[2], sc[3]);
+  const float s2 = fmaxf(sc[4], sc[5]);
+  const float s3 = fmaxf(sc[6], sc[7]);
+  uint64_t kp[4], kq[4];
+  uint32_t i0, i1, j0 = 0, j1 = 0;
+  if constexpr (M24) {
+    top2_lanes(sc[0], sc[1], sc[2], sc[3], kp, i0, i1);
+    top2_lanes(sc[4], sc[5], sc[6], sc[7], kq, j0, j1);
+  } else {
+    top2_lanes(s0, s1, s2, s3, kp, i0, i1);
+  }
   const uint32_t eb = e8m0_code(quad_max(fmaxf(fmaxf(s0, s1), fmaxf(s2, s3))));
   const float s_bb = exp2i((int)eb - 127);
   uint32_t bw = 0;
@@ -70,9 +84,15 @@ SHARQ_DEV void mx_quantize_store(const float y[8], uint32_t g, __amdgpu_buffer_r
     const v2f d[4] = {dq_fp4x2<0>(bw, s_bb), dq_fp4x2<1>(bw, s_bb), dq_fp4x2<2>(bw, s_bb), dq_fp4x2<3>(bw, s_bb)};
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const bool kept = lane_in(kp[p]);
-      R[2 * p] = __fsub_rn(y[2 * p], kept ? d[p].x : 0.0f);
-      R[2 * p + 1] = __fsub_rn(y[2 * p + 1], kept ? d[p].y : 0.0f);
+      if constexpr (M24) {
+        const uint64_t* k = p < 2 ? kp : kq;
+        R[2 * p] = __fsub_rn(y[2 * p], lane_in(k[(2 * p) & 3]) ? d[p].x : 0.0f);
+        R[2 * p + 1] = __fsub_rn(y[2 * p + 1], lane_in(k[(2 * p + 1) & 3]) ? d[p].y : 0.0f);
+      } else {
+        const bool kept = lane_in(kp[p]);
+        R[2 * p] = __fsub_rn(y[2 * p], kept ? d[p].x : 0.0f);
+        R[2 * p + 1] = __fsub_rn(y[2 * p + 1], kept ? d[p].y : 0.0f);
+      }
     }
   }
   const float rmax = fmaxf(fmaxf(fmaxf(fabsf(R[0]), fabsf(R[1])), fmaxf(fabsf(R[2]), fabsf(R[3]))),
@@ -84,17 +104,30 @@ SHARQ_DEV void mx_quantize_store(const float y[8], uint32_t g, __amdgpu_buffer_r
   rw = cvt_fp4x2<1>(rw, R[2], R[3], s_r);
   rw = cvt_fp4x2<2>(rw, R[4], R[5], s_r);
   rw = cvt_fp4x2<3>(rw, R[6], R[7], s_r);
-  // ---- compacted kept pair bytes (byte permute; selector 0x0C reads zero)
-  const uint32_t kept2 = __builtin_amdgcn_perm(0u, bw, i0 | (i1 << 8) | 0x0C0C0000u);
-  // metadata of the quad's 4 groups as 16 bits in its first lane
-  const uint32_t nib = i0 | (i1 << 2);
-  const uint32_t b8 = nib | (dpp_u<kDppQuadXor1>(nib) << 4);
-  const uint32_t m16 = (b8 & 0xFFu) | (dpp_u<kDppQuadXor2>(b8) << 8);
   // (block values only from the quad's first lane)
   const uint32_t qo = (g & 3) == 0 ? 0u : kOut;
-  __builtin_amdgcn_raw_buffer_store_b16((uint16_t)kept2, o_bc, 2 * g, 0, AUX);
-  __builtin_amdgcn_raw_buffer_store_b32(rw, o_rc, 4 * g, 0, AUX);
-  __builtin_amdgcn_raw_buffer_store_b16((uint16_t)m16, o_mt, (g >> 1) | qo, 0, AUX);
+  if constexpr (M24) {
+    // kept codes of each half: nibbles i0, i1 of bits 0-15 and j0, j1 of
+    // bits 16-31; metadata of the quad's 4 groups as 32 bits in its first lane
+    const uint32_t ba = __builtin_amdgcn_ubfe(bw, 4 * i0, 4) | (__builtin_amdgcn_ubfe(bw, 4 * i1, 4) << 4);
+    const uint32_t bb = __builtin_amdgcn_ubfe(bw, 16 + 4 * j0, 4) | (__builtin_amdgcn_ubfe(bw, 16 + 4 * j1, 4) << 4);
+    const uint32_t mb = i0 | (i1 << 2) | (j0 << 4) | (j1 << 6);
+    const uint32_t m16 = mb | (dpp_u<kDppQuadXor1>(mb) << 8);
+    const uint32_t m32 = (m16 & 0xFFFFu) | (dpp_u<kDppQuadXor2>(m16) << 16);
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(ba | (bb << 8)), o_bc, 2 * g, 0, AUX);
+    __builtin_amdgcn_raw_buffer_store_b32(rw, o_rc, 4 * g, 0, AUX);
+    __builtin_amdgcn_raw_buffer_store_b32(m32, o_mt, g | qo, 0, AUX);
+  } else {
+    // ---- compacted kept pair bytes (byte permute; selector 0x0C reads zero)
+    const uint32_t kept2 = __builtin_amdgcn_perm(0u, bw, i0 | (i1 << 8) | 0x0C0C0000u);
+    // metadata of the quad's 4 groups as 16 bits in its first lane
+    const uint32_t nib = i0 | (i1 << 2);
+    const uint32_t b8 = nib | (dpp_u<kDppQuadXor1>(nib) << 4);
+    const uint32_t m16 = (b8 & 0xFFu) | (dpp_u<kDppQuadXor2>(b8) << 8);
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)kept2, o_bc, 2 * g, 0, AUX);
+    __builtin_amdgcn_raw_buffer_store_b32(rw, o_rc, 4 * g, 0, AUX);
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)m16, o_mt, (g >> 1) | qo, 0, AUX);
+  }
   __builtin_amdgcn_raw_buffer_store_b8((uint8_t)eb, o_sb, (g >> 2) | qo, 0, AUX);
   __builtin_amdgcn_raw_buffer_store_b8((uint8_t)er, o_sr, (g >> 2) | qo, 0, AUX);
 }

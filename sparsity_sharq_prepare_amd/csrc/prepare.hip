@@ -137,7 +137,7 @@ SHARQ_DEV uint32_t select_kept(uint32_t word, uint32_t nib) {
 // the thread's groups is read once, and the next block's rows are loaded while
 // the current block is quantized, so HBM reads, the arithmetic and the stores
 // of different rows overlap inside every wave.
-template <int TPR, int MAXC, bool BF16, bool NORM>
+template <int TPR, int MAXC, bool BF16, bool NORM, bool M24 = false>
 struct MxRowPass {
   static constexpr int WGT = TPR > 256 ? TPR : 256;  // threads per workgroup
   static constexpr int RPW = WGT / TPR, WPR = TPR / kWave;
@@ -178,7 +178,7 @@ struct MxRowPass {
                                                __builtin_amdgcn_readfirstlane(row_ok ? row_bytes : 0), 0x00020000);
     };
     const __amdgpu_buffer_rsrc_t o_bc = orow(bb_codes, K >> 2), o_rc = orow(res_codes, K >> 1);
-    const __amdgpu_buffer_rsrc_t o_mt = orow(bb_meta, K >> 4), o_sb = orow(bb_scale, K >> 5);
+    const __amdgpu_buffer_rsrc_t o_mt = orow(bb_meta, M24 ? K >> 3 : K >> 4), o_sb = orow(bb_scale, K >> 5);
     const __amdgpu_buffer_rsrc_t o_sr = orow(res_scale, K >> 5);
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
@@ -201,19 +201,19 @@ struct MxRowPass {
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[i] = __fmul_rn(__fmul_rn(y[i], inv), gm[i]);
       }
-      mx_quantize_store(y, g, o_bc, o_rc, o_mt, o_sb, o_sr);
+      mx_quantize_store<0, M24>(y, g, o_bc, o_rc, o_mt, o_sb, o_sr);
     }
   }
 };
 
-template <int TPR, int MAXC, bool BF16, bool NORM>
+template <int TPR, int MAXC, bool BF16, bool NORM, bool M24>
 __global__ __launch_bounds__(TPR > 256 ? TPR : 256) void prepare_mx_kernel(const void* __restrict__ X, int T, int K, int64_t ldx,
                                                          const float* __restrict__ gamma, float eps,
                                                          uint8_t* __restrict__ bb_codes, uint8_t* __restrict__ bb_meta,
                                                          uint8_t* __restrict__ bb_scale,
                                                          uint8_t* __restrict__ res_codes,
                                                          uint8_t* __restrict__ res_scale) {
-  using Pass = MxRowPass<TPR, MAXC, BF16, NORM>;
+  using Pass = MxRowPass<TPR, MAXC, BF16, NORM, M24>;
   constexpr int RPW = Pass::RPW;
   // two parities: a block's cross-wave partial sums are read before the
   // barrier of the next block, so the block after next may overwrite them
@@ -611,11 +611,14 @@ size_t prepare_nv_workspace(int T, int K) {
 
 hipError_t launch_prepare_mx(const void* X, bool bf16, int T, int K, int64_t ldx, const float* gamma, float eps,
                              uint8_t* bb_codes, uint8_t* bb_meta, uint8_t* bb_scale, uint8_t* res_codes,
-                             uint8_t* res_scale, hipStream_t s) {
+                             uint8_t* res_scale, hipStream_t s, bool m24) {
   const PrepGeom g = prep_geometry_mx(T, K);
-#define L2(TPR, MAXC, B, N)                                                                           \
-  hipLaunchKernelGGL((prepare_mx_kernel<TPR, MAXC, B, N>), dim3(g.blocks), dim3(g.threads), 0, s, X, T, K, ldx, gamma, \
-                     eps, bb_codes, bb_meta, bb_scale, res_codes, res_scale)
+#define L3(TPR, MAXC, B, N, M)                                                                                      \
+  hipLaunchKernelGGL((prepare_mx_kernel<TPR, MAXC, B, N, M>), dim3(g.blocks), dim3(g.threads), 0, s, X, T, K, ldx, \
+                     gamma, eps, bb_codes, bb_meta, bb_scale, res_codes, res_scale)
+#define L2(TPR, MAXC, B, N)                  \
+  if (m24) L3(TPR, MAXC, B, N, true);        \
+  else L3(TPR, MAXC, B, N, false)
 #define L(TPR, MAXC)                                   \
   if (bf16) {                                          \
     if (gamma) L2(TPR, MAXC, true, true);              \
@@ -627,6 +630,7 @@ hipError_t launch_prepare_mx(const void* X, bool bf16, int T, int K, int64_t ldx
   SHARQ_PREP_MX_DISPATCH(L)
 #undef L
 #undef L2
+#undef L3
   return hipGetLastError();
 }
 

@@ -62,7 +62,7 @@ class PreparedAct:
     T: int
     K: int
     bb_codes: torch.Tensor         # uint8 (T, K/4)
-    bb_meta: torch.Tensor          # uint8 (T, K/16)
+    bb_meta: torch.Tensor          # uint8 (T, K/16 | K/8 for the 2:4 backbone)
     bb_scale: torch.Tensor         # uint8 (T, K/32)
     res_codes: torch.Tensor        # uint8 (T, K/2)
     res_scale: torch.Tensor        # uint8 (T, K/32 | K/16)
@@ -99,10 +99,12 @@ def empty_weight(fmt: str, K: int, D: int, n_groups: int = 1, device="cuda") -> 
 def empty_act(fmt: str, T: int, K: int, device="cuda") -> PreparedAct:
     sz = L.act_sizes(L.FORMATS[fmt], T, K)
     u8 = dict(dtype=torch.uint8, device=device)
-    res_scale = torch.empty((T, K // 32 if fmt == "mxfp4" else K // 16), **u8)
-    ts = None if fmt == "mxfp4" else torch.empty(2, dtype=torch.float32, device=device)
+    nv = fmt == "nvfp4"
+    res_scale = torch.empty((T, K // 16 if nv else K // 32), **u8)
+    ts = torch.empty(2, dtype=torch.float32, device=device) if nv else None
     ws = torch.empty(max(sz[6], 16), **u8) if sz[6] else None
-    return PreparedAct(fmt, T, K, torch.empty((T, K // 4), **u8), torch.empty((T, K // 16), **u8),
+    meta = torch.empty((T, K // 8 if fmt == "mxfp4_24" else K // 16), **u8)
+    return PreparedAct(fmt, T, K, torch.empty((T, K // 4), **u8), meta,
                        torch.empty((T, K // 32), **u8), torch.empty((T, K // 2), **u8), res_scale, ts, ws)
 
 

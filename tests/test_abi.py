@@ -190,3 +190,19 @@ def test_plain_baseline_validation_errors():
     assert f(c, s, 8, _fake_weight(K=512), Y, 32, None) == L.SHARQ_ERR_INVALID_ARGUMENT
     assert f(c, s, 0, _fake_weight(K=512), Y, 64, None) == L.SHARQ_ERR_UNSUPPORTED_SHAPE
     assert f(None, s, 8, _fake_weight(K=512), Y, 64, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+
+
+def test_mxfp4_24_format_rules():
+    lib = L.lib()
+    sz = (ctypes.c_size_t * 7)()
+    assert lib.sharq_act_sizes(L.SHARQ_MXFP4_24, 8, 256, sz) == L.SHARQ_OK
+    assert list(sz) == [8 * 64, 8 * 32, 8 * 8, 8 * 128, 8 * 8, 0, 0]       # metadata K/8 per row
+    w5 = (ctypes.c_size_t * 5)()
+    assert lib.sharq_weight_sizes(L.SHARQ_MXFP4_24, 256, 64, 1, w5) == L.SHARQ_ERR_INVALID_ARGUMENT
+    Y = 0x30000
+    a24 = _fake_act(fmt=L.SHARQ_MXFP4_24)
+    # 2:4 activations multiply MXFP4 weights, not NVFP4 ones
+    assert lib.sharq_linear(a24, _fake_weight(fmt=1), None, None, 8, Y, 64, None) == L.SHARQ_ERR_FORMAT_MISMATCH
+    # the single-launch decode offers the 4:8 backbone only
+    assert lib.sharq_prepare_linear(0x50000, 1, 8, 256, 256, None, 1e-6, a24, _fake_weight(), Y, 64, 0x90000, 16,
+                                    None) == L.SHARQ_ERR_INVALID_ARGUMENT

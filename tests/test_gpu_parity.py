@@ -557,3 +557,105 @@ def test_plain_linear_dense_prefill_sampled():
     wref = O.pack_weight(case.w_f32()[:, cols])
     Yr, S = O.plain_linear_mx_sampled(ref_c, ref_s, wref, r, np.searchsorted(cols, c))
     assert_gemm_close(Y.cpu().numpy()[r, c], Yr, S)
+
+
+# ------------------------------------------------------------------ 2:4 element-wise backbone (MXFP4)
+def oracle_prepare_24(case, eps=1e-6):
+    return O.prepare(case.x_f32(), case.gamma, eps, "mxfp4", mask="2:4")
+
+
+M24_PREP = [  # (T, K, dtype, gamma): the prepare geometries, ragged T, no normalization
+    (37, 256, "bf16", True), (5, 768, "bf16", True), (3, 32, "f32", True), (300, 4096, "bf16", True),
+    (4099, 2048, "bf16", True), (17, 14336, "bf16", True), (64, 4096, "bf16", False), (2100, 4096, "f32", True),
+]
+
+
+@pytest.mark.parametrize("T,K,dtype,gamma", M24_PREP)
+def test_prepare_24_shapes(T, K, dtype, gamma):
+    case = synth.random_case(11 * T + K, T, K, 8, dtype=dtype, gamma=gamma)
+    act = ops.prepare(dev_x(case), dev_gamma(case.gamma), 1e-6, "mxfp4_24")
+    compare_act(act, oracle_prepare_24(case))
+
+
+def test_prepare_24_edge_rows():
+    # zero row, worked-example row, signed zeros, tiny and large magnitudes,
+    # exact ties inside groups of 4
+    K = 64
+    x = np.zeros((6, K), np.float32)
+    x[1, :] = 0.2
+    x[1, 5] = 12.0
+    x[2, ::2] = -0.0
+    x[2, 1::2] = 1e-30
+    x[3, :] = np.float32(3.0e30) * np.cos(np.arange(K))
+    x[4, :] = np.tile(np.array([1, -1, 1, -1, 2, 2, -2, -2], np.float32), K // 8)
+    x[5, :] = np.float32(1e-38) * np.arange(K)
+    case = synth.LinearCase("edge", "mxfp4", "f32", 6, K, 8, x, None, np.zeros((K, 8), np.float32))
+    act = ops.prepare(dev_x(case), None, 1e-6, "mxfp4_24")
+    compare_act(act, O.prepare(x, None, 1e-6, "mxfp4", mask="2:4"))
+    g = np.ones(K, np.float32)
+    act = ops.prepare(dev_x(case), dev_gamma(g), 1e-6, "mxfp4_24")
+    compare_act(act, O.prepare(x, g, 1e-6, "mxfp4", mask="2:4"))
+
+
+M24_LINEAR = [  # decode (<= 8 rows), skinny (<= 64), general tile (> 64 rows, any K % 128), ragged
+    (1, 512, 200), (8, 512, 200), (5, 1152, 72), (7, 16384, 48), (13, 256, 64), (64, 384, 130),
+    (65, 512, 300), (300, 512, 520), (700, 128, 40), (256, 1024, 256), (70, 512, 1),
+]
+
+
+@pytest.mark.parametrize("T,K,D", M24_LINEAR)
+def test_linear_24_shapes(T, K, D):
+    case = synth.random_case(T + 3 * K + D + 1, T, K, D)
+    act = ops.prepare(dev_x(case), dev_gamma(case.gamma), 1e-6, "mxfp4_24")
+    w = ops.pack_weight(dev_w(case.w, "bf16"))
+    Y = ops.linear(act, w)
+    ref = oracle_prepare_24(case)
+    compare_act(act, ref)
+    Yr, S = O.sharq_linear(ref, O.pack_weight(case.w_f32()))
+    assert_gemm_close(Y.cpu().numpy(), Yr, S)
+
+
+@pytest.mark.parametrize("i", range(3), ids=DECODE_IDS)
+def test_linear_24_decode_full_sampled(i):
+    case = synth.decode_case(i)
+    act = ops.prepare(dev_x(case), dev_gamma(case.gamma), 1e-6, "mxfp4_24")
+    w = ops.pack_weight(dev_w(case.w, "bf16"))
+    Y = ops.linear(act, w)
+    ref = oracle_prepare_24(case)
+    compare_act(act, ref)
+    r, c = sample_pairs(case.T, case.D, 3000, seed=case.K + 1)
+    Yr, S = O.sharq_linear_sampled(ref, O.pack_weight(case.w_f32()), r, c)
+    assert_gemm_close(Y.cpu().numpy()[r, c], Yr, S)
+
+
+def test_linear_24_prefill_sampled():
+    case = synth.prefill_case()
+    act = ops.prepare(dev_x(case), dev_gamma(case.gamma), 1e-6, "mxfp4_24")
+    w = ops.pack_weight(dev_w(case.w, "bf16"))
+    Y = ops.linear(act, w)
+    rows = np.random.default_rng(4).choice(case.T, 48, replace=False)
+    refp = O.prepare(case.x_f32()[rows], case.gamma, 1e-6, "mxfp4", mask="2:4")
+    g = act.as_numpy()
+    for k in ("bb_codes", "bb_meta", "bb_scale", "res_codes", "res_scale"):
+        assert_bytes_equal(k, g[k][rows], refp[k])
+    r, c = sample_pairs(case.T, case.D, 2000, seed=5)
+    ref = oracle_prepare_24(case)
+    cols = np.unique(c)
+    wref = O.pack_weight(case.w_f32()[:, cols])
+    Yr, S = O.sharq_linear_sampled(ref, wref, r, np.searchsorted(cols, c))
+    assert_gemm_close(Y.cpu().numpy()[r, c], Yr, S)
+
+
+def test_grouped_24_small():
+    rng = np.random.default_rng(18)
+    E, T, K, D = 8, 64, 256, 160
+    go, ri = synth.draw_routing(rng, T, E, 2)
+    case = synth.random_case(18, T, K, 1)
+    W = synth.f32_to_bf16_bits(rng.standard_normal((E, K, D)).astype(np.float32) * 0.02)
+    act = ops.prepare(dev_x(case), dev_gamma(case.gamma), 1e-6, "mxfp4_24")
+    w = ops.pack_weight(dev_w(W, "bf16"))
+    Y = ops.linear(act, w, group_offsets=torch.from_numpy(go).cuda(), row_index=torch.from_numpy(ri).cuda())
+    ref = oracle_prepare_24(case)
+    wps = [O.pack_weight(synth.bf16_bits_to_f32(W[e])) for e in range(E)]
+    Yr, S = O.grouped_linear(ref, wps, go, ri)
+    assert_gemm_close(Y.cpu().numpy(), Yr, S)

@@ -216,3 +216,49 @@ def test_nvfp4_residual_size_4p5_bits():
     p = O.prepare(case.x_f32(), case.gamma, 1e-6, fmt="nvfp4")
     bits = (p["res_codes"].shape[1] + p["res_scale"].shape[1]) * 8 / 512
     assert bits == 4.5
+
+
+# --------------------------------------------------------- N:M masks (2:4)
+def test_nm_keep_matches_pair_rule_and_brute_force():
+    rng = np.random.default_rng(17)
+    y = rng.integers(0, 4, (40, 64)).astype(np.float32) * np.where(rng.random((40, 64)) < 0.5, -1, 1)
+    # 4:8 in pairs is the general rule with units of 2
+    assert np.array_equal(O.nm_keep(y, 4, 8, unit=2), O.mask_from_pairs(*O.pair_top2(y)))
+    # 2:4: brute force over the 6 choices; the first (lexicographic) choice
+    # with the largest sum of |y| (integer scores: ties are frequent)
+    M = O.nm_keep(y, 2, 4)
+    import itertools
+    combos = list(itertools.combinations(range(4), 2))
+    for t in range(y.shape[0]):
+        for g in range(16):
+            a = np.abs(y[t, 4 * g: 4 * g + 4])
+            best = max(combos, key=lambda c: (a[c[0]] + a[c[1]], -combos.index(c)))
+            exp = np.zeros(4, bool)
+            exp[list(best)] = True
+            assert np.array_equal(M[t, 4 * g: 4 * g + 4], exp), (t, g, a)
+    assert np.all(M.reshape(40, 16, 4).sum(-1) == 2)
+
+
+def test_prepare_24_worked_example_and_identities():
+    # the explainer's block (one 12 among 0.2s) with the 2:4 backbone:
+    # group 1 (k = 4..7) keeps k = 5 (the 12) and k = 4 (ties to the lower
+    # index); every other group keeps its first two positions
+    x = np.full((1, 32), np.float32(0.2), dtype=np.float32)
+    x[0, 5] = 12.0
+    p = O.prepare(x, None, fmt="mxfp4", mask="2:4")
+    assert p["bb_meta"][0].tolist() == [0x44] * 4             # nibble 0 | 1 << 2 = 4 in every group
+    # backbone scale 2^1 (amax 12): 0.2 / 2 -> 0, 12 / 2 = 6 -> code 7
+    assert p["bb_scale"][0].tolist() == [128]
+    assert p["bb_codes"][0].tolist() == [0x00, 0x70, 0, 0, 0, 0, 0, 0]
+    # residual: 0 at k = 5, 0.2 elsewhere -> scale 2^-4, 0.2 * 16 = 3.2 -> code 5
+    assert p["res_scale"][0].tolist() == [123]
+    Xt, Rt = O.act_dequant(p)
+    assert Xt[0, 5] == 12.0 and np.all(Xt[0, np.arange(32) != 5] == 0)
+    assert np.all(Rt[0, np.arange(32) != 5] == 0.1875) and Rt[0, 5] == 0
+    # y = X~_sp + R bit for bit; exactly 2 of every 4 kept
+    case = synth.random_case(5, 6, 512, 8)
+    q = O.prepare(case.x_f32(), case.gamma, 1e-6, "mxfp4", mask="2:4")
+    assert np.array_equal(q["Xt_sp"] + q["R"], q["y"])
+    assert np.all(q["mask"].reshape(6, -1, 4).sum(-1) == 2)
+    with pytest.raises(ValueError):
+        O.prepare(case.x_f32(), case.gamma, 1e-6, "nvfp4", mask="2:4")
