@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decode", choices=["decode", "prefill", "nvfp4", "moe"])
+    p.add_argument("--mask", default="4:8", choices=["4:8", "2:4"],
+                   help="backbone mask of the MXFP4 workloads: 4:8 in pairs, or 2:4 element-wise")
     p.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = enough for > 512 MB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -83,15 +85,17 @@ class Job:
     def gemm_flops_issued(self):         # zero-filled backbone on dense MFMA: 4 T K D
         return 4.0 * self.rows * self.K * self.D
 
+    def act_bytes_per_elem(self):        # prepared activation bytes per input element
+        return {"mxfp4": 0.875, "mxfp4_24": 0.9375, "nvfp4": 0.90625}[self.fmt]
+
     def gemm_bytes(self):
         w = self.groups * self.D * self.K * (0.5 + 1.0 / 32)
-        a = self.X.shape[0] * self.K * 0.875
+        a = self.X.shape[0] * self.K * self.act_bytes_per_elem()
         return w + a + 4.0 * self.rows * self.D
 
     def prep_bytes(self):
         xb = self.X.element_size()
-        out = 0.875 if self.fmt == "mxfp4" else 0.90625
-        return self.X.shape[0] * self.K * (xb + out) + 4.0 * self.K
+        return self.X.shape[0] * self.K * (xb + self.act_bytes_per_elem()) + 4.0 * self.K
 
     def fused_bytes(self):               # X, gamma and weights in; prepared activations and Y out
         w = self.D * self.K * (0.5 + 1.0 / 32)
@@ -106,12 +110,13 @@ def _dev(a, bf16=True):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def build_jobs(workload: str, copies: int):
+def build_jobs(workload: str, copies: int, mask: str = "4:8"):
     import numpy as np
     import torch
     from sparsity_sharq_prepare_amd import ops, synth
 
     jobs, cases, pack_times = [], [], []
+    afmt = "mxfp4_24" if mask == "2:4" else "mxfp4"      # activation format of the MXFP4 workloads
 
     def pack_copies(W, fmt, n):
         out = []
@@ -133,14 +138,14 @@ def build_jobs(workload: str, copies: int):
         for i in range(3):
             c = synth.decode_case(i)
             W = _dev(c.w)
-            jobs.append(Job(c.name, "mxfp4", _dev(c.x), _dev(c.gamma, False), pack_copies(W, "mxfp4", n),
+            jobs.append(Job(c.name, afmt, _dev(c.x), _dev(c.gamma, False), pack_copies(W, "mxfp4", n),
                             c.T, c.K, c.D))
             del W
             cases.append(c)
     elif workload == "prefill":
         c = synth.prefill_case()
         W = _dev(c.w)
-        jobs.append(Job(c.name, "mxfp4", _dev(c.x), _dev(c.gamma, False),
+        jobs.append(Job(c.name, afmt, _dev(c.x), _dev(c.gamma, False),
                         pack_copies(W, "mxfp4", n_copies(c.K * c.D * 0.53125)), c.T, c.K, c.D))
         cases.append(c)
     elif workload == "nvfp4":
@@ -155,7 +160,7 @@ def build_jobs(workload: str, copies: int):
             W = _dev(mc.w)
             go = torch.from_numpy(mc.group_offsets).cuda()
             ri = None if mc.row_index is None else torch.from_numpy(mc.row_index).cuda()
-            jobs.append(Job(mc.name, "mxfp4", _dev(mc.x), _dev(mc.gamma, False),
+            jobs.append(Job(mc.name, afmt, _dev(mc.x), _dev(mc.gamma, False),
                             pack_copies(W, "mxfp4", n_copies(W.numel() * 0.53125)), mc.x.shape[0], mc.K, mc.D,
                             rows=mc.total_rows, group_offsets=go, row_index=ri))
             cases.append(mc)
@@ -405,13 +410,13 @@ def gpu_error_outputs(jobs, rows):
     out = []
     for j, r in zip(jobs, rows):
         e = {}
-        if j.fmt == "mxfp4" and j.groups == 1:
+        if j.fmt in ("mxfp4", "mxfp4_24") and j.groups == 1:
             X = j.X[:r]
             if j.K % 512 == 0:
                 y = ops.rmsnorm(X, j.gamma, 1e-6)
                 codes, scales = ops.quantize_mx(y)
                 e["plain"] = ops.linear_dense(codes, scales, j.weights[0])
-            act = ops.prepare(X, j.gamma, 1e-6, "mxfp4")
+            act = ops.prepare(X, j.gamma, 1e-6, j.fmt)
             act.res_codes.zero_()
             e["sparse_only"] = ops.linear(act, j.weights[0])
         out.append({k: v.float().cpu().numpy() for k, v in e.items()})
@@ -471,7 +476,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    jobs, cases, pack_times = build_jobs(args.workload, args.copies)
+    if args.mask == "2:4" and args.workload == "nvfp4":
+        print("the 2:4 backbone is an MXFP4 option", file=sys.stderr)
+        sys.exit(2)
+    jobs, cases, pack_times = build_jobs(args.workload, args.copies, args.mask)
     wall, n_steps, prep_ms, gemm_ms, fused_ms = timed(jobs, args.steps, args.warmup)
     ms_step = wall * 1e3 / n_steps
 
@@ -527,6 +535,7 @@ def main():
                                 "prefill": "llama3.1-8b prefill linear 4096x4096x14336, MXFP4",
                                 "nvfp4": "qwen2.5-7b linears T=2048 (3584x18944, 18944x3584), NVFP4 emulated",
                                 "moe": "qwen3-30b-a3b moe linears, 128 experts top-8, 4096 tokens, up 2048x768 + down 768x2048, MXFP4"}[args.workload],
+                   "backbone_mask": "4:8 in pairs" if args.mask == "4:8" else "2:4 element-wise",
                    "tokens_per_step": tokens, "weight_copies_rotated": len(jobs[0].weights)},
         "tokens_per_s": round(tok_s, 1),
         "roofline": roofline,
