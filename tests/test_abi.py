@@ -206,3 +206,12 @@ def test_mxfp4_24_format_rules():
     # the single-launch decode offers the 4:8 backbone only
     assert lib.sharq_prepare_linear(0x50000, 1, 8, 256, 256, None, 1e-6, a24, _fake_weight(), Y, 64, 0x90000, 16,
                                     None) == L.SHARQ_ERR_INVALID_ARGUMENT
+
+
+def test_prepare_k_limit():
+    lib = L.lib()
+    K = 32768 + 128
+    a = _fake_act(K=K)
+    assert lib.sharq_prepare(0x50000, 1, 8, K, K, None, 1e-6, a, None, 0, None) == L.SHARQ_ERR_UNSUPPORTED_SHAPE
+    assert "maximum" in lib.sharq_last_error().decode()
+    assert lib.sharq_rmsnorm(0x50000, 1, 8, K, K, None, 1e-6, 0x30000, K, None) == L.SHARQ_ERR_UNSUPPORTED_SHAPE

@@ -659,3 +659,22 @@ def test_grouped_24_small():
     wps = [O.pack_weight(synth.bf16_bits_to_f32(W[e])) for e in range(E)]
     Yr, S = O.grouped_linear(ref, wps, go, ri)
     assert_gemm_close(Y.cpu().numpy(), Yr, S)
+
+
+# ------------------------------------------------------------------ largest supported K
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "mxfp4_24"])
+def test_prepare_and_linear_at_max_k(fmt):
+    # K = 32768: 256 threads x 16 groups of 8 per row, the prepare kernels'
+    # register limit; the GEMM runs the skinny path (K beyond the decode
+    # kernel's staged maximum) and the tile path
+    K = 32768
+    for T, D in ((3, 40), (70, 96)):
+        base = "nvfp4" if fmt == "nvfp4" else "mxfp4"
+        case = synth.random_case(T + D, T, K, D, fmt=base)
+        act = ops.prepare(dev_x(case), dev_gamma(case.gamma), 1e-6, fmt)
+        w = ops.pack_weight(dev_w(case.w, "bf16"), base)
+        Y = ops.linear(act, w)
+        ref = O.prepare(case.x_f32(), case.gamma, 1e-6, base, mask="2:4" if fmt == "mxfp4_24" else "4:8")
+        compare_act(act, ref)
+        Yr, S = O.sharq_linear(ref, O.pack_weight(case.w_f32(), base))
+        assert_gemm_close(Y.cpu().numpy(), Yr, S)
