@@ -169,7 +169,7 @@ sharq_status sharq_prepare(const void *X, int32_t dtype, int32_t T, int32_t K, i
  * group_offsets[e+1]-1 use expert e's weights; row_index as above.
  * Y: (device) fp32 total_rows x D, row r at Y + r * ldy (ldy >= D).
  * Size limit: a->T * K / 2 and D * K / 2 (one group's payload) must each
- * stay under 4 GiB - 256 bytes (32-bit buffer offsets), else
+ * stay under 2 GiB - 256 bytes (buffer offsets below bit 31), else
  * UNSUPPORTED_SHAPE.
  * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, FORMAT_MISMATCH, HIP. */
 sharq_status sharq_linear(const sharq_act *a, const sharq_weight *w, const int32_t *group_offsets,
@@ -228,7 +228,8 @@ sharq_status sharq_quantize_mx(const float *Y, int32_t T, int32_t K, int64_t ldy
  * codes, scales: (device) plain MXFP4 activations as sharq_quantize_mx
  * writes them (T rows); w: (host) MXFP4 weight, n_groups == 1, its dense
  * scale view is used; Y: (device) fp32 T x D, row t at Y + t * ldy.
- * w->K % 512 == 0; the size limits of sharq_linear apply.
+ * w->K % 512 == 0; the size limits of sharq_linear apply (T * K / 2 and
+ * D * K / 2 under 2 GiB - 256 bytes).
  * Errors: INVALID_ARGUMENT, UNSUPPORTED_SHAPE, FORMAT_MISMATCH, HIP. */
 sharq_status sharq_linear_dense(const uint8_t *codes, const uint8_t *scales, int32_t T,
                                 const sharq_weight *w, float *Y, int64_t ldy, void *stream);

@@ -46,7 +46,10 @@ bool valid_dtype(int32_t d) { return d == SHARQ_F32 || d == SHARQ_BF16; }
 size_t dtype_size(int32_t d) { return d == SHARQ_F32 ? 4 : 2; }
 
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
-constexpr int64_t kMaxDescBytes = ((int64_t)1 << 32) - 256;
+// buffers the GEMM kernels address through buffer descriptors stay below
+// 2 GiB: the kernels mark absent loads with offset bit 31, which must then lie
+// past every such buffer (a load past a descriptor's size returns zeros)
+constexpr int64_t kMaxDescBytes = ((int64_t)1 << 31) - 256;
 
 sharq_status check_k(int32_t K, int mult) {
   if (K <= 0 || K % mult != 0)

@@ -939,7 +939,9 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
   for (int j = 0; j < 2; ++j) {
     const int sl = 64 * (w + 8 * j) + l, row = sl >> 2, q = (sl & 3) ^ swz(row);
     o_dn[j] = act_row(row) * kR + 16 * q;
-    o_b[j] = w_row(row) * kR + 16 * q;
+    // staged columns past the tile's BNE are never read: an offset past the
+    // buffer loads zeros without a memory request
+    o_b[j] = row < BNE ? w_row(row) * kR + 16 * q : 0x80000000u;
   }
   uint32_t o_sp;
   {
@@ -950,7 +952,7 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
   // waves 0-3: backbone scale rows and weight scale columns 64 wq + l;
   // waves 4-7: residual scale rows and the same weight columns again
   const uint32_t o_sa = act_row(64 * wq + l) * kS;
-  const uint32_t o_sw = w_row(64 * wq + l) * kS;
+  const uint32_t o_sw = 64 * wq + l < BNE ? w_row(64 * wq + l) * kS : 0x80000000u;
   const int4v r_sa = w < 4 ? r_ssp : r_sdn;
 
   auto issue_main = [&](int s, Tile8Main& st) {

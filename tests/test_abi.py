@@ -90,6 +90,11 @@ def test_linear_validation_errors():
     assert lib.sharq_linear(_fake_act(K=4096), _fake_weight(K=4096, D=big_t), None, None, 8, Y, big_t, None) == \
         L.SHARQ_ERR_UNSUPPORTED_SHAPE
     assert "bytes" in lib.sharq_last_error().decode()
+    # ... and past 2 GiB: offsets with bit 31 set mark absent loads, so no
+    # buffer may reach that far
+    t2 = (1 << 32) // 4096                                 # T * K / 2 = 2 GiB
+    assert lib.sharq_linear(_fake_act(T=t2, K=4096), _fake_weight(K=4096), None, None, 8, Y, 64, None) == \
+        L.SHARQ_ERR_UNSUPPORTED_SHAPE
     # null activation buffer
     bad = _fake_act()
     bad.res_codes = None
