@@ -2,13 +2,15 @@
 // NVFP4 scaling, §3.4-§3.5 dual path with one shared weight payload).
 //
 // gfx950's scaled MFMA takes only power-of-two (E8M0) block scales, so an
-// E4M3 block scale cannot ride along.  The product of an E2M1 value (2
-// significant bits) and an E4M3 scale (4 significant bits) has at most 6
-// significant bits and is exact in bf16, so each operand element is
-// dequantized to q * dec(scale) in bf16 while staging and multiplied on the
-// bf16 MFMA (v_mfma_f32_32x32x16_bf16, exact products, fp32 accumulation).
-// (v_cvt_scalef32_pk_bf16_fp4 cannot do the dequantization: it applies only
-// the power-of-two part of its scale, measured on MI355X.)
+// E4M3 block scale cannot ride along.  An E2M1 value (2 significant bits)
+// times an E4M3 scale (4 significant bits) has at most 6 significant bits and
+// lies in [2^-10, 2688] when nonzero, so it is exact in fp16.  Each operand
+// element is therefore dequantized to q * dec(scale) in fp16 while staging
+// (one packed fp16 multiply per two values) and multiplied on the fp16 MFMA
+// (v_mfma_f32_32x32x16_f16: exact products, fp32 accumulation).
+// (v_cvt_scalef32_pk_bf16_fp4 cannot apply the whole scale: it uses only its
+// scale's power-of-two part, measured on MI355X; the conversions here take
+// scale 1.)
 // The fp32 tensor scales differ between the paths, so the backbone and the
 // residual keep one accumulator each inside the same tile and the epilogue
 // forms Y = s_w * (s_sp * acc_sp + s_dn * acc_dn).
@@ -19,43 +21,50 @@ namespace sharq {
 
 namespace {
 
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kNM = 256;                  // tile rows
 constexpr int kNN = 128;                  // tile columns
-constexpr int kKS = 32;                   // K per step (one backbone block, two residual blocks)
+constexpr int kKS = 64;                   // K per step: two halves of 32 (one backbone block, two residual blocks each)
 
-// 32x32x16 bf16: lane l holds row / column (l & 31), K-values 8 (l >> 5) .. +7
+// 32x32x16 f16: lane l holds row / column (l & 31), K-values 8 (l >> 5) .. +7
 // of the 16; result register i of lane l is row 8 (i / 4) + 4 (l >> 5) + i % 4,
 // column l & 31
-SHARQ_DEV v16f mfma_bf16(uint4 a, uint4 b, v16f c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+SHARQ_DEV v16f mfma_f16(uint4 a, uint4 b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
 }
 
-// 8 E2M1 codes (one 32-bit word) times dec -> 8 bf16 (exact: q * dec has <= 6 significant bits)
-SHARQ_DEV uint4 dequant8_bf16(uint32_t word, float dec) {
-  const v2f p0 = dq_fp4x2<0>(word, 1.0f), p1 = dq_fp4x2<1>(word, 1.0f);
-  const v2f p2 = dq_fp4x2<2>(word, 1.0f), p3 = dq_fp4x2<3>(word, 1.0f);
-  const float v[8] = {p0.x * dec, p0.y * dec, p1.x * dec, p1.y * dec, p2.x * dec, p2.y * dec, p3.x * dec, p3.y * dec};
-  uint32_t o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)   // exact values: the bf16 pattern is the upper half of the fp32 pattern
-    o[i] = __builtin_amdgcn_perm(__float_as_uint(v[2 * i + 1]), __float_as_uint(v[2 * i]), 0x07060302u);
-  return make_uint4(o[0], o[1], o[2], o[3]);
+// dec(E4M3 code) as a pair of fp16 (exact: every E4M3 value is an fp16 normal)
+SHARQ_DEV v2h dec_h2(uint32_t code) {
+  const _Float16 d = (_Float16)e4m3_decode(code);
+  return (v2h){d, d};
 }
 
-// 16-byte chunk q (0..3, 8 bf16) of a staged 64-byte row.  A 16-byte LDS
-// access is served 16 lanes at a time over 256 bytes of banks; 16
-// consecutive rows at one chunk land on 4 (row & 3) x 4 (q ^ ((row >> 2) & 3))
-// distinct 16-byte bank groups, so reads and writes are conflict-free
-SHARQ_DEV int nslot(int row, int q) { return row * 4 + (q ^ ((row >> 2) & 3)); }
+// 8 E2M1 codes (one 32-bit word) times dec -> 8 fp16 (exact, see above)
+SHARQ_DEV uint4 dequant8_f16(uint32_t word, v2h dec) {
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 0) * dec;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 1) * dec;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 2) * dec;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, 1.0f, 3) * dec;
+  return make_uint4(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                    __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3));
+}
+
+// 16-byte chunk q (0..7, 8 fp16) of a staged 128-byte row.  A 16-byte LDS
+// access is served 16 lanes at a time over 256 bytes of banks.  Sixteen
+// consecutive rows (from a multiple of 16) at one chunk land on 2 (row & 1) x
+// 8 (q ^ ((row >> 1) & 7)) distinct 16-byte bank groups, and so do the
+// staging writes (8 rows x the two halves' chunks 4 h + i), so reads and
+// writes are conflict-free
+SHARQ_DEV int nslot(int row, int q) { return row * 8 + (q ^ ((row >> 1) & 7)); }
 
 struct NvStage {
-  uint4 a_sp[kNM * 4];        // backbone, bf16, 64 B per row
-  uint4 a_dn[kNM * 4];        // residual
-  uint4 b[kNN * 4];           // weight columns
-};
+  uint4 a_sp[kNM * 8];        // backbone, fp16, 128 B per row
+  uint4 a_dn[kNM * 8];        // residual
+  uint4 b[kNN * 8];           // weight columns
+};                            // 80 KB; two stages fill the 160 KB of LDS
 
 // expand 4 groups (8 compacted bytes + 4 metadata nibbles) into 16 code bytes
 SHARQ_DEV uint4 expand4(uint32_t c_lo, uint32_t c_hi, uint32_t meta16) {
@@ -72,16 +81,18 @@ SHARQ_DEV uint4 expand4(uint32_t c_lo, uint32_t c_hi, uint32_t meta16) {
 
 // Tile 256 x 128, four waves (one per SIMD): wave w covers rows 64 w ..
 // and all 128 columns, with one accumulator per path (the two paths have
-// different tensor scales), 256 accumulator registers.  K advances 32 per step.
+// different tensor scales), 256 accumulator registers.  K advances 64 per step.
 //
-// Staging (no DMA: operands are dequantized on the way): every thread owns
-// one backbone row and one residual row of the tile, threads 0-127 also one
-// weight column; per step a thread loads its rows' 32 values (raw buffer
-// loads; rows and columns outside the tile read row 0, whose products reach
-// only outputs that are never stored), dequantizes them to bf16 and writes
-// 16-byte chunks to LDS.  Loads run two steps ahead; the dequantization of
-// step s+1 comes after step s's fragment reads so that it can fill the
-// shadow of step s's MFMAs.
+// Staging (no DMA: operands are dequantized on the way).  A step's row of 64
+// values is split in two halves of 32 (one backbone scale block, two
+// residual ones); thread t stages half t & 1 of tile rows t >> 1 and
+// 128 + (t >> 1) and of weight column t >> 1, so the two lanes of a row read
+// adjacent bytes and one load instruction covers 32 rows.  Per step a thread
+// loads its halves (raw buffer loads; rows and columns outside the tile read
+// row 0, whose products reach only outputs that are never stored),
+// dequantizes them to fp16 and writes 16-byte chunks to LDS.  Loads run two
+// steps ahead; the dequantization of step s+1 comes after step s's fragment
+// reads so that it can fill the shadow of step s's MFMAs.
 __global__ __launch_bounds__(256, 1) void linear_nv_tile(
     const uint8_t* __restrict__ bb_codes, const uint8_t* __restrict__ bb_meta, const uint8_t* __restrict__ bb_scale,
     const uint8_t* __restrict__ res_codes, const uint8_t* __restrict__ res_scale, const float* __restrict__ a_ts,
@@ -108,57 +119,67 @@ __global__ __launch_bounds__(256, 1) void linear_nv_tile(
   const __amdgpu_buffer_rsrc_t r_rs = rsrc(res_scale, (int64_t)an * kS16);
   const __amdgpu_buffer_rsrc_t r_w = rsrc(payload, (int64_t)D * kR), r_ws = rsrc(wscale, (int64_t)D * kS32);
 
-  // ---- staging roles
-  const bool b_role = w < 2;                           // waves 0-1: also weight columns (uniform)
-  const int srow = tid;
-  const int gr = m0 + srow;
-  const uint32_t ar = gr < rows ? (uint32_t)gather_row(row_index, gr, act_rows) : 0u;
-  const int gc = n0 + (tid & 127);
+  // ---- staging roles: half h of rows srow[0], srow[1] and of column scol
+  const uint32_t h = tid & 1;
+  const int srow[2] = {tid >> 1, 128 + (tid >> 1)}, scol = tid >> 1;
+  uint32_t ar[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int gr = m0 + srow[j];
+    ar[j] = gr < rows ? (uint32_t)gather_row(row_index, gr, act_rows) : 0u;
+  }
+  const int gc = n0 + scol;
   const uint32_t wc = gc < D ? (uint32_t)gc : 0u;
 
-  struct Ld {
-    uint2 bc;            // backbone: compacted codes of 4 groups
+  struct LdA {
+    uint2 bc;            // backbone: compacted codes of the half's 4 groups
     uint32_t bm, bsc;    // backbone metadata (16 bits), scale byte
     uint4 rc;            // residual codes (16 B)
     uint32_t rsc;        // residual: two scale bytes
-    uint4 wcd;           // weight codes
+  };
+  struct Ld {
+    LdA a[2];
+    uint4 wcd;           // weight codes (16 B)
     uint32_t wsc;        // weight scale byte
   };
   auto load = [&](int s, Ld& L) {
     const uint32_t ss = (uint32_t)min(s, KS - 1);      // past the end: reload the last step (unused)
-    const auto c = __builtin_amdgcn_raw_buffer_load_b64(r_bc, ar * kA + 8u * ss, 0, 0);
-    L.bc = make_uint2(c[0], c[1]);
-    L.bm = __builtin_amdgcn_raw_buffer_load_b16(r_bm, ar * kM + 2u * ss, 0, 0);
-    L.bsc = __builtin_amdgcn_raw_buffer_load_b8(r_bs, ar * kS32 + ss, 0, 0);
-    const auto r = __builtin_amdgcn_raw_buffer_load_b128(r_rc, ar * kR + 16u * ss, 0, 0);
-    L.rc = make_uint4(r[0], r[1], r[2], r[3]);
-    L.rsc = __builtin_amdgcn_raw_buffer_load_b16(r_rs, ar * kS16 + 2u * ss, 0, 0);
-    if (b_role) {
-      const auto b = __builtin_amdgcn_raw_buffer_load_b128(r_w, wc * kR + 16u * ss, 0, 0);
-      L.wcd = make_uint4(b[0], b[1], b[2], b[3]);
-      L.wsc = __builtin_amdgcn_raw_buffer_load_b8(r_ws, wc * kS32 + ss, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const auto c = __builtin_amdgcn_raw_buffer_load_b64(r_bc, ar[j] * kA + 16u * ss + 8u * h, 0, 0);
+      L.a[j].bc = make_uint2(c[0], c[1]);
+      L.a[j].bm = __builtin_amdgcn_raw_buffer_load_b16(r_bm, ar[j] * kM + 4u * ss + 2u * h, 0, 0);
+      L.a[j].bsc = __builtin_amdgcn_raw_buffer_load_b8(r_bs, ar[j] * kS32 + 2u * ss + h, 0, 0);
+      const auto r = __builtin_amdgcn_raw_buffer_load_b128(r_rc, ar[j] * kR + 32u * ss + 16u * h, 0, 0);
+      L.a[j].rc = make_uint4(r[0], r[1], r[2], r[3]);
+      L.a[j].rsc = __builtin_amdgcn_raw_buffer_load_b16(r_rs, ar[j] * kS16 + 4u * ss + 2u * h, 0, 0);
     }
+    const auto b = __builtin_amdgcn_raw_buffer_load_b128(r_w, wc * kR + 32u * ss + 16u * h, 0, 0);
+    L.wcd = make_uint4(b[0], b[1], b[2], b[3]);
+    L.wsc = __builtin_amdgcn_raw_buffer_load_b8(r_ws, wc * kS32 + 2u * ss + h, 0, 0);
   };
   auto store = [&](const Ld& L, NvStage& S) {
-    const uint4 e = expand4(L.bc.x, L.bc.y, L.bm);
-    const float dec = e4m3_decode(L.bsc & 0xFFu);
-    S.a_sp[nslot(srow, 0)] = dequant8_bf16(e.x, dec);
-    S.a_sp[nslot(srow, 1)] = dequant8_bf16(e.y, dec);
-    S.a_sp[nslot(srow, 2)] = dequant8_bf16(e.z, dec);
-    S.a_sp[nslot(srow, 3)] = dequant8_bf16(e.w, dec);
-    const float d0 = e4m3_decode(L.rsc & 0xFFu), d1 = e4m3_decode((L.rsc >> 8) & 0xFFu);
-    S.a_dn[nslot(srow, 0)] = dequant8_bf16(L.rc.x, d0);
-    S.a_dn[nslot(srow, 1)] = dequant8_bf16(L.rc.y, d0);
-    S.a_dn[nslot(srow, 2)] = dequant8_bf16(L.rc.z, d1);
-    S.a_dn[nslot(srow, 3)] = dequant8_bf16(L.rc.w, d1);
-    if (b_role) {
-      const float db = e4m3_decode(L.wsc & 0xFFu);
-      const int cc = tid & 127;
-      S.b[nslot(cc, 0)] = dequant8_bf16(L.wcd.x, db);
-      S.b[nslot(cc, 1)] = dequant8_bf16(L.wcd.y, db);
-      S.b[nslot(cc, 2)] = dequant8_bf16(L.wcd.z, db);
-      S.b[nslot(cc, 3)] = dequant8_bf16(L.wcd.w, db);
+    const int q0 = 4 * (int)h;                         // the half's first 16-byte chunk
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const LdA& A = L.a[j];
+      const uint4 e = expand4(A.bc.x, A.bc.y, A.bm);
+      const v2h dec = dec_h2(A.bsc & 0xFFu);
+      S.a_sp[nslot(srow[j], q0 + 0)] = dequant8_f16(e.x, dec);
+      S.a_sp[nslot(srow[j], q0 + 1)] = dequant8_f16(e.y, dec);
+      S.a_sp[nslot(srow[j], q0 + 2)] = dequant8_f16(e.z, dec);
+      S.a_sp[nslot(srow[j], q0 + 3)] = dequant8_f16(e.w, dec);
+      const v2h d0 = dec_h2(A.rsc & 0xFFu), d1 = dec_h2((A.rsc >> 8) & 0xFFu);
+      S.a_dn[nslot(srow[j], q0 + 0)] = dequant8_f16(A.rc.x, d0);
+      S.a_dn[nslot(srow[j], q0 + 1)] = dequant8_f16(A.rc.y, d0);
+      S.a_dn[nslot(srow[j], q0 + 2)] = dequant8_f16(A.rc.z, d1);
+      S.a_dn[nslot(srow[j], q0 + 3)] = dequant8_f16(A.rc.w, d1);
     }
+    const v2h db = dec_h2(L.wsc & 0xFFu);
+    S.b[nslot(scol, q0 + 0)] = dequant8_f16(L.wcd.x, db);
+    S.b[nslot(scol, q0 + 1)] = dequant8_f16(L.wcd.y, db);
+    S.b[nslot(scol, q0 + 2)] = dequant8_f16(L.wcd.z, db);
+    S.b[nslot(scol, q0 + 3)] = dequant8_f16(L.wcd.w, db);
   };
 
   // ---- MFMA fragments and accumulators
@@ -173,35 +194,39 @@ __global__ __launch_bounds__(256, 1) void linear_nv_tile(
       acc_dn[f][n] = (v16f){};
     }
   struct Frag {
-    uint4 sp[2][2], dn[2][2], b[2][4];   // [k-slice][f or n]
+    uint4 sp[2], dn[2], b[4];   // [f or n] of one 16-wide K slice
   };
-  auto read = [&](const NvStage& S, Frag& F) {
+  auto read = [&](const NvStage& S, int ks, Frag& F) {
+    const int q = 2 * ks + kh;                         // chunk: K-values 8 q .. 8 q + 7
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int q = 2 * ks + kh;                       // chunk: K-values 8 q .. 8 q + 7
-#pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        F.sp[ks][f] = S.a_sp[nslot(wm0 + 32 * f + lr, q)];
-        F.dn[ks][f] = S.a_dn[nslot(wm0 + 32 * f + lr, q)];
-      }
-#pragma unroll
-      for (int n = 0; n < 4; ++n) F.b[ks][n] = S.b[nslot(32 * n + lr, q)];
+    for (int f = 0; f < 2; ++f) {
+      F.sp[f] = S.a_sp[nslot(wm0 + 32 * f + lr, q)];
+      F.dn[f] = S.a_dn[nslot(wm0 + 32 * f + lr, q)];
     }
+#pragma unroll
+    for (int n = 0; n < 4; ++n) F.b[n] = S.b[nslot(32 * n + lr, q)];
   };
   auto mfma = [&](const Frag& F) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
+      for (int n = 0; n < 4; ++n) {
+        acc_sp[f][n] = mfma_f16(F.sp[f], F.b[n], acc_sp[f][n]);
+        acc_dn[f][n] = mfma_f16(F.dn[f], F.b[n], acc_dn[f][n]);
+      }
+  };
+  // one step: fragments of the four K slices of stage S, then (behind the
+  // first slice's reads) the staging of the next step into N
+  auto step = [&](const NvStage& S, const Ld& Lnext, NvStage& N) {
+    Frag fr[4];
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          acc_sp[f][n] = mfma_bf16(F.sp[ks][f], F.b[ks][n], acc_sp[f][n]);
-          acc_dn[f][n] = mfma_bf16(F.dn[ks][f], F.b[ks][n], acc_dn[f][n]);
-        }
+    for (int ks = 0; ks < 4; ++ks) read(S, ks, fr[ks]);
+    store(Lnext, N);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) mfma(fr[ks]);
   };
 
   Ld l0, l1;
-  Frag fr;
   load(0, l0);
   load(1, l1);
   store(l0, st[0]);
@@ -210,15 +235,11 @@ __global__ __launch_bounds__(256, 1) void linear_nv_tile(
   for (int s = 0; s < KS; s += 2) {
     // step s: st[0] holds step s, st[1] receives step s+1
     load(s + 2, l0);
-    read(st[0], fr);
-    store(l1, st[1]);
-    mfma(fr);
+    step(st[0], l1, st[1]);
     __syncthreads();
     // step s+1
     load(s + 3, l1);
-    read(st[1], fr);
-    store(l0, st[0]);
-    mfma(fr);
+    step(st[1], l0, st[0]);
     __syncthreads();
   }
 
