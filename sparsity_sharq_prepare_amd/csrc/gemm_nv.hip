@@ -224,6 +224,14 @@ __global__ __launch_bounds__(256, 1) void linear_nv_tile(
     store(Lnext, N);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) mfma(fr[ks]);
+    // one wave per SIMD: interleave the staging's VALU work and LDS writes
+    // with the MFMAs so that it runs in their shadow
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      if (i % 3 == 0) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
   };
 
   Ld l0, l1;
