@@ -351,6 +351,38 @@ SHARQ_DEV float nv_scaled(float v, float d) {
   return fminf(fmaxf(t, -6.0f), 6.0f);          // saturation (|t| <= 6 is left exact)
 }
 
+// E2M1 codes (one 32-bit word, value i in nibble i) of fl(v[i] / d) under
+// nv_scaled.  Fast path: with r = rcp(d) (within 1 ulp of 1/d), the products
+// v * fl(r (1 - 2^-20)) and v * fl(r (1 + 2^-20)) bracket fl(v / d) strictly
+// (three roundings and the reciprocal's error stay below 2^-21 relative), and
+// clamping and E2M1 rounding are monotonic, so when both brackets give the
+// same codes those are the codes of fl(v / d).  They differ only within about
+// 2^-20 of an E2M1 rounding midpoint (or for non-normal d); then the group
+// takes the correctly rounded division.
+SHARQ_DEV uint32_t nv_codes8(const float v[8], float d) {
+  if (d >= 0x1p-125f && d <= 0x1p125f) {
+    const float r = __builtin_amdgcn_rcpf(d);
+    const float rl = __fmul_rn(r, 1.0f - 0x1p-20f), rh = __fmul_rn(r, 1.0f + 0x1p-20f);
+    auto cl = [](float t) { return fminf(fmaxf(t, -6.0f), 6.0f); };
+    uint32_t lo = 0, hi = 0;
+    lo = cvt_fp4x2<0>(lo, cl(__fmul_rn(v[0], rl)), cl(__fmul_rn(v[1], rl)), 1.0f);
+    lo = cvt_fp4x2<1>(lo, cl(__fmul_rn(v[2], rl)), cl(__fmul_rn(v[3], rl)), 1.0f);
+    lo = cvt_fp4x2<2>(lo, cl(__fmul_rn(v[4], rl)), cl(__fmul_rn(v[5], rl)), 1.0f);
+    lo = cvt_fp4x2<3>(lo, cl(__fmul_rn(v[6], rl)), cl(__fmul_rn(v[7], rl)), 1.0f);
+    hi = cvt_fp4x2<0>(hi, cl(__fmul_rn(v[0], rh)), cl(__fmul_rn(v[1], rh)), 1.0f);
+    hi = cvt_fp4x2<1>(hi, cl(__fmul_rn(v[2], rh)), cl(__fmul_rn(v[3], rh)), 1.0f);
+    hi = cvt_fp4x2<2>(hi, cl(__fmul_rn(v[4], rh)), cl(__fmul_rn(v[5], rh)), 1.0f);
+    hi = cvt_fp4x2<3>(hi, cl(__fmul_rn(v[6], rh)), cl(__fmul_rn(v[7], rh)), 1.0f);
+    if (lo == hi) return lo;
+  }
+  uint32_t w = 0;
+  w = cvt_fp4x2<0>(w, nv_scaled(v[0], d), nv_scaled(v[1], d), 1.0f);
+  w = cvt_fp4x2<1>(w, nv_scaled(v[2], d), nv_scaled(v[3], d), 1.0f);
+  w = cvt_fp4x2<2>(w, nv_scaled(v[4], d), nv_scaled(v[5], d), 1.0f);
+  w = cvt_fp4x2<3>(w, nv_scaled(v[6], d), nv_scaled(v[7], d), 1.0f);
+  return w;
+}
+
 // max over the WG of per-thread values (non-negative), written to out[blockIdx.x]
 SHARQ_DEV void block_max_store(float v, float* out, float* lds) {
 #pragma unroll
@@ -453,11 +485,7 @@ __global__ __launch_bounds__(256) void prepare_nv_phase23(const void* __restrict
     const uint32_t sc_b = e4m3_encode(__fdiv_rn(__fdiv_rn(bamax, 6.0f), s_sp));
     const float dec_b = e4m3_decode(sc_b);
     const float d_b = __fmul_rn(dec_b, s_sp);
-    uint32_t bw = 0;
-    bw = cvt_fp4x2<0>(bw, nv_scaled(y[0], d_b), nv_scaled(y[1], d_b), 1.0f);
-    bw = cvt_fp4x2<1>(bw, nv_scaled(y[2], d_b), nv_scaled(y[3], d_b), 1.0f);
-    bw = cvt_fp4x2<2>(bw, nv_scaled(y[4], d_b), nv_scaled(y[5], d_b), 1.0f);
-    bw = cvt_fp4x2<3>(bw, nv_scaled(y[6], d_b), nv_scaled(y[7], d_b), 1.0f);
+    const uint32_t bw = nv_codes8(y, d_b);
     float R[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -482,11 +510,7 @@ __global__ __launch_bounds__(256) void prepare_nv_phase23(const void* __restrict
       rmax = fmaxf(rmax, shfl_xor_f(rmax, 1));
       const uint32_t sc_r = e4m3_encode(__fdiv_rn(__fdiv_rn(rmax, 6.0f), s_dn));
       const float d_r = __fmul_rn(e4m3_decode(sc_r), s_dn);
-      uint32_t rw = 0;
-      rw = cvt_fp4x2<0>(rw, nv_scaled(R[0], d_r), nv_scaled(R[1], d_r), 1.0f);
-      rw = cvt_fp4x2<1>(rw, nv_scaled(R[2], d_r), nv_scaled(R[3], d_r), 1.0f);
-      rw = cvt_fp4x2<2>(rw, nv_scaled(R[4], d_r), nv_scaled(R[5], d_r), 1.0f);
-      rw = cvt_fp4x2<3>(rw, nv_scaled(R[6], d_r), nv_scaled(R[7], d_r), 1.0f);
+      const uint32_t rw = nv_codes8(R, d_r);
       if (ok) {
         *reinterpret_cast<uint32_t*>(res_codes + r * (K >> 1) + 4 * (int64_t)g) = rw;
         if ((g & 1) == 0) res_scale[r * (K >> 4) + (g >> 1)] = (uint8_t)sc_r;

@@ -71,6 +71,34 @@ def test_prepare_edge_rows(fmt):
     compare_act(act, O.prepare(x, g, 1e-6, fmt))
 
 
+def test_prepare_nvfp4_code_midpoints():
+    # NVFP4 element codes at and next to the E2M1 rounding midpoints, where the
+    # kernel's reciprocal-based fast path must defer to the correctly rounded
+    # division: x = 2688 somewhere makes the backbone tensor scale exactly 1,
+    # each 32-block's maximum 6 * 2^j makes its scale 2^j exactly, and the other
+    # values sit on midpoints (and grid points) times 2^j, moved by 0, +-1,
+    # +-2, +-4, +-8 and +-64 ulp
+    rng = np.random.default_rng(7)
+    T, K = 16, 512
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0], np.float32)
+    steps = np.array([0, 1, -1, 2, -2, 4, -4, 8, -8, 64, -64], np.int32)
+    base = mids[rng.integers(0, len(mids), (T, K))]
+    bits = base.view(np.int32) + steps[rng.integers(0, len(steps), (T, K))]
+    x = bits.view(np.float32) * np.where(rng.random((T, K)) < 0.5, -1, 1).astype(np.float32)
+    j = rng.integers(-6, 7, (T, K // 32)).astype(np.float32)
+    x = x * np.repeat(np.exp2(j), 32, axis=1).astype(np.float32)
+    x[:, ::32] = np.float32(6.0) * np.exp2(j).astype(np.float32)       # block maxima
+    x[0, 0] = np.float32(2688.0)                                        # tensor amax
+    x = x.astype(np.float32)
+    case = synth.LinearCase("midpoints", "nvfp4", "f32", T, K, 8, x, None, np.zeros((K, 8), np.float32))
+    act = ops.prepare(dev_x(case), None, 1e-6, "nvfp4")
+    ref = O.prepare(x, None, 1e-6, "nvfp4")
+    compare_act(act, ref)
+    # the construction reaches the intended scales: the backbone tensor scale
+    # is exactly 1
+    assert ref["tensor_scales"][0] == np.float32(1.0)
+
+
 DECODE_IDS = [f"{K}x{D}" for K, D in synth.DECODE_SHAPES]
 NVFP4_IDS = [f"{K}x{D}" for K, D in synth.NVFP4_SHAPES]
 
