@@ -31,7 +31,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA
-BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense 16-bit MFMA (bf16 and fp16 alike)
 METRIC = "SharQ linear TFLOPS-eff + tokens/s at Llama-3.1-8B shapes; % HBM/MFMA peak"
 
 
@@ -529,7 +529,7 @@ def main():
     out = {
         "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOPS-eff", "n_gpus": 1, "steps": n_steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "mxfp4" if args.workload != "nvfp4" else "nvfp4-emu(bf16 mfma)",
+        "vs_baseline": None, "dtype": "mxfp4" if args.workload != "nvfp4" else "nvfp4-emu(fp16 mfma)",
         "data": "synthetic",
         "config": {"workload": {"decode": "llama3.1-8b decode linears, T=8, (4096x4096, 4096x14336, 14336x4096), MXFP4",
                                 "prefill": "llama3.1-8b prefill linear 4096x4096x14336, MXFP4",
