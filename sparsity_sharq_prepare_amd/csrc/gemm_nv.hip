@@ -79,21 +79,21 @@ SHARQ_DEV uint4 expand4(uint32_t c_lo, uint32_t c_hi, uint32_t meta16) {
 
 }  // namespace
 
-// Tile 256 x 128, four waves (one per SIMD): wave w covers rows 64 w ..
+// Tile 256 x 128, eight waves (two per SIMD): wave w covers rows 32 w ..
 // and all 128 columns, with one accumulator per path (the two paths have
-// different tensor scales), 256 accumulator registers.  K advances 64 per step.
+// different tensor scales), 128 accumulator registers.  K advances 64 per step.
 //
 // Staging (no DMA: operands are dequantized on the way).  A step's row of 64
 // values is split in two halves of 32 (one backbone scale block, two
-// residual ones); thread t stages half t & 1 of tile rows t >> 1 and
-// 128 + (t >> 1) and of weight column t >> 1, so the two lanes of a row read
-// adjacent bytes and one load instruction covers 32 rows.  Per step a thread
+// residual ones); thread t stages half t & 1 of tile row t >> 1, and
+// threads below 256 also of weight column t >> 1, so the two lanes of a row
+// read adjacent bytes and one load instruction covers 32 rows.  Per step a thread
 // loads its halves (raw buffer loads; rows and columns outside the tile read
 // row 0, whose products reach only outputs that are never stored),
 // dequantizes them to fp16 and writes 16-byte chunks to LDS.  Loads run two
 // steps ahead; the dequantization of step s+1 comes after step s's fragment
 // reads so that it can fill the shadow of step s's MFMAs.
-__global__ __launch_bounds__(256, 1) void linear_nv_tile(
+__global__ __launch_bounds__(512, 1) void linear_nv_tile(
     const uint8_t* __restrict__ bb_codes, const uint8_t* __restrict__ bb_meta, const uint8_t* __restrict__ bb_scale,
     const uint8_t* __restrict__ res_codes, const uint8_t* __restrict__ res_scale, const float* __restrict__ a_ts,
     const int32_t* __restrict__ row_index, int rows, int act_rows, int K, const uint8_t* __restrict__ payload,
@@ -119,14 +119,14 @@ __global__ __launch_bounds__(256, 1) void linear_nv_tile(
   const __amdgpu_buffer_rsrc_t r_rs = rsrc(res_scale, (int64_t)an * kS16);
   const __amdgpu_buffer_rsrc_t r_w = rsrc(payload, (int64_t)D * kR), r_ws = rsrc(wscale, (int64_t)D * kS32);
 
-  // ---- staging roles: half h of rows srow[0], srow[1] and of column scol
+  // ---- staging roles: half h of row srow and (waves 0-3) of column scol
   const uint32_t h = tid & 1;
-  const int srow[2] = {tid >> 1, 128 + (tid >> 1)}, scol = tid >> 1;
-  uint32_t ar[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int gr = m0 + srow[j];
-    ar[j] = gr < rows ? (uint32_t)gather_row(row_index, gr, act_rows) : 0u;
+  const bool b_role = w < 4;                           // uniform per wave
+  const int srow[1] = {tid >> 1}, scol = (tid >> 1) & 127;
+  uint32_t ar[1];
+  {
+    const int gr = m0 + srow[0];
+    ar[0] = gr < rows ? (uint32_t)gather_row(row_index, gr, act_rows) : 0u;
   }
   const int gc = n0 + scol;
   const uint32_t wc = gc < D ? (uint32_t)gc : 0u;
@@ -138,14 +138,14 @@ __global__ __launch_bounds__(256, 1) void linear_nv_tile(
     uint32_t rsc;        // residual: two scale bytes
   };
   struct Ld {
-    LdA a[2];
+    LdA a[1];
     uint4 wcd;           // weight codes (16 B)
     uint32_t wsc;        // weight scale byte
   };
   auto load = [&](int s, Ld& L) {
     const uint32_t ss = (uint32_t)min(s, KS - 1);      // past the end: reload the last step (unused)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 1; ++j) {
       const auto c = __builtin_amdgcn_raw_buffer_load_b64(r_bc, ar[j] * kA + 16u * ss + 8u * h, 0, 0);
       L.a[j].bc = make_uint2(c[0], c[1]);
       L.a[j].bm = __builtin_amdgcn_raw_buffer_load_b16(r_bm, ar[j] * kM + 4u * ss + 2u * h, 0, 0);
@@ -154,14 +154,16 @@ __global__ __launch_bounds__(256, 1) void linear_nv_tile(
       L.a[j].rc = make_uint4(r[0], r[1], r[2], r[3]);
       L.a[j].rsc = __builtin_amdgcn_raw_buffer_load_b16(r_rs, ar[j] * kS16 + 4u * ss + 2u * h, 0, 0);
     }
-    const auto b = __builtin_amdgcn_raw_buffer_load_b128(r_w, wc * kR + 32u * ss + 16u * h, 0, 0);
-    L.wcd = make_uint4(b[0], b[1], b[2], b[3]);
-    L.wsc = __builtin_amdgcn_raw_buffer_load_b8(r_ws, wc * kS32 + 2u * ss + h, 0, 0);
+    if (b_role) {
+      const auto b = __builtin_amdgcn_raw_buffer_load_b128(r_w, wc * kR + 32u * ss + 16u * h, 0, 0);
+      L.wcd = make_uint4(b[0], b[1], b[2], b[3]);
+      L.wsc = __builtin_amdgcn_raw_buffer_load_b8(r_ws, wc * kS32 + 2u * ss + h, 0, 0);
+    }
   };
   auto store = [&](const Ld& L, NvStage& S) {
     const int q0 = 4 * (int)h;                         // the half's first 16-byte chunk
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 1; ++j) {
       const LdA& A = L.a[j];
       const uint4 e = expand4(A.bc.x, A.bc.y, A.bm);
       const v2h dec = dec_h2(A.bsc & 0xFFu);
@@ -175,31 +177,33 @@ __global__ __launch_bounds__(256, 1) void linear_nv_tile(
       S.a_dn[nslot(srow[j], q0 + 2)] = dequant8_f16(A.rc.z, d1);
       S.a_dn[nslot(srow[j], q0 + 3)] = dequant8_f16(A.rc.w, d1);
     }
-    const v2h db = dec_h2(L.wsc & 0xFFu);
-    S.b[nslot(scol, q0 + 0)] = dequant8_f16(L.wcd.x, db);
-    S.b[nslot(scol, q0 + 1)] = dequant8_f16(L.wcd.y, db);
-    S.b[nslot(scol, q0 + 2)] = dequant8_f16(L.wcd.z, db);
-    S.b[nslot(scol, q0 + 3)] = dequant8_f16(L.wcd.w, db);
+    if (b_role) {
+      const v2h db = dec_h2(L.wsc & 0xFFu);
+      S.b[nslot(scol, q0 + 0)] = dequant8_f16(L.wcd.x, db);
+      S.b[nslot(scol, q0 + 1)] = dequant8_f16(L.wcd.y, db);
+      S.b[nslot(scol, q0 + 2)] = dequant8_f16(L.wcd.z, db);
+      S.b[nslot(scol, q0 + 3)] = dequant8_f16(L.wcd.w, db);
+    }
   };
 
   // ---- MFMA fragments and accumulators
-  const int wm0 = w * 64;
+  const int wm0 = w * 32;
   const int kh = l >> 5, lr = l & 31;
-  v16f acc_sp[2][4], acc_dn[2][4];
+  v16f acc_sp[1][4], acc_dn[1][4];
 #pragma unroll
-  for (int f = 0; f < 2; ++f)
+  for (int f = 0; f < 1; ++f)
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       acc_sp[f][n] = (v16f){};
       acc_dn[f][n] = (v16f){};
     }
   struct Frag {
-    uint4 sp[2], dn[2], b[4];   // [f or n] of one 16-wide K slice
+    uint4 sp[1], dn[1], b[4];   // [f or n] of one 16-wide K slice
   };
   auto read = [&](const NvStage& S, int ks, Frag& F) {
     const int q = 2 * ks + kh;                         // chunk: K-values 8 q .. 8 q + 7
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
+    for (int f = 0; f < 1; ++f) {
       F.sp[f] = S.a_sp[nslot(wm0 + 32 * f + lr, q)];
       F.dn[f] = S.a_dn[nslot(wm0 + 32 * f + lr, q)];
     }
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(256, 1) void linear_nv_tile(
   };
   auto mfma = [&](const Frag& F) {
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int f = 0; f < 1; ++f)
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         acc_sp[f][n] = mfma_f16(F.sp[f], F.b[n], acc_sp[f][n]);
@@ -218,21 +222,24 @@ __global__ __launch_bounds__(256, 1) void linear_nv_tile(
   // one step: fragments of the four K slices of stage S, then (behind the
   // first slice's reads) the staging of the next step into N
   auto step = [&](const NvStage& S, const Ld& Lnext, NvStage& N) {
-    Frag fr[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) read(S, ks, fr[ks]);
+    Frag fr[2];
+    read(S, 0, fr[0]);
     store(Lnext, N);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) mfma(fr[ks]);
-    // one wave per SIMD: interleave the staging's VALU work and LDS writes
-    // with the MFMAs so that it runs in their shadow
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks + 1 < 4) read(S, ks + 1, fr[(ks + 1) & 1]);
+      mfma(fr[ks & 1]);
+    }
+    // interleave the staging's VALU work and LDS writes with the MFMAs so
+    // that it runs in their shadow
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
+    for (int i = 0; i < 32; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       if (i % 3 == 0) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
     }
   };
+
 
   Ld l0, l1;
   load(0, l0);
@@ -254,7 +261,7 @@ __global__ __launch_bounds__(256, 1) void linear_nv_tile(
   // ---- epilogue: Y = s_w * (s_sp * acc_sp + s_dn * acc_dn)
   const float s_sp = a_ts[0], s_dn = a_ts[1], s_w = w_ts[0];
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
+  for (int f = 0; f < 1; ++f) {
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
       const int c = n0 + 32 * n + lr;
@@ -274,7 +281,7 @@ hipError_t launch_linear_nv(const uint8_t* bb_codes, const uint8_t* bb_meta, con
                             const uint8_t* wscale, const float* w_ts, int D, float* Y, int64_t ldy, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const int nt = ((rows + kNM - 1) / kNM) * ((D + kNN - 1) / kNN);
-  hipLaunchKernelGGL(linear_nv_tile, dim3(nt), dim3(256), 0, s, bb_codes, bb_meta, bb_scale, res_codes, res_scale,
+  hipLaunchKernelGGL(linear_nv_tile, dim3(nt), dim3(512), 0, s, bb_codes, bb_meta, bb_scale, res_codes, res_scale,
                      a_ts, row_index, rows, act_rows, K, payload, wscale, w_ts, D, Y, ldy);
   return hipGetLastError();
 }
