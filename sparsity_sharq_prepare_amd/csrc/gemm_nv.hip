@@ -91,8 +91,8 @@ SHARQ_DEV uint4 expand4(uint32_t c_lo, uint32_t c_hi, uint32_t meta16) {
 // loads its halves (raw buffer loads; rows and columns outside the tile read
 // row 0, whose products reach only outputs that are never stored),
 // dequantizes them to fp16 and writes 16-byte chunks to LDS.  Loads run two
-// steps ahead; the dequantization of step s+1 comes after step s's fragment
-// reads so that it can fill the shadow of step s's MFMAs.
+// steps ahead.  The two waves of a SIMD overlap one's staging with the
+// other's MFMAs (measured faster than interleaving them by schedule hints).
 __global__ __launch_bounds__(512, 1) void linear_nv_tile(
     const uint8_t* __restrict__ bb_codes, const uint8_t* __restrict__ bb_meta, const uint8_t* __restrict__ bb_scale,
     const uint8_t* __restrict__ res_codes, const uint8_t* __restrict__ res_scale, const float* __restrict__ a_ts,
@@ -230,16 +230,7 @@ __global__ __launch_bounds__(512, 1) void linear_nv_tile(
       if (ks + 1 < 4) read(S, ks + 1, fr[(ks + 1) & 1]);
       mfma(fr[ks & 1]);
     }
-    // interleave the staging's VALU work and LDS writes with the MFMAs so
-    // that it runs in their shadow
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      if (i % 3 == 0) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-    }
   };
-
 
   Ld l0, l1;
   load(0, l0);
