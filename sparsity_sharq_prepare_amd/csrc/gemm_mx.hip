@@ -574,6 +574,50 @@ struct TileFrag {
 
 }  // namespace
 
+// Grouped tiles: tile `bid` of the concatenation, over experts in order, of
+// each expert's ceil(rows_e / BM) x tiles_n tiles.  Every thread below 256
+// loads one expert's offsets (coalesced), tile counts are prefix-summed
+// across the workgroup in `scan` (256 ints of LDS), and the thread whose
+// range holds the tile publishes it through `hit` (4 ints of LDS).  Needs at
+// least 256 threads; all threads must call it.  Returns false for a surplus
+// workgroup (uniform).
+SHARQ_DEV bool find_group_tile(int bid, int n_groups, const int32_t* __restrict__ group_offsets, int rows, int BM,
+                               int tiles_n, int* scan, int* hit, int& expert, int& start, int& count, int& tile) {
+  const int tid = threadIdx.x;
+  if (tid == 0) hit[0] = -1;
+  int carry = 0;
+  for (int e0 = 0; e0 < n_groups; e0 += 256) {        // uniform
+    const int e = e0 + tid;
+    int st = 0, cnt = 0, te = 0;
+    if (tid < 256 && e < n_groups) {
+      st = min(max(group_offsets[e], 0), rows);
+      cnt = min(max(group_offsets[e + 1], st), rows) - st;
+      te = ((cnt + BM - 1) / BM) * tiles_n;
+    }
+    if (tid < 256) scan[tid] = te;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {         // inclusive Hillis-Steele scan
+      const int v = (tid < 256 && tid >= off) ? scan[tid - off] : 0;
+      __syncthreads();
+      if (tid < 256) scan[tid] += v;
+      __syncthreads();
+    }
+    if (tid < 256 && e < n_groups) {
+      const int incl = carry + scan[tid], excl = incl - te;
+      if (bid >= excl && bid < incl) {
+        hit[0] = e; hit[1] = st; hit[2] = cnt; hit[3] = bid - excl;
+      }
+    }
+    carry += scan[255];
+    __syncthreads();
+  }
+  expert = hit[0];
+  start = hit[1];
+  count = hit[2];
+  tile = hit[3];
+  return expert >= 0;
+}
+
 template <int BM, bool GROUPED, int WN, bool M24 = false>
 __global__ __launch_bounds__(256 * WN, 1) void linear_mx_tile(
     const uint8_t* __restrict__ bb_codes, const uint8_t* __restrict__ bb_meta, const uint8_t* __restrict__ bb_scale,
@@ -610,43 +654,12 @@ __global__ __launch_bounds__(256 * WN, 1) void linear_mx_tile(
     row_end = rows;
     n0 = tn * kBN;
   } else {
-    // tile -> expert: every thread loads one expert's offsets (coalesced),
-    // tile counts are prefix-summed across the workgroup in LDS, and the
-    // thread whose range holds this tile publishes it
     __shared__ int g_scan[256];
     __shared__ int g_hit[4];                            // expert, first row, rows, tile within expert
-    const int bid = blockIdx.x;
-    if (tid == 0) g_hit[0] = -1;
-    int carry = 0;
-    for (int e0 = 0; e0 < n_groups; e0 += 256) {        // uniform
-      const int e = e0 + tid;
-      int st = 0, cnt = 0, te = 0;
-      if (tid < 256 && e < n_groups) {
-        st = min(max(group_offsets[e], 0), rows);
-        cnt = min(max(group_offsets[e + 1], st), rows) - st;
-        te = ((cnt + BM - 1) / BM) * tiles_n;
-      }
-      if (tid < 256) g_scan[tid] = te;
-      __syncthreads();
-      for (int off = 1; off < 256; off <<= 1) {         // inclusive Hillis-Steele scan
-        const int v = (tid < 256 && tid >= off) ? g_scan[tid - off] : 0;
-        __syncthreads();
-        if (tid < 256) g_scan[tid] += v;
-        __syncthreads();
-      }
-      if (tid < 256 && e < n_groups) {
-        const int incl = carry + g_scan[tid], excl = incl - te;
-        if (bid >= excl && bid < incl) {
-          g_hit[0] = e; g_hit[1] = st; g_hit[2] = cnt; g_hit[3] = bid - excl;
-        }
-      }
-      carry += g_scan[255];
-      __syncthreads();
-    }
-    const int e = g_hit[0];
-    if (e < 0) return;                                  // surplus workgroup (uniform)
+    int e, start, cnt, b;
+    if (!find_group_tile(blockIdx.x, n_groups, group_offsets, rows, BM, tiles_n, g_scan, g_hit, e, start, cnt, b))
+      return;                                           // surplus workgroup (uniform)
     grp = e;
-    const int start = g_hit[1], cnt = g_hit[2], b = g_hit[3];
     const int tm = b / tiles_n, tn = b % tiles_n;
     m0 = start + tm * BM;
     row_end = start + cnt;
@@ -877,19 +890,22 @@ struct Tile8Side {             // four steps
 
 }  // namespace
 
-template <int WROWS, int BNE, bool DENSE = false>
+template <int WROWS, int BNE, bool DENSE = false, bool GROUPED = false>
 __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
     const uint8_t* __restrict__ bb_codes, const uint8_t* __restrict__ bb_meta, const uint8_t* __restrict__ bb_scale,
     const uint8_t* __restrict__ res_codes, const uint8_t* __restrict__ res_scale, const int32_t* __restrict__ row_index,
     int rows, int act_rows, int K, const uint8_t* __restrict__ payload, const uint8_t* __restrict__ wscale, int D,
-    float* __restrict__ Y, int64_t ldy) {
+    int n_groups, const int32_t* __restrict__ group_offsets, float* __restrict__ Y, int64_t ldy) {
   // WROWS = 4: waves 4 (rows) x 2 (columns), 64 x 128 each; WROWS = 8: 8 x 1,
   // 32 x 256 each (every backbone fragment expanded by one wave only)
   // BNE: columns the tile computes (256, or 224 so that more shapes give a
   // whole number of rounds over the CUs); staging stays 256 columns wide.
   // DENSE: the plain MXFP4 GEMM of the comparison baseline, one operand
   // (res_codes / res_scale hold plain codes and scales; no backbone)
+  // GROUPED: per-expert weights (n_groups of them, group_offsets delimiting
+  // each expert's rows), tiles numbered expert by expert
   static_assert(BNE == kBN || WROWS == 8, "narrow tiles only with the 8 x 1 layout");
+  static_assert(!(GROUPED && DENSE), "the plain baseline is not grouped");
   // DMA instructions per wave: per step (residual, weight, backbone codes) and
   // per side group (metadata, activation scales, weight scales)
   constexpr int NMAIN = DENSE ? 4 : 5, NSIDE = DENSE ? 2 : 3;
@@ -906,14 +922,31 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
   // that run together on one XCD then share a few activation and weight
   // tiles through its L2 instead of all 16 row tiles of the activations
   // (measured at 4096 x 4096 x 14336: 269 -> 243 us)
-  const int tiles_n = (D + BNE - 1) / BNE, tiles_m = (rows + BM - 1) / BM;
-  const int nt = tiles_m * tiles_n;
-  int bi = blockIdx.x;
-  if ((nt & 7) == 0) bi = (bi & 7) * (nt >> 3) + (bi >> 3);
-  constexpr int kBand = 4;
-  const int band = bi / (kBand * tiles_n), band_m = min(kBand, tiles_m - band * kBand);
-  const int in_band = bi - band * kBand * tiles_n;
-  const int m0 = (band * kBand + in_band % band_m) * BM, n0 = (in_band / band_m) * BNE;
+  const int tiles_n = (D + BNE - 1) / BNE;
+  int grp = 0, m0, n0, row_end = rows;
+  if constexpr (!GROUPED) {
+    const int tiles_m = (rows + BM - 1) / BM;
+    const int nt = tiles_m * tiles_n;
+    int bi = blockIdx.x;
+    if ((nt & 7) == 0) bi = (bi & 7) * (nt >> 3) + (bi >> 3);
+    constexpr int kBand = 4;
+    const int band = bi / (kBand * tiles_n), band_m = min(kBand, tiles_m - band * kBand);
+    const int in_band = bi - band * kBand * tiles_n;
+    m0 = (band * kBand + in_band % band_m) * BM;
+    n0 = (in_band / band_m) * BNE;
+  } else {
+    // the lookup's LDS lives in the third ring stage, which the first DMA
+    // reaches only after the main loop's first barrier, when every thread has
+    // read the result
+    int* scan = reinterpret_cast<int*>(&lds[2].a_dn[0]);
+    int e, start, cnt, b;
+    if (!find_group_tile(blockIdx.x, n_groups, group_offsets, rows, BM, tiles_n, scan, scan + 256, e, start, cnt, b))
+      return;                                           // surplus workgroup (uniform)
+    grp = e;
+    m0 = start + (b / tiles_n) * BM;
+    n0 = (b % tiles_n) * BNE;
+    row_end = start + cnt;
+  }
 
   const int KS = K >> 7, G = KS >> 2;
   const uint32_t kA = K >> 2, kM = K >> 4, kS = K >> 5, kR = K >> 1;
@@ -922,14 +955,14 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
   const int4v r_mt = make_rsrc(bb_meta, (uint32_t)act_rows * kM);
   const int4v r_ssp = make_rsrc(bb_scale, (uint32_t)act_rows * kS);
   const int4v r_sdn = make_rsrc(res_scale, (uint32_t)act_rows * kS);
-  const int4v r_b = make_rsrc(payload, (uint32_t)D * kR);
-  const int4v r_sb = make_rsrc(wscale, (uint32_t)D * kS);
+  const int4v r_b = make_rsrc(payload + (int64_t)grp * D * kR, (uint32_t)D * kR);
+  const int4v r_sb = make_rsrc(wscale + (int64_t)grp * D * kS, (uint32_t)D * kS);
 
-  // activation row of tile row r (rows past the end read row 0: their
+  // activation row of tile row r (rows past the tile's end read row 0: their
   // products reach only outputs that are never stored)
   auto act_row = [&](int r) -> uint32_t {
     const int gr = m0 + r;
-    return gr < rows ? (uint32_t)gather_row(row_index, gr, act_rows) : 0u;
+    return gr < row_end ? (uint32_t)gather_row(row_index, gr, act_rows) : 0u;
   };
   auto w_row = [&](int c) -> uint32_t { return n0 + c < D ? (uint32_t)(n0 + c) : 0u; };
 
@@ -1073,7 +1106,7 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int r = m0 + wm0 + 32 * fm + 8 * (i >> 2) + 4 * kh + (i & 3);
-        if (r < rows) Y[(int64_t)r * ldy + c] = acc[fm][n][i];
+        if (r < row_end) Y[(int64_t)r * ldy + c] = acc[fm][n][i];
       }
     }
   }
@@ -1210,10 +1243,10 @@ hipError_t launch_linear_mx_impl(const uint8_t* bb_codes, const uint8_t* bb_meta
       const bool narrow = (int64_t)((t224 + ncu - 1) / ncu) * 224 < (int64_t)((t256 + ncu - 1) / ncu) * 256;
       if (narrow)
         hipLaunchKernelGGL((linear_mx_tile8<8, 224>), dim3(t224), dim3(512), 0, s, bb_codes, bb_meta, bb_scale,
-                           res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, Y, ldy);
+                           res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, 1, nullptr, Y, ldy);
       else
         hipLaunchKernelGGL((linear_mx_tile8<8, 256>), dim3(t256), dim3(512), 0, s, bb_codes, bb_meta, bb_scale,
-                           res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, Y, ldy);
+                           res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, 1, nullptr, Y, ldy);
       return hipGetLastError();
     }
     hipLaunchKernelGGL((linear_mx_tile<256, false, 2, M24>), dim3(tiles_m * tiles_n), dim3(512), 0, s, bb_codes, bb_meta,
@@ -1222,8 +1255,15 @@ hipError_t launch_linear_mx_impl(const uint8_t* bb_codes, const uint8_t* bb_meta
   } else {
     // 256 x 256 tiles, eight waves (two per SIMD); measured on the MoE
     // shapes faster than 128 x 256 with four (down 157 vs 199 us, up 146 vs
-    // 149 us) despite the emptier last row tile of each expert
+    // 149 us) despite the emptier last row tile of each expert.  A bound on
+    // the tile count; surplus workgroups return at once.
     const int bound = ((rows + 255) / 256 + n_groups) * tiles_n;
+    if (K % 512 == 0 && !M24) {
+      hipLaunchKernelGGL((linear_mx_tile8<8, 256, false, true>), dim3(bound), dim3(512), 0, s, bb_codes, bb_meta,
+                         bb_scale, res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, n_groups,
+                         group_offsets, Y, ldy);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL((linear_mx_tile<256, true, 2, M24>), dim3(bound), dim3(512), 0, s, bb_codes, bb_meta, bb_scale,
                        res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, n_groups, group_offsets, Y,
                        ldy);
@@ -1254,10 +1294,10 @@ hipError_t launch_linear_dense_mx(const uint8_t* codes, const uint8_t* scales, i
   const bool narrow = (int64_t)((t224 + ncu - 1) / ncu) * 224 < (int64_t)((t256 + ncu - 1) / ncu) * 256;
   if (narrow)
     hipLaunchKernelGGL((linear_mx_tile8<8, 224, true>), dim3(t224), dim3(512), 0, s, nullptr, nullptr, nullptr, codes,
-                       scales, nullptr, rows, rows, K, payload, wscale, D, Y, ldy);
+                       scales, nullptr, rows, rows, K, payload, wscale, D, 1, nullptr, Y, ldy);
   else
     hipLaunchKernelGGL((linear_mx_tile8<8, 256, true>), dim3(t256), dim3(512), 0, s, nullptr, nullptr, nullptr, codes,
-                       scales, nullptr, rows, rows, K, payload, wscale, D, Y, ldy);
+                       scales, nullptr, rows, rows, K, payload, wscale, D, 1, nullptr, Y, ldy);
   return hipGetLastError();
 }
 

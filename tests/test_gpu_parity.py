@@ -283,6 +283,29 @@ def test_grouped_small():
     assert_gemm_close(Y.cpu().numpy(), Yr, S)
 
 
+@pytest.mark.parametrize("gather", [False, True])
+def test_grouped_eight_wave_tile(gather):
+    # K % 512 == 0 takes the eight-wave grouped tile: experts of 0, 300 (two
+    # row tiles, the second ragged), 17, 0 and 520 rows, a ragged column tile
+    # (D = 300), expert-sorted rows or rows gathered from 400 activations
+    rng = np.random.default_rng(21)
+    E, K, D = 5, 1024, 300
+    go = np.concatenate([[0], np.cumsum([0, 300, 17, 0, 520])]).astype(np.int32)
+    R = int(go[-1])
+    T = 400 if gather else R
+    ri = rng.integers(0, T, R).astype(np.int32) if gather else None
+    case = synth.random_case(21, T, K, 1)
+    W = synth.f32_to_bf16_bits(rng.standard_normal((E, K, D)).astype(np.float32) * 0.02)
+    act = ops.prepare(dev_x(case), dev_gamma(case.gamma), 1e-6)
+    w = ops.pack_weight(dev_w(W, "bf16"))
+    Y = ops.linear(act, w, group_offsets=torch.from_numpy(go).cuda(),
+                   row_index=None if ri is None else torch.from_numpy(ri).cuda(), total_rows=R)
+    ref = oracle_prepare(case)
+    wps = [O.pack_weight(synth.bf16_bits_to_f32(W[e])) for e in range(E)]
+    Yr, S = O.grouped_linear(ref, wps, go, ri)
+    assert_gemm_close(Y.cpu().numpy(), Yr, S)
+
+
 @pytest.mark.parametrize("proj", ["up", "down"])
 def test_grouped_moe_full_sampled(proj):
     mc = synth.moe_case(proj)
