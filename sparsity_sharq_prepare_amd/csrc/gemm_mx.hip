@@ -858,7 +858,7 @@ __global__ __launch_bounds__(256 * WN, 1) void linear_mx_tile(
 }
 
 // ============================================================================
-// prefill tile kernel, two waves per SIMD (K % 512 == 0)
+// prefill tile kernel, two waves per SIMD (K % 128 == 0)
 // ============================================================================
 // Tile 256 x 256, eight waves, two per SIMD covering each other's LDS and
 // barrier latency; each wave holds a 128-register accumulator.  The layout
@@ -948,7 +948,10 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
     row_end = start + cnt;
   }
 
-  const int KS = K >> 7, G = KS >> 2;
+  // K % 128 == 0: KS steps of 128, side groups of 4 steps (the last one may
+  // be partial; its rows' side bytes past the step count are loaded but not
+  // read)
+  const int KS = K >> 7, G = (KS + 3) >> 2;
   const uint32_t kA = K >> 2, kM = K >> 4, kS = K >> 5, kR = K >> 1;
   const int4v r_dn = make_rsrc(res_codes, (uint32_t)act_rows * kR);
   const int4v r_sp = make_rsrc(bb_codes, (uint32_t)act_rows * kA);
@@ -1077,6 +1080,7 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int s = 4 * g + p;
+      if (s >= KS) break;                                 // partial last side group (uniform)
       // stage s (and at p = 0 side group g) landed; stage s+1 (and after
       // p = 2 side group g+1) may still be in flight.  After the barrier every
       // wave is past its reads of step s-1, whose buffer stage s+2 reuses.
@@ -1236,7 +1240,7 @@ hipError_t launch_linear_mx_impl(const uint8_t* bb_codes, const uint8_t* bb_meta
     const int tiles_m = (rows + 255) / 256;
     // (the 2:4 backbone's larger metadata does not fit the eight-wave tile's
     // LDS ring; it takes the general tile below)
-    if (K % 512 == 0 && !M24) {
+    if (K % 128 == 0 && !M24) {
       // tile width 256 or 224: the one with fewer rounds x width over the CUs
       const int ncu = num_cus_gemm();
       const int t256 = tiles_m * ((D + 255) / 256), t224 = tiles_m * ((D + 223) / 224);
@@ -1258,7 +1262,7 @@ hipError_t launch_linear_mx_impl(const uint8_t* bb_codes, const uint8_t* bb_meta
     // 149 us) despite the emptier last row tile of each expert.  A bound on
     // the tile count; surplus workgroups return at once.
     const int bound = ((rows + 255) / 256 + n_groups) * tiles_n;
-    if (K % 512 == 0 && !M24) {
+    if (K % 128 == 0 && !M24) {
       hipLaunchKernelGGL((linear_mx_tile8<8, 256, false, true>), dim3(bound), dim3(512), 0, s, bb_codes, bb_meta,
                          bb_scale, res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, n_groups,
                          group_offsets, Y, ldy);

@@ -159,6 +159,9 @@ def test_linear_tiny_config():
 LINEAR_SHAPES = [  # skinny (T <= 64) and tile paths, ragged rows and columns
     (1, 512, 200), (8, 512, 200), (13, 256, 64), (64, 384, 130), (65, 512, 300), (300, 512, 520),
     (256, 1024, 256), (700, 128, 40),
+    # K % 512 != 0 on the tile path: 3, 5 and 6 steps of 128 (a partial last
+    # group of four steps; 24-byte scale rows at K = 768)
+    (100, 384, 72), (257, 640, 300), (333, 768, 250),
     # decode path (<= 8 rows): uneven steps per wave, the largest staged K, and
     # a K beyond it (general skinny path)
     (5, 1152, 72), (7, 16384, 48), (2, 18944, 40),
@@ -283,13 +286,15 @@ def test_grouped_small():
     assert_gemm_close(Y.cpu().numpy(), Yr, S)
 
 
+@pytest.mark.parametrize("K", [1024, 768])
 @pytest.mark.parametrize("gather", [False, True])
-def test_grouped_eight_wave_tile(gather):
-    # K % 512 == 0 takes the eight-wave grouped tile: experts of 0, 300 (two
-    # row tiles, the second ragged), 17, 0 and 520 rows, a ragged column tile
-    # (D = 300), expert-sorted rows or rows gathered from 400 activations
+def test_grouped_eight_wave_tile(gather, K):
+    # the eight-wave grouped tile: experts of 0, 300 (two row tiles, the
+    # second ragged), 17, 0 and 520 rows, a ragged column tile (D = 300),
+    # expert-sorted rows or rows gathered from 400 activations; K = 768 ends
+    # on a partial group of four steps
     rng = np.random.default_rng(21)
-    E, K, D = 5, 1024, 300
+    E, D = 5, 300
     go = np.concatenate([[0], np.cumsum([0, 300, 17, 0, 520])]).astype(np.int32)
     R = int(go[-1])
     T = 400 if gather else R
