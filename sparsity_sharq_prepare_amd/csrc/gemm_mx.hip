@@ -887,10 +887,20 @@ struct Tile8Side {             // four steps
   uint4 s_dn[256];
   uint4 s_b[256];
 };
+// 2:4 backbone: its metadata (16 B per row and step) goes with the step's
+// codes, and the side ring keeps the scales only (3 x 44 KB + 2 x 12 KB)
+struct Tile8Main24 : Tile8Main {
+  uint4 meta[256];             // 16 B per row: the step's four 32-value blocks
+};
+struct Tile8Side24 {
+  uint4 s_sp[256];
+  uint4 s_dn[256];
+  uint4 s_b[256];
+};
 
 }  // namespace
 
-template <int WROWS, int BNE, bool DENSE = false, bool GROUPED = false>
+template <int WROWS, int BNE, bool DENSE = false, bool GROUPED = false, bool M24 = false, bool PARTIAL = false>
 __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
     const uint8_t* __restrict__ bb_codes, const uint8_t* __restrict__ bb_meta, const uint8_t* __restrict__ bb_scale,
     const uint8_t* __restrict__ res_codes, const uint8_t* __restrict__ res_scale, const int32_t* __restrict__ row_index,
@@ -904,14 +914,20 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
   // (res_codes / res_scale hold plain codes and scales; no backbone)
   // GROUPED: per-expert weights (n_groups of them, group_offsets delimiting
   // each expert's rows), tiles numbered expert by expert
+  // M24: the 2:4 element-wise backbone (metadata K/8 bytes per row)
+  // PARTIAL: K % 512 != 0, the last side group of four steps is partial
+  // (a separate instance keeps the K % 512 == 0 loop free of the check)
   static_assert(BNE == kBN || WROWS == 8, "narrow tiles only with the 8 x 1 layout");
-  static_assert(!(GROUPED && DENSE), "the plain baseline is not grouped");
-  // DMA instructions per wave: per step (residual, weight, backbone codes) and
-  // per side group (metadata, activation scales, weight scales)
-  constexpr int NMAIN = DENSE ? 4 : 5, NSIDE = DENSE ? 2 : 3;
+  static_assert(!(GROUPED && DENSE) && !(M24 && DENSE), "the plain baseline has no backbone");
+  // DMA instructions per wave: per step (residual, weight, backbone codes;
+  // 2:4: and metadata) and per side group (4:8: metadata; activation scales,
+  // weight scales)
+  constexpr int NMAIN = DENSE ? 4 : (M24 ? 6 : 5), NSIDE = DENSE || M24 ? 2 : 3;
   constexpr int BM = 256, WM = BM / WROWS, WNC = BNE * WROWS / 8, FM = WM / 32, FN = WNC / 32;
-  __shared__ Tile8Main lds[kNS];
-  __shared__ Tile8Side side[2];
+  using MainT = std::conditional_t<M24, Tile8Main24, Tile8Main>;
+  using SideT = std::conditional_t<M24, Tile8Side24, Tile8Side>;
+  __shared__ MainT lds[kNS];
+  __shared__ SideT side[2];
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int wq = w & 3;
@@ -951,8 +967,8 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
   // K % 128 == 0: KS steps of 128, side groups of 4 steps (the last one may
   // be partial; its rows' side bytes past the step count are loaded but not
   // read)
-  const int KS = K >> 7, G = (KS + 3) >> 2;
-  const uint32_t kA = K >> 2, kM = K >> 4, kS = K >> 5, kR = K >> 1;
+  const int KS = K >> 7, G = PARTIAL ? (KS + 3) >> 2 : KS >> 2;
+  const uint32_t kA = K >> 2, kM = K >> (M24 ? 3 : 4), kS = K >> 5, kR = K >> 1;
   const int4v r_dn = make_rsrc(res_codes, (uint32_t)act_rows * kR);
   const int4v r_sp = make_rsrc(bb_codes, (uint32_t)act_rows * kA);
   const int4v r_mt = make_rsrc(bb_meta, (uint32_t)act_rows * kM);
@@ -984,24 +1000,29 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
     const int sl = 64 * w + l, row = sl >> 1, h = (sl & 1) ^ ((row >> 3) & 1);
     o_sp = act_row(row) * kA + 16 * h;
   }
-  const uint32_t o_mt = act_row((64 * w + l) >> 1) * kM + 16 * (l & 1);   // 2 lanes x 16 B per row
+  // 4:8: 2 lanes x 16 B per row and side group; 2:4: 16 B per row and step,
+  // waves w and w + 4 loading the same rows (same bytes to the same place)
+  const uint32_t o_mt = M24 ? act_row(64 * wq + l) * kM : act_row((64 * w + l) >> 1) * kM + 16 * (l & 1);
   // waves 0-3: backbone scale rows and weight scale columns 64 wq + l;
   // waves 4-7: residual scale rows and the same weight columns again
   const uint32_t o_sa = act_row(64 * wq + l) * kS;
   const uint32_t o_sw = 64 * wq + l < BNE ? w_row(64 * wq + l) * kS : 0x80000000u;
   const int4v r_sa = w < 4 ? r_ssp : r_sdn;
 
-  auto issue_main = [&](int s, Tile8Main& st) {
+  auto issue_main = [&](int s, MainT& st) {
     const uint32_t s64 = 64u * s, s32 = 32u * s;
 #pragma unroll
     for (int j = 0; j < 2; ++j) dma16(r_dn, o_dn[j], s64, lds_addr(&st.a_dn[64 * (w + 8 * j)]));
 #pragma unroll
     for (int j = 0; j < 2; ++j) dma16(r_b, o_b[j], s64, lds_addr(&st.b[64 * (w + 8 * j)]));
     if constexpr (!DENSE) dma16(r_sp, o_sp, s32, lds_addr(&st.a_sp[64 * w]));
+    if constexpr (M24) dma16(r_mt, o_mt, 16u * s, lds_addr(&st.meta[64 * wq]));
   };
-  auto issue_side = [&](int g, Tile8Side& sd) {
+  auto issue_side = [&](int g, SideT& sd) {
     if constexpr (DENSE) {
       dma16(r_sdn, o_sa, 16u * g, lds_addr(&sd.s_dn[64 * wq]));   // waves w and w + 4: same bytes
+    } else if constexpr (M24) {
+      dma16(r_sa, o_sa, 16u * g, lds_addr(w < 4 ? &sd.s_sp[64 * wq] : &sd.s_dn[64 * wq]));
     } else {
       dma16(r_mt, o_mt, 32u * g, lds_addr(&sd.meta[64 * w]));
       dma16(r_sa, o_sa, 16u * g, lds_addr(w < 4 ? &sd.s_sp[64 * wq] : &sd.s_dn[64 * wq]));
@@ -1015,17 +1036,16 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
   // high 16 bits) and the compacted backbone (low / high 8 bytes) are read
   // once; per half-step only the weight and residual code fragments
   struct StepFrag {
-    uint32_t bs[FN], ssp[FM], sdn[FM], mt[FM];
+    uint32_t bs[FN], ssp[FM], sdn[FM], mt[FM], mt2[FM];   // mt2: 2:4 only
     uint4 sp[FM];
   };
   struct HalfFrag {
     uint4 b[FN], dn[FM];
   };
-  auto read_step = [&](const Tile8Main& st, const Tile8Side& sd, int p, StepFrag& S) {
+  auto read_step = [&](const MainT& st, const SideT& sd, int p, StepFrag& S) {
     const uint16_t* s_b = reinterpret_cast<const uint16_t*>(sd.s_b);
     const uint16_t* s_sp = reinterpret_cast<const uint16_t*>(sd.s_sp);
     const uint16_t* s_dn = reinterpret_cast<const uint16_t*>(sd.s_dn);
-    const uint32_t* meta = reinterpret_cast<const uint32_t*>(sd.meta);
 #pragma unroll
     for (int n = 0; n < FN; ++n) S.bs[n] = s_b[8 * (wn0 + 32 * n + lr) + 2 * p + kh];
 #pragma unroll
@@ -1033,13 +1053,20 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
       const int r = wm0 + 32 * f + lr;
       if constexpr (!DENSE) {
         S.sp[f] = st.a_sp[slot_sp(r, kh)];
-        S.mt[f] = meta[8 * r + 2 * p + kh];
+        if constexpr (M24) {
+          // the lane's two 32-value blocks: dwords 2 kh and 2 kh + 1 of the row
+          const uint2 m = reinterpret_cast<const uint2*>(st.meta)[2 * r + kh];
+          S.mt[f] = m.x;
+          S.mt2[f] = m.y;
+        } else {
+          S.mt[f] = reinterpret_cast<const uint32_t*>(sd.meta)[8 * r + 2 * p + kh];
+        }
         S.ssp[f] = s_sp[8 * r + 2 * p + kh];
       }
       S.sdn[f] = s_dn[8 * r + 2 * p + kh];
     }
   };
-  auto read_half = [&](const Tile8Main& st, HalfFrag& H, auto jc) {
+  auto read_half = [&](const MainT& st, HalfFrag& H, auto jc) {
     constexpr int J = decltype(jc)::value;
 #pragma unroll
     for (int n = 0; n < FN; ++n) H.b[n] = st.b[slot(wn0 + 32 * n + lr, 2 * kh + J)];
@@ -1058,8 +1085,12 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
 #pragma unroll
     for (int f = 0; f < FM; ++f) {
       if constexpr (!DENSE) {
-        const uint4 asp = J == 0 ? expand4_fast(S.sp[f].x, S.sp[f].y, S.mt[f] & 0xFFFFu)
-                                 : expand4_fast(S.sp[f].z, S.sp[f].w, S.mt[f] >> 16);
+        uint4 asp;
+        if constexpr (M24)
+          asp = J == 0 ? expand_24(S.sp[f].x, S.sp[f].y, S.mt[f]) : expand_24(S.sp[f].z, S.sp[f].w, S.mt2[f]);
+        else
+          asp = J == 0 ? expand4_fast(S.sp[f].x, S.sp[f].y, S.mt[f] & 0xFFFFu)
+                       : expand4_fast(S.sp[f].z, S.sp[f].w, S.mt[f] >> 16);
 #pragma unroll
         for (int n = 0; n < FN; ++n) acc[f][n] = mfma32_fp4_sel<J>(asp, H.b[n], acc[f][n], S.ssp[f], S.bs[n]);
       }
@@ -1076,11 +1107,12 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
   issue_side(0, side[0]);
   issue_main(min(1, KS - 1), lds[1]);
   for (int g = 0; g < G; ++g) {
-    const Tile8Side& sd = side[g & 1];
+    const SideT& sd = side[g & 1];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int s = 4 * g + p;
-      if (s >= KS) break;                                 // partial last side group (uniform)
+      if constexpr (PARTIAL)
+        if (s >= KS) break;                               // partial last side group (uniform)
       // stage s (and at p = 0 side group g) landed; stage s+1 (and after
       // p = 2 side group g+1) may still be in flight.  After the barrier every
       // wave is past its reads of step s-1, whose buffer stage s+2 reuses.
@@ -1090,7 +1122,7 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
       issue_main(min(s + 2, KS - 1), lds[(s + 2) % kNS]);
       // side group g+1 replaces group g-1, last read at step 4 g - 1
       if (p == 2) issue_side(min(g + 1, G - 1), side[(g + 1) & 1]);
-      const Tile8Main& cur = lds[s % kNS];
+      const MainT& cur = lds[s % kNS];
       read_step(cur, sd, p, sf);
       read_half(cur, hf, j0);
       mfma_half(sf, hf, j0);
@@ -1238,19 +1270,23 @@ hipError_t launch_linear_mx_impl(const uint8_t* bb_codes, const uint8_t* bb_meta
   const int tiles_n = (D + kBN - 1) / kBN;
   if (n_groups == 1) {
     const int tiles_m = (rows + 255) / 256;
-    // (the 2:4 backbone's larger metadata does not fit the eight-wave tile's
-    // LDS ring; it takes the general tile below)
-    if (K % 128 == 0 && !M24) {
+    if (K % 128 == 0) {
       // tile width 256 or 224: the one with fewer rounds x width over the CUs
       const int ncu = num_cus_gemm();
       const int t256 = tiles_m * ((D + 255) / 256), t224 = tiles_m * ((D + 223) / 224);
       const bool narrow = (int64_t)((t224 + ncu - 1) / ncu) * 224 < (int64_t)((t256 + ncu - 1) / ncu) * 256;
-      if (narrow)
-        hipLaunchKernelGGL((linear_mx_tile8<8, 224>), dim3(t224), dim3(512), 0, s, bb_codes, bb_meta, bb_scale,
-                           res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, 1, nullptr, Y, ldy);
-      else
-        hipLaunchKernelGGL((linear_mx_tile8<8, 256>), dim3(t256), dim3(512), 0, s, bb_codes, bb_meta, bb_scale,
-                           res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, 1, nullptr, Y, ldy);
+#define T8(BNE_, PARTIAL_)                                                                                            \
+  hipLaunchKernelGGL((linear_mx_tile8<8, BNE_, false, false, M24, PARTIAL_>), dim3(narrow ? t224 : t256), dim3(512), 0, \
+                     s, bb_codes, bb_meta, bb_scale, res_codes, res_scale, row_index, rows, act_rows, K, payload,       \
+                     wscale, D, 1, nullptr, Y, ldy)
+      if (K % 512 == 0) {
+        if (narrow) T8(224, false);
+        else T8(256, false);
+      } else {
+        if (narrow) T8(224, true);
+        else T8(256, true);
+      }
+#undef T8
       return hipGetLastError();
     }
     hipLaunchKernelGGL((linear_mx_tile<256, false, 2, M24>), dim3(tiles_m * tiles_n), dim3(512), 0, s, bb_codes, bb_meta,
@@ -1262,10 +1298,14 @@ hipError_t launch_linear_mx_impl(const uint8_t* bb_codes, const uint8_t* bb_meta
     // 149 us) despite the emptier last row tile of each expert.  A bound on
     // the tile count; surplus workgroups return at once.
     const int bound = ((rows + 255) / 256 + n_groups) * tiles_n;
-    if (K % 128 == 0 && !M24) {
-      hipLaunchKernelGGL((linear_mx_tile8<8, 256, false, true>), dim3(bound), dim3(512), 0, s, bb_codes, bb_meta,
-                         bb_scale, res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, n_groups,
-                         group_offsets, Y, ldy);
+    if (K % 128 == 0) {
+#define T8G(PARTIAL_)                                                                                                 \
+  hipLaunchKernelGGL((linear_mx_tile8<8, 256, false, true, M24, PARTIAL_>), dim3(bound), dim3(512), 0, s, bb_codes,    \
+                     bb_meta, bb_scale, res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, n_groups, \
+                     group_offsets, Y, ldy)
+      if (K % 512 == 0) T8G(false);
+      else T8G(true);
+#undef T8G
       return hipGetLastError();
     }
     hipLaunchKernelGGL((linear_mx_tile<256, true, 2, M24>), dim3(bound), dim3(512), 0, s, bb_codes, bb_meta, bb_scale,

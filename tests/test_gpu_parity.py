@@ -653,9 +653,10 @@ def test_prepare_24_edge_rows():
     compare_act(act, O.prepare(x, g, 1e-6, "mxfp4", mask="2:4"))
 
 
-M24_LINEAR = [  # decode (<= 8 rows), skinny (<= 64), general tile (> 64 rows, any K % 128), ragged
+M24_LINEAR = [  # decode (<= 8 rows), skinny (<= 64), eight-wave tile (> 64 rows, any K % 128), ragged
     (1, 512, 200), (8, 512, 200), (5, 1152, 72), (7, 16384, 48), (13, 256, 64), (64, 384, 130),
     (65, 512, 300), (300, 512, 520), (700, 128, 40), (256, 1024, 256), (70, 512, 1),
+    (100, 384, 72), (333, 768, 250),
 ]
 
 
