@@ -476,31 +476,19 @@ __global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
 }
 
 // ============================================================================
-// tile kernel (prefill / grouped)
+// shared pieces of the tile kernel
 // ============================================================================
-// Workgroup tile BM x 256 (BM = 256 plain, 128 grouped), K steps of 128, four
-// waves stacked along M (each BM/4 rows x 256 columns; every backbone
-// fragment is expanded by exactly one wave), one wave per SIMD with the whole
-// accumulator tile in the 256 AGPRs.
+// Staging is buffer->LDS DMA (buffer_load_dwordx4 ... lds) into LDS rings,
+// no staging registers; the per-step offset is a scalar and reads past a
+// buffer return zeros.  The DMAs are issued from inline assembly: they write
+// no registers, and keeping them out of the compiler's sight stops it from
+// waiting for every in-flight DMA before each LDS read (it cannot tell the
+// ring buffers apart); completion is tracked by explicit vmcnt waits.
 //
-// Staging: buffer->LDS DMA (buffer_load_dword{,x4} ... lds) into a 3-deep LDS
-// ring, no staging registers; the per-step offset is a scalar and reads past
-// a buffer return zeros.  The DMAs are issued from inline assembly: they
-// write no registers, and keeping them out of the compiler's sight stops it
-// from waiting for every in-flight DMA before each LDS read (it cannot tell
-// the ring buffers apart); completion is tracked by the explicit vmcnt waits.
-//
-// Software pipeline over K half-steps, fragments double-buffered in
-// registers: per step s, read half 1 of s | MFMAs of half 0 | wait for
-// stage s+1, barrier, read half 0 of s+1, issue stage s+3 into the buffer
-// of step s | MFMAs of half 1.  Every fragment read overlaps a group of
-// MFMAs, the loads run about two and a half steps ahead, and there is one
-// barrier per step.
-//
-// K order inside a step: lane half kh handles the 32-value blocks 2 kh and
-// 2 kh + 1 (sub-steps j = 0, 1), so its two scale bytes are one 16-bit LDS
-// read and the MFMA's op_sel picks byte j.  A, B and both paths use the same
-// order, so the sum is unchanged.
+// K order inside a 128-step: lane half kh handles the 32-value blocks 2 kh
+// and 2 kh + 1 (sub-steps j = 0, 1), so its two scale bytes are one 16-bit
+// LDS read and the MFMA's op_sel picks byte j.  A, B and both paths use the
+// same order, so the sum is unchanged.
 namespace {
 
 constexpr int kBN = 256;
@@ -516,17 +504,6 @@ SHARQ_DEV int slot(int row, int q) { return row * 4 + (q ^ swz(row)); }
 // 16-byte half h of a 32-byte compacted-backbone row
 SHARQ_DEV int slot_sp(int row, int h) { return row * 2 + (h ^ ((row >> 3) & 1)); }
 
-template <int BM, bool M24 = false>
-struct TileStage {
-  uint4 a_dn[BM * 4];          // residual codes, 64 B per row (swizzled 16 B slots)
-  uint4 b[kBN * 4];            // weight payload, 64 B per column
-  uint4 a_sp[BM * 2];          // compacted backbone, 32 B per row
-  uint32_t meta[BM * (M24 ? 4 : 2)];   // backbone metadata, 8 B per row (2:4: 16 B)
-  uint32_t s_sp[BM];           // 4 scale bytes per row / column
-  uint32_t s_dn[BM];
-  uint32_t s_b[kBN];
-};
-
 typedef int int4v __attribute__((ext_vector_type(4)));
 
 // raw buffer resource (gfx9 layout): base, num_records = bytes, no stride
@@ -535,13 +512,9 @@ SHARQ_DEV int4v make_rsrc(const void* base, uint32_t bytes) {
   return (int4v){(int)(uint32_t)p, (int)((uint32_t)(p >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
 }
 SHARQ_DEV uint32_t lds_addr(const void* p) { return (uint32_t)reinterpret_cast<uintptr_t>(p); }
-// lane l of the wave writes its 16 (4) bytes at LDS address lds + 16 l (4 l)
+// lane l of the wave writes its 16 bytes at LDS address lds + 16 l
 SHARQ_DEV void dma16(int4v rs, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(soff), "{m0}"(lds)
-               : "memory");
-}
-SHARQ_DEV void dma4(int4v rs, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(soff), "{m0}"(lds)
                : "memory");
 }
 
@@ -551,26 +524,12 @@ template <int N>
 SHARQ_DEV void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
-// s_waitcnt lgkmcnt 0 only
-SHARQ_DEV void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
 
 template <int J>
 SHARQ_DEV v16f mfma32_fp4_sel(uint4 a, uint4 b, v16f c, uint32_t sa, uint32_t sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_v8i(a), as_v8i(b), c, 4, 4, J, (int)sa, J, (int)sb);
 }
-
-// register copy of one K half-step's fragments (lane half kh, sub-step J:
-// K block 2 kh + J of the step)
-template <int FM, int FN>
-struct TileFrag {
-  uint4 b[FN];
-  uint32_t bs[FN];             // scale bytes of blocks 2 kh, 2 kh + 1 (op_sel picks J)
-  uint4 dn[FM];
-  uint2 sp[FM];                // compacted backbone of the block (4 groups x 2 bytes)
-  uint32_t mt[FM];             // its 4 metadata nibbles
-  uint32_t ssp[FM], sdn[FM];
-};
 
 }  // namespace
 
@@ -616,245 +575,6 @@ SHARQ_DEV bool find_group_tile(int bid, int n_groups, const int32_t* __restrict_
   count = hit[2];
   tile = hit[3];
   return expert >= 0;
-}
-
-template <int BM, bool GROUPED, int WN, bool M24 = false>
-__global__ __launch_bounds__(256 * WN, 1) void linear_mx_tile(
-    const uint8_t* __restrict__ bb_codes, const uint8_t* __restrict__ bb_meta, const uint8_t* __restrict__ bb_scale,
-    const uint8_t* __restrict__ res_codes, const uint8_t* __restrict__ res_scale, const int32_t* __restrict__ row_index,
-    int rows, int act_rows, int K, const uint8_t* __restrict__ payload, const uint8_t* __restrict__ wscale, int D,
-    int n_groups, const int32_t* __restrict__ group_offsets, float* __restrict__ Y, int64_t ldy) {
-  using Stage = TileStage<BM, M24>;
-  // 4 x WN waves: wave w covers rows (w & 3) * WM .. and columns (w >> 2) * WNC ..
-  constexpr int NW = 4 * WN;
-  constexpr int WM = BM / 4, WNC = kBN / WN, FM = WM / 32, FN = WNC / 32;
-  static_assert(WN == 1 || BM == 256, "two waves per SIMD only for the 256-row tile");
-  using Frag = TileFrag<FM, FN>;
-  // DMA instructions per wave and stage: A_dn, B, A_sp, meta, scale rows
-  // (WN = 1: s_sp, s_dn, s_b; WN = 2: waves 0-3 s_sp and s_dn, waves 4-7 s_b
-  // twice, so every wave issues the same number and one wait count fits all)
-  constexpr int N_DN = BM / (16 * NW), N_B = 16 / NW, N_SP = BM / (32 * NW), N_MT = BM / ((M24 ? 16 : 32) * NW);
-  constexpr int NDMA = N_DN + N_B + N_SP + N_MT + (WN == 1 ? 3 : 2);
-  __shared__ Stage lds[kNS];
-  const int tid = threadIdx.x, l = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
-  const int tiles_n = (D + kBN - 1) / kBN;
-
-  // ---- tile -> (group, first row, row end, first column)
-  int grp = 0, m0, row_end, n0;
-  if (!GROUPED) {
-    const int tiles_m = (rows + BM - 1) / BM;
-    const int nt = tiles_m * tiles_n;
-    int b = blockIdx.x;
-    if ((nt & 7) == 0) b = (b & 7) * (nt >> 3) + (b >> 3);   // consecutive tiles on one XCD
-    // bands of 4 row tiles sweeping the columns, as in linear_mx_tile8
-    const int band = b / (4 * tiles_n), band_m = min(4, tiles_m - band * 4), in_band = b - band * 4 * tiles_n;
-    const int tm = band * 4 + in_band % band_m, tn = in_band / band_m;
-    m0 = tm * BM;
-    row_end = rows;
-    n0 = tn * kBN;
-  } else {
-    __shared__ int g_scan[256];
-    __shared__ int g_hit[4];                            // expert, first row, rows, tile within expert
-    int e, start, cnt, b;
-    if (!find_group_tile(blockIdx.x, n_groups, group_offsets, rows, BM, tiles_n, g_scan, g_hit, e, start, cnt, b))
-      return;                                           // surplus workgroup (uniform)
-    grp = e;
-    const int tm = b / tiles_n, tn = b % tiles_n;
-    m0 = start + tm * BM;
-    row_end = start + cnt;
-    n0 = tn * kBN;
-  }
-
-  const int KS = K >> 7;
-  const uint32_t kA = K >> 2, kM = K >> (M24 ? 3 : 4), kS = K >> 5, kR = K >> 1;
-  const int4v r_dn = make_rsrc(res_codes, (uint32_t)act_rows * kR);
-  const int4v r_sp = make_rsrc(bb_codes, (uint32_t)act_rows * kA);
-  const int4v r_mt = make_rsrc(bb_meta, (uint32_t)act_rows * kM);
-  const int4v r_ssp = make_rsrc(bb_scale, (uint32_t)act_rows * kS);
-  const int4v r_sdn = make_rsrc(res_scale, (uint32_t)act_rows * kS);
-  const int4v r_b = make_rsrc(payload + (int64_t)grp * D * kR, (uint32_t)D * kR);
-  const int4v r_sb = make_rsrc(wscale + (int64_t)grp * D * kS, (uint32_t)D * kS);
-
-  // activation row of tile row r (rows outside the tile read row 0: their
-  // products reach only outputs that are never stored)
-  auto act_row = [&](int r) -> uint32_t {
-    const int gr = m0 + r;
-    return gr < row_end ? (uint32_t)gather_row(row_index, gr, act_rows) : 0u;
-  };
-  auto w_row = [&](int c) -> uint32_t { return n0 + c < D ? (uint32_t)(n0 + c) : 0u; };
-
-  // ---- per-lane DMA byte offsets (step 0); instruction j of this wave fills
-  // slots [64 j', 64 j' + 64) of its region, j' = w + 4 j
-  uint32_t o_dn[N_DN], o_b[N_B], o_sp[N_SP], o_mt[N_MT];
-#pragma unroll
-  for (int j = 0; j < N_DN; ++j) {
-    const int sl = 64 * (w + NW * j) + l, row = sl >> 2, q = (sl & 3) ^ swz(row);
-    o_dn[j] = act_row(row) * kR + 16 * q;
-  }
-#pragma unroll
-  for (int j = 0; j < N_B; ++j) {
-    const int sl = 64 * (w + NW * j) + l, col = sl >> 2, q = (sl & 3) ^ swz(col);
-    o_b[j] = w_row(col) * kR + 16 * q;
-  }
-#pragma unroll
-  for (int j = 0; j < N_SP; ++j) {
-    const int sl = 64 * (w + NW * j) + l, row = sl >> 1, h = (sl & 1) ^ ((row >> 3) & 1);
-    o_sp[j] = act_row(row) * kA + 16 * h;
-  }
-#pragma unroll
-  for (int j = 0; j < N_MT; ++j) {                      // dword slots: 2 per row (2:4: 4)
-    const int sl = 64 * (w + NW * j) + l, row = M24 ? sl >> 2 : sl >> 1, h = M24 ? sl & 3 : sl & 1;
-    o_mt[j] = act_row(row) * kM + 4 * h;
-  }
-  // scale rows: one dword (4 blocks) per row; for BM = 128 waves 2, 3 repeat
-  // the rows of waves 0, 1 (same bytes to the same place)
-  const int wq = w & 3;
-  const int srow = (64 * wq + l) & (BM - 1);
-  const uint32_t o_ssp = act_row(srow) * kS;
-  const uint32_t o_sb = w_row(64 * wq + l) * kS;
-  const int sdst = 64 * (wq & (BM / 64 - 1));
-
-  auto issue = [&](int s, Stage& st) {
-    const uint32_t s64 = 64u * s, s32 = 32u * s, s8 = (M24 ? 16u : 8u) * s, s4 = 4u * s;
-#pragma unroll
-    for (int j = 0; j < N_DN; ++j) dma16(r_dn, o_dn[j], s64, lds_addr(&st.a_dn[64 * (w + NW * j)]));
-#pragma unroll
-    for (int j = 0; j < N_B; ++j) dma16(r_b, o_b[j], s64, lds_addr(&st.b[64 * (w + NW * j)]));
-#pragma unroll
-    for (int j = 0; j < N_SP; ++j) dma16(r_sp, o_sp[j], s32, lds_addr(&st.a_sp[64 * (w + NW * j)]));
-#pragma unroll
-    for (int j = 0; j < N_MT; ++j) dma4(r_mt, o_mt[j], s8, lds_addr(&st.meta[64 * (w + NW * j)]));
-    if (WN == 1) {
-      dma4(r_ssp, o_ssp, s4, lds_addr(&st.s_sp[sdst]));
-      dma4(r_sdn, o_ssp, s4, lds_addr(&st.s_dn[sdst]));
-      dma4(r_sb, o_sb, s4, lds_addr(&st.s_b[64 * w]));
-    } else if (w < 4) {                                // uniform branch
-      dma4(r_ssp, o_ssp, s4, lds_addr(&st.s_sp[sdst]));
-      dma4(r_sdn, o_ssp, s4, lds_addr(&st.s_dn[sdst]));
-    } else {
-      dma4(r_sb, o_sb, s4, lds_addr(&st.s_b[64 * wq]));
-      dma4(r_sb, o_sb, s4, lds_addr(&st.s_b[64 * wq]));   // same bytes again: equal counts
-    }
-  };
-
-  const int wm0 = (w & 3) * WM, wn0 = (w >> 2) * WNC;
-  const int kh = l >> 5, lr = l & 31;
-  auto read = [&](const Stage& st, Frag& F, auto jc) {
-    constexpr int J = decltype(jc)::value;
-    const uint16_t* s_b = reinterpret_cast<const uint16_t*>(st.s_b);
-    const uint16_t* s_sp = reinterpret_cast<const uint16_t*>(st.s_sp);
-    const uint16_t* s_dn = reinterpret_cast<const uint16_t*>(st.s_dn);
-    const uint2* a_sp = reinterpret_cast<const uint2*>(st.a_sp);
-    const uint16_t* meta = reinterpret_cast<const uint16_t*>(st.meta);
-    const uint32_t* meta32 = st.meta;
-#pragma unroll
-    for (int n = 0; n < FN; ++n) {
-      const int c = wn0 + 32 * n + lr;
-      F.b[n] = st.b[slot(c, 2 * kh + J)];
-      F.bs[n] = s_b[2 * c + kh];
-    }
-#pragma unroll
-    for (int f = 0; f < FM; ++f) {
-      const int r = wm0 + 32 * f + lr;
-      F.dn[f] = st.a_dn[slot(r, 2 * kh + J)];
-      F.sp[f] = a_sp[2 * slot_sp(r, kh) + J];
-      F.mt[f] = M24 ? meta32[4 * r + 2 * kh + J] : meta[4 * r + 2 * kh + J];
-      F.ssp[f] = s_sp[2 * r + kh];
-      F.sdn[f] = s_dn[2 * r + kh];
-    }
-  };
-
-  v16f acc[FM][FN];
-#pragma unroll
-  for (int f = 0; f < FM; ++f)
-#pragma unroll
-    for (int n = 0; n < FN; ++n) acc[f][n] = (v16f){};
-
-  auto mfma_half = [&](const Frag& F, auto jc) {
-    constexpr int J = decltype(jc)::value;
-#pragma unroll
-    for (int f = 0; f < FM; ++f) {
-      const uint4 asp = M24 ? expand_24(F.sp[f].x, F.sp[f].y, F.mt[f]) : expand4_fast(F.sp[f].x, F.sp[f].y, F.mt[f]);
-#pragma unroll
-      for (int n = 0; n < FN; ++n) acc[f][n] = mfma32_fp4_sel<J>(asp, F.b[n], acc[f][n], F.ssp[f], F.bs[n]);
-#pragma unroll
-      for (int n = 0; n < FN; ++n) acc[f][n] = mfma32_fp4_sel<J>(F.dn[f], F.b[n], acc[f][n], F.sdn[f], F.bs[n]);
-    }
-  };
-
-  const std::integral_constant<int, 0> j0{};
-  const std::integral_constant<int, 1> j1{};
-  if constexpr (WN == 1) {
-    Frag f0, f1;
-    issue(0, lds[0]);
-    issue(min(1, KS - 1), lds[1]);
-    issue(min(2, KS - 1), lds[2]);
-    wait_vm_lgkm0<2 * NDMA>();
-    __builtin_amdgcn_s_barrier();
-    read(lds[0], f0, j0);
-    // the last step is peeled off so that the loop body is one basic block
-    // and the phase order below is the order of issue
-    for (int s = 0; s < KS - 1; ++s) {
-      Stage& cur = lds[s % kNS];
-      // the half-0 fragments were read a whole MFMA group ago; retiring them
-      // here keeps the wait for them from also covering the reads below
-      wait_lgkm0();
-      read(cur, f1, j1);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_half(f0, j0);
-      __builtin_amdgcn_sched_barrier(0);
-      // stage s+1 landed (stage s+2 may be in flight) and every wave is past
-      // its reads of the buffer of step s
-      wait_vm_lgkm0<NDMA>();
-      __builtin_amdgcn_s_barrier();
-      read(lds[(s + 1) % kNS], f0, j0);
-      // past the end the last step is reloaded into the idle buffer, so every
-      // step issues the same loads and one wait count fits all
-      issue(min(s + 3, KS - 1), cur);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_half(f1, j1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    read(lds[(KS - 1) % kNS], f1, j1);
-    mfma_half(f0, j0);
-    mfma_half(f1, j1);
-  } else {
-    // two waves per SIMD: the other wave covers this one's LDS latency, so
-    // fragments are read right before their MFMAs (single-buffered) and the
-    // loads run two steps ahead
-    Frag f;
-    issue(0, lds[0]);
-    issue(min(1, KS - 1), lds[1]);
-    for (int s = 0; s < KS; ++s) {
-      // stage s landed (s+1 may be in flight); after the barrier every wave is
-      // also past its reads of the buffer of step s-1, which stage s+2 reuses
-      wait_vm_lgkm0<NDMA>();
-      __builtin_amdgcn_s_barrier();
-      issue(min(s + 2, KS - 1), lds[(s + 2) % kNS]);
-      const Stage& cur = lds[s % kNS];
-      read(cur, f, j0);
-      mfma_half(f, j0);
-      read(cur, f, j1);
-      mfma_half(f, j1);
-    }
-  }
-  wait_vm_lgkm0<0>();                                  // no DMA may land after the tile ends
-
-  // ---- epilogue: fp32 store of the single accumulator tile
-#pragma unroll
-  for (int f = 0; f < FM; ++f) {
-#pragma unroll
-    for (int n = 0; n < FN; ++n) {
-      const int c = n0 + wn0 + 32 * n + lr;
-      if (c >= D) continue;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = m0 + wm0 + 32 * f + 8 * (i >> 2) + 4 * kh + (i & 3);
-        if (r < row_end) Y[(int64_t)r * ldy + c] = acc[f][n][i];
-      }
-    }
-  }
 }
 
 // ============================================================================
@@ -1267,50 +987,42 @@ hipError_t launch_linear_mx_impl(const uint8_t* bb_codes, const uint8_t* bb_meta
 #undef L
     return hipGetLastError();
   }
-  const int tiles_n = (D + kBN - 1) / kBN;
+  // the eight-wave tile (256 rows, 256 or 224 columns); K % 128 == 0 is
+  // checked by the caller, and K % 512 != 0 takes the instance whose last
+  // group of four steps is partial
+  if (K % 128 != 0) return hipErrorInvalidValue;
+  const bool partial = K % 512 != 0;
   if (n_groups == 1) {
+    // tile width 256 or 224: the one with fewer rounds x width over the CUs
     const int tiles_m = (rows + 255) / 256;
-    if (K % 128 == 0) {
-      // tile width 256 or 224: the one with fewer rounds x width over the CUs
-      const int ncu = num_cus_gemm();
-      const int t256 = tiles_m * ((D + 255) / 256), t224 = tiles_m * ((D + 223) / 224);
-      const bool narrow = (int64_t)((t224 + ncu - 1) / ncu) * 224 < (int64_t)((t256 + ncu - 1) / ncu) * 256;
+    const int ncu = num_cus_gemm();
+    const int t256 = tiles_m * ((D + 255) / 256), t224 = tiles_m * ((D + 223) / 224);
+    const bool narrow = (int64_t)((t224 + ncu - 1) / ncu) * 224 < (int64_t)((t256 + ncu - 1) / ncu) * 256;
 #define T8(BNE_, PARTIAL_)                                                                                            \
   hipLaunchKernelGGL((linear_mx_tile8<8, BNE_, false, false, M24, PARTIAL_>), dim3(narrow ? t224 : t256), dim3(512), 0, \
                      s, bb_codes, bb_meta, bb_scale, res_codes, res_scale, row_index, rows, act_rows, K, payload,       \
                      wscale, D, 1, nullptr, Y, ldy)
-      if (K % 512 == 0) {
-        if (narrow) T8(224, false);
-        else T8(256, false);
-      } else {
-        if (narrow) T8(224, true);
-        else T8(256, true);
-      }
-#undef T8
-      return hipGetLastError();
+    if (narrow) {
+      if (partial) T8(224, true);
+      else T8(224, false);
+    } else {
+      if (partial) T8(256, true);
+      else T8(256, false);
     }
-    hipLaunchKernelGGL((linear_mx_tile<256, false, 2, M24>), dim3(tiles_m * tiles_n), dim3(512), 0, s, bb_codes, bb_meta,
-                       bb_scale, res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, 1, group_offsets, Y,
-                       ldy);
+#undef T8
   } else {
-    // 256 x 256 tiles, eight waves (two per SIMD); measured on the MoE
-    // shapes faster than 128 x 256 with four (down 157 vs 199 us, up 146 vs
-    // 149 us) despite the emptier last row tile of each expert.  A bound on
-    // the tile count; surplus workgroups return at once.
-    const int bound = ((rows + 255) / 256 + n_groups) * tiles_n;
-    if (K % 128 == 0) {
+    // grouped: 256-wide tiles (measured on the MoE shapes, the general
+    // eight-wave tile of 256 x 256 was faster than 128 x 256 with four waves
+    // despite the emptier last row tile of each expert).  A bound on the
+    // tile count; surplus workgroups return at once.
+    const int bound = ((rows + 255) / 256 + n_groups) * ((D + 255) / 256);
 #define T8G(PARTIAL_)                                                                                                 \
   hipLaunchKernelGGL((linear_mx_tile8<8, 256, false, true, M24, PARTIAL_>), dim3(bound), dim3(512), 0, s, bb_codes,    \
                      bb_meta, bb_scale, res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, n_groups, \
                      group_offsets, Y, ldy)
-      if (K % 512 == 0) T8G(false);
-      else T8G(true);
+    if (partial) T8G(true);
+    else T8G(false);
 #undef T8G
-      return hipGetLastError();
-    }
-    hipLaunchKernelGGL((linear_mx_tile<256, true, 2, M24>), dim3(bound), dim3(512), 0, s, bb_codes, bb_meta, bb_scale,
-                       res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, n_groups, group_offsets, Y,
-                       ldy);
   }
   return hipGetLastError();
 }

@@ -37,21 +37,23 @@ from collections import defaultdict
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SOURCES = {
     "linear_mx_decode": ["gemm_mx.hip", "common.h", "prep_device.h"],
-    "linear_mx_tile": ["gemm_mx.hip", "common.h", "prep_device.h"],
+    "linear_mx_tile": ["gemm_mx.hip", "common.h", "prep_device.h"],   # linear_mx_tile8 instances
     "linear_nv_tile": ["gemm_nv.hip", "common.h"],
     "prepare_mx_kernel": ["prepare.hip", "common.h", "prep_device.h"],
 }
 # dispatch names a kernel's counters are averaged over (all substrings must
-# match): the decode step's GEMM is the two-launch form (template flag false)
+# match): the decode step's GEMM is the two-launch form on the 4:8 backbone
+# (linear_mx_decode<NK, CG, J, FUSED = false, M24 = false>)
 MATCH = {
-    "linear_mx_decode": ("linear_mx_decode<", ", false>"),
+    "linear_mx_decode": ("linear_mx_decode<", ", false, false>"),
     "linear_mx_tile": ("linear_mx_tile",),
     "linear_nv_tile": ("linear_nv_tile",),
     "prepare_mx_kernel": ("prepare_mx_kernel",),
 }
-# ... and none of these: the plain baseline's dense tile (template flag true)
+# ... and none of these: the plain baseline's dense tile
+# (linear_mx_tile8<8, BNE, DENSE = true, ...>)
 EXCLUDE = {
-    "linear_mx_tile": ("linear_mx_tile8<8, 224, true>", "linear_mx_tile8<8, 256, true>"),
+    "linear_mx_tile": ("linear_mx_tile8<8, 224, true,", "linear_mx_tile8<8, 256, true,"),
 }
 
 
@@ -77,14 +79,18 @@ def per_dispatch(path: str, counter: str) -> dict:
     return {d: (names[d], v) for d, v in vals.items()}
 
 
+def selects(kernel: str, name: str) -> bool:
+    """Whether dispatch `name` (as the profiler prints it) counts for `kernel`."""
+    return all(m in name for m in MATCH[kernel]) and not any(x in name for x in EXCLUDE.get(kernel, ()))
+
+
 def kernel_bytes(path: str, counter: str, kernel: str, copy_bytes: int):
     disp = per_dispatch(path, counter)
     copies = [v for n, v in disp.values() if "copyBuffer" in n]
     if not copies:
         raise SystemExit(f"{path}: no copyBuffer dispatch for the calibration")
     factor = copy_bytes / (max(copies) * 1024.0)
-    ks = [v for n, v in disp.values()
-          if all(m in n for m in MATCH[kernel]) and not any(x in n for x in EXCLUDE.get(kernel, ()))]
+    ks = [v for n, v in disp.values() if selects(kernel, n)]
     if not ks:
         raise SystemExit(f"{path}: no dispatch of {kernel}")
     return sum(ks) / len(ks) * 1024.0 * factor, factor, len(ks)
