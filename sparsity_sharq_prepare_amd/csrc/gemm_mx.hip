@@ -533,21 +533,25 @@ SHARQ_DEV v16f mfma32_fp4_sel(uint4 a, uint4 b, v16f c, uint32_t sa, uint32_t sb
 
 }  // namespace
 
-// Grouped tiles: tile `bid` of the concatenation, over experts in order, of
-// each expert's ceil(rows_e / BM) x tiles_n tiles.  Every thread below 256
-// loads one expert's offsets (coalesced), tile counts are prefix-summed
-// across the workgroup in `scan` (256 ints of LDS), and the thread whose
-// range holds the tile publishes it through `hit` (4 ints of LDS).  Needs at
-// least 256 threads; all threads must call it.  Returns false for a surplus
-// workgroup (uniform).
+// Grouped tiles: the tiles are the concatenation, over experts in order, of
+// each expert's ceil(rows_e / BM) x tiles_n tiles.  Workgroups reach the 8
+// XCDs round robin, so workgroup bid takes tile x q + min(x, r) + bid / 8
+// (x = bid % 8; q, r = total / 8, total % 8): each XCD works through one
+// contiguous stretch of the tile order and its L2 holds the few experts of
+// that stretch.  Every thread below 256 loads one expert's offsets
+// (coalesced), tile counts are prefix-summed across the workgroup in `scan`
+// (256 ints of LDS), and the thread whose range holds the tile publishes it
+// through `hit` (4 ints of LDS).  Needs at least 256 threads and n_groups >=
+// 1; all threads must call it.  Returns false for a surplus workgroup
+// (uniform).
 SHARQ_DEV bool find_group_tile(int bid, int n_groups, const int32_t* __restrict__ group_offsets, int rows, int BM,
                                int tiles_n, int* scan, int* hit, int& expert, int& start, int& count, int& tile) {
   const int tid = threadIdx.x;
   if (tid == 0) hit[0] = -1;
-  int carry = 0;
-  for (int e0 = 0; e0 < n_groups; e0 += 256) {        // uniform
+  // tile counts of experts e0 .. e0 + 255, inclusive prefix sums in scan[]
+  auto chunk = [&](int e0, int& st, int& cnt, int& te) {
     const int e = e0 + tid;
-    int st = 0, cnt = 0, te = 0;
+    st = 0, cnt = 0, te = 0;
     if (tid < 256 && e < n_groups) {
       st = min(max(group_offsets[e], 0), rows);
       cnt = min(max(group_offsets[e + 1], st), rows) - st;
@@ -561,10 +565,32 @@ SHARQ_DEV bool find_group_tile(int bid, int n_groups, const int32_t* __restrict_
       if (tid < 256) scan[tid] += v;
       __syncthreads();
     }
-    if (tid < 256 && e < n_groups) {
+  };
+  // the total tile count first (with one chunk, the locating pass has it)
+  int total = 0;
+  if (n_groups > 256) {
+    for (int e0 = 0; e0 < n_groups; e0 += 256) {      // uniform
+      int st, cnt, te;
+      chunk(e0, st, cnt, te);
+      total += scan[255];
+      __syncthreads();
+    }
+  }
+  int t = -1, carry = 0;
+  for (int e0 = 0; e0 < n_groups; e0 += 256) {        // uniform
+    int st, cnt, te;
+    chunk(e0, st, cnt, te);
+    if (e0 == 0) {
+      if (n_groups <= 256) total = scan[255];
+      if (bid < total) {
+        const int q = total >> 3, r = total & 7, x = bid & 7;
+        t = x * q + min(x, r) + (bid >> 3);
+      }
+    }
+    if (tid < 256 && e0 + tid < n_groups) {
       const int incl = carry + scan[tid], excl = incl - te;
-      if (bid >= excl && bid < incl) {
-        hit[0] = e; hit[1] = st; hit[2] = cnt; hit[3] = bid - excl;
+      if (t >= excl && t < incl) {
+        hit[0] = e0 + tid; hit[1] = st; hit[2] = cnt; hit[3] = t - excl;
       }
     }
     carry += scan[255];
@@ -578,22 +604,25 @@ SHARQ_DEV bool find_group_tile(int bid, int n_groups, const int32_t* __restrict_
 }
 
 // ============================================================================
-// prefill tile kernel, two waves per SIMD (K % 128 == 0)
+// tile kernel (more than 64 rows; plain and grouped; K % 128 == 0)
 // ============================================================================
-// Tile 256 x 256, eight waves, two per SIMD covering each other's LDS and
-// barrier latency; each wave holds a 128-register accumulator.  The layout
-// used is 8 x 1 (wave w: rows 32 w .., all 256 columns), so every backbone
-// fragment is expanded by one wave only (measured about 5% faster than 4 x 2
-// with 64 x 128 per wave, despite the larger weight-fragment reads).
+// Tile 256 x 256 (or 224 columns), eight waves, two per SIMD covering each
+// other's LDS and barrier latency; each wave holds a 128-register
+// accumulator.  The layout used is 8 x 1 (wave w: rows 32 w .., all
+// columns), so every backbone fragment is expanded by one wave only
+// (measured about 5% faster than 4 x 2 with 64 x 128 per wave, despite the
+// larger weight-fragment reads).
 //
 // Operand bytes per row and 128-step (codes: 64 B residual, 32 B backbone,
-// 64 B weight) go through a 3-deep LDS ring as before.  The small per-row
-// data (4 B of scales per row and step, 8 B of metadata) would cost one cache
-// line per 4-8 bytes if fetched per step, so it comes in groups of four steps
-// (16 B of scales, 32 B of metadata per row) into a double-buffered side
-// ring, fetched two steps before the group starts.  Every wave issues the
-// same loads (5 per step, 3 more on the third step of a group), so the
-// explicit wait counts are per step of a group: 5, 5, 5, 8.
+// 64 B weight) go through a 3-deep LDS ring.  The small per-row data (4 B of
+// scales per row and step, 8 B of 4:8 metadata) would cost one cache line per
+// 4-8 bytes if fetched per step, so it comes in groups of four steps (16 B of
+// scales, 32 B of metadata per row) into a double-buffered side ring,
+// fetched two steps before the group starts.  Every wave issues the same
+// loads (5 per step, 3 more on the third step of a group), so the explicit
+// wait counts are per step of a group: 5, 5, 5, 8.  The 2:4 backbone's
+// metadata (16 B per row and step) is staged with each step instead: 6 per
+// step, 2 more on the third step of a group.
 namespace {
 
 struct Tile8Main {
