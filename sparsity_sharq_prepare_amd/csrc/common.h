@@ -196,6 +196,16 @@ SHARQ_DEV uint32_t expand_group(uint32_t two, uint32_t nib) {
 }
 
 // activation row of output row r: row_index[r] clamped into [0, act_rows), or r
+// Tile of workgroup b among n (b < n).  Workgroups reach the 8 XCDs round
+// robin, so XCD x = b % 8 gets the contiguous stretch x q + min(x, r) ..
+// of the tile order (q, r = n / 8, n % 8), in dispatch order: the tiles that
+// run together on one XCD share operands through its L2.  A bijection on
+// [0, n) for every n.
+SHARQ_DEV int xcd_tile(int b, int n) {
+  const int q = n >> 3, r = n & 7, x = b & 7;
+  return x * q + min(x, r) + (b >> 3);
+}
+
 SHARQ_DEV int64_t gather_row(const int32_t* row_index, int r, int act_rows) {
   if (!row_index) return r;
   const int v = row_index[r];

@@ -534,11 +534,9 @@ SHARQ_DEV v16f mfma32_fp4_sel(uint4 a, uint4 b, v16f c, uint32_t sa, uint32_t sb
 }  // namespace
 
 // Grouped tiles: the tiles are the concatenation, over experts in order, of
-// each expert's ceil(rows_e / BM) x tiles_n tiles.  Workgroups reach the 8
-// XCDs round robin, so workgroup bid takes tile x q + min(x, r) + bid / 8
-// (x = bid % 8; q, r = total / 8, total % 8): each XCD works through one
-// contiguous stretch of the tile order and its L2 holds the few experts of
-// that stretch.  Every thread below 256 loads one expert's offsets
+// each expert's ceil(rows_e / BM) x tiles_n tiles; workgroup bid takes tile
+// xcd_tile(bid, total), so each XCD works through one contiguous stretch of
+// the tile order and its L2 holds the few experts of that stretch.  Every thread below 256 loads one expert's offsets
 // (coalesced), tile counts are prefix-summed across the workgroup in `scan`
 // (256 ints of LDS), and the thread whose range holds the tile publishes it
 // through `hit` (4 ints of LDS).  Needs at least 256 threads and n_groups >=
@@ -582,10 +580,7 @@ SHARQ_DEV bool find_group_tile(int bid, int n_groups, const int32_t* __restrict_
     chunk(e0, st, cnt, te);
     if (e0 == 0) {
       if (n_groups <= 256) total = scan[255];
-      if (bid < total) {
-        const int q = total >> 3, r = total & 7, x = bid & 7;
-        t = x * q + min(x, r) + (bid >> 3);
-      }
+      if (bid < total) t = xcd_tile(bid, total);
     }
     if (tid < 256 && e0 + tid < n_groups) {
       const int incl = carry + scan[tid], excl = incl - te;
@@ -692,8 +687,7 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
   if constexpr (!GROUPED) {
     const int tiles_m = (rows + BM - 1) / BM;
     const int nt = tiles_m * tiles_n;
-    int bi = blockIdx.x;
-    if ((nt & 7) == 0) bi = (bi & 7) * (nt >> 3) + (bi >> 3);
+    const int bi = xcd_tile(blockIdx.x, nt);
     constexpr int kBand = 4;
     const int band = bi / (kBand * tiles_n), band_m = min(kBand, tiles_m - band * kBand);
     const int in_band = bi - band * kBand * tiles_n;

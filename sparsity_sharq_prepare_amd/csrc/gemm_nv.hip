@@ -103,8 +103,7 @@ __global__ __launch_bounds__(512, 1) void linear_nv_tile(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tiles_m = (rows + kNM - 1) / kNM, tiles_n = (D + kNN - 1) / kNN;
   const int nt = tiles_m * tiles_n;
-  int bi = blockIdx.x;
-  if ((nt & 7) == 0) bi = (bi & 7) * (nt >> 3) + (bi >> 3);   // consecutive tiles on one XCD
+  const int bi = xcd_tile(blockIdx.x, nt);                    // consecutive tiles on one XCD
   const int m0 = (bi % tiles_m) * kNM, n0 = (bi / tiles_m) * kNN;
   const int KS = K / kKS;
   const uint32_t kA = K >> 2, kM = K >> 4, kS32 = K >> 5, kS16 = K >> 4, kR = K >> 1;
