@@ -25,8 +25,8 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-constexpr int kNM = 256;                  // tile rows
-constexpr int kNN = 128;                  // tile columns
+constexpr int kNM = 128;                  // tile rows
+constexpr int kNN = 256;                  // tile columns
 constexpr int kKS = 64;                   // K per step: two halves of 32 (one backbone block, two residual blocks each)
 
 // 32x32x16 f16: lane l holds row / column (l & 31), K-values 8 (l >> 5) .. +7
@@ -64,7 +64,7 @@ struct NvStage {
   uint4 a_sp[kNM * 8];        // backbone, fp16, 128 B per row
   uint4 a_dn[kNM * 8];        // residual
   uint4 b[kNN * 8];           // weight columns
-};                            // 80 KB; two stages fill the 160 KB of LDS
+};                            // 64 KB; two stages
 
 // expand 4 groups (8 compacted bytes + 4 metadata nibbles) into 16 code bytes
 SHARQ_DEV uint4 expand4(uint32_t c_lo, uint32_t c_hi, uint32_t meta16) {
@@ -79,15 +79,19 @@ SHARQ_DEV uint4 expand4(uint32_t c_lo, uint32_t c_hi, uint32_t meta16) {
 
 }  // namespace
 
-// Tile 256 x 128, eight waves (two per SIMD): wave w covers rows 32 w ..
-// and all 128 columns, with one accumulator per path (the two paths have
-// different tensor scales), 128 accumulator registers.  K advances 64 per step.
+// Tile 128 x 256, eight waves (two per SIMD): wave w covers rows 32 (w & 3)
+// .. and columns 128 (w >> 2) .., with one accumulator per path (the two
+// paths have different tensor scales), 128 accumulator registers.  K
+// advances 64 per step.  (The activation side costs most of the staging
+// work and is staged once per column tile, so the wider tile stages it half
+// as often as 256 x 128 did.)
 //
 // Staging (no DMA: operands are dequantized on the way).  A step's row of 64
 // values is split in two halves of 32 (one backbone scale block, two
-// residual ones); thread t stages half t & 1 of tile row t >> 1, and
-// threads below 256 also of weight column t >> 1, so the two lanes of a row
-// read adjacent bytes and one load instruction covers 32 rows.  Per step a thread
+// residual ones); thread t stages half t & 1 of weight column t >> 1, and
+// threads below 256 also of tile row t >> 1 (waves 0-3, one on each SIMD),
+// so the two lanes of a row read adjacent bytes and one load instruction
+// covers 32 rows.  Per step a thread
 // loads its halves (raw buffer loads; rows and columns outside the tile read
 // row 0, whose products reach only outputs that are never stored),
 // dequantizes them to fp16 and writes 16-byte chunks to LDS.  Loads run two
@@ -118,10 +122,10 @@ __global__ __launch_bounds__(512, 1) void linear_nv_tile(
   const __amdgpu_buffer_rsrc_t r_rs = rsrc(res_scale, (int64_t)an * kS16);
   const __amdgpu_buffer_rsrc_t r_w = rsrc(payload, (int64_t)D * kR), r_ws = rsrc(wscale, (int64_t)D * kS32);
 
-  // ---- staging roles: half h of row srow and (waves 0-3) of column scol
+  // ---- staging roles: half h of column scol and (waves 0-3) of row srow
   const uint32_t h = tid & 1;
-  const bool b_role = w < 4;                           // uniform per wave
-  const int srow[1] = {tid >> 1}, scol = (tid >> 1) & 127;
+  const bool a_role = w < 4;                           // uniform per wave
+  const int srow[1] = {(tid >> 1) & 127}, scol = tid >> 1;
   uint32_t ar[1];
   {
     const int gr = m0 + srow[0];
@@ -143,8 +147,8 @@ __global__ __launch_bounds__(512, 1) void linear_nv_tile(
   };
   auto load = [&](int s, Ld& L) {
     const uint32_t ss = (uint32_t)min(s, KS - 1);      // past the end: reload the last step (unused)
-#pragma unroll
-    for (int j = 0; j < 1; ++j) {
+    if (a_role) {
+      const int j = 0;
       const auto c = __builtin_amdgcn_raw_buffer_load_b64(r_bc, ar[j] * kA + 16u * ss + 8u * h, 0, 0);
       L.a[j].bc = make_uint2(c[0], c[1]);
       L.a[j].bm = __builtin_amdgcn_raw_buffer_load_b16(r_bm, ar[j] * kM + 4u * ss + 2u * h, 0, 0);
@@ -153,16 +157,14 @@ __global__ __launch_bounds__(512, 1) void linear_nv_tile(
       L.a[j].rc = make_uint4(r[0], r[1], r[2], r[3]);
       L.a[j].rsc = __builtin_amdgcn_raw_buffer_load_b16(r_rs, ar[j] * kS16 + 4u * ss + 2u * h, 0, 0);
     }
-    if (b_role) {
-      const auto b = __builtin_amdgcn_raw_buffer_load_b128(r_w, wc * kR + 32u * ss + 16u * h, 0, 0);
-      L.wcd = make_uint4(b[0], b[1], b[2], b[3]);
-      L.wsc = __builtin_amdgcn_raw_buffer_load_b8(r_ws, wc * kS32 + 2u * ss + h, 0, 0);
-    }
+    const auto b = __builtin_amdgcn_raw_buffer_load_b128(r_w, wc * kR + 32u * ss + 16u * h, 0, 0);
+    L.wcd = make_uint4(b[0], b[1], b[2], b[3]);
+    L.wsc = __builtin_amdgcn_raw_buffer_load_b8(r_ws, wc * kS32 + 2u * ss + h, 0, 0);
   };
   auto store = [&](const Ld& L, NvStage& S) {
     const int q0 = 4 * (int)h;                         // the half's first 16-byte chunk
-#pragma unroll
-    for (int j = 0; j < 1; ++j) {
+    if (a_role) {
+      const int j = 0;
       const LdA& A = L.a[j];
       const uint4 e = expand4(A.bc.x, A.bc.y, A.bm);
       const v2h dec = dec_h2(A.bsc & 0xFFu);
@@ -176,17 +178,15 @@ __global__ __launch_bounds__(512, 1) void linear_nv_tile(
       S.a_dn[nslot(srow[j], q0 + 2)] = dequant8_f16(A.rc.z, d1);
       S.a_dn[nslot(srow[j], q0 + 3)] = dequant8_f16(A.rc.w, d1);
     }
-    if (b_role) {
-      const v2h db = dec_h2(L.wsc & 0xFFu);
-      S.b[nslot(scol, q0 + 0)] = dequant8_f16(L.wcd.x, db);
-      S.b[nslot(scol, q0 + 1)] = dequant8_f16(L.wcd.y, db);
-      S.b[nslot(scol, q0 + 2)] = dequant8_f16(L.wcd.z, db);
-      S.b[nslot(scol, q0 + 3)] = dequant8_f16(L.wcd.w, db);
-    }
+    const v2h db = dec_h2(L.wsc & 0xFFu);
+    S.b[nslot(scol, q0 + 0)] = dequant8_f16(L.wcd.x, db);
+    S.b[nslot(scol, q0 + 1)] = dequant8_f16(L.wcd.y, db);
+    S.b[nslot(scol, q0 + 2)] = dequant8_f16(L.wcd.z, db);
+    S.b[nslot(scol, q0 + 3)] = dequant8_f16(L.wcd.w, db);
   };
 
   // ---- MFMA fragments and accumulators
-  const int wm0 = w * 32;
+  const int wm0 = (w & 3) * 32, wn0 = (w >> 2) * 128;
   const int kh = l >> 5, lr = l & 31;
   v16f acc_sp[1][4], acc_dn[1][4];
 #pragma unroll
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(512, 1) void linear_nv_tile(
       F.dn[f] = S.a_dn[nslot(wm0 + 32 * f + lr, q)];
     }
 #pragma unroll
-    for (int n = 0; n < 4; ++n) F.b[n] = S.b[nslot(32 * n + lr, q)];
+    for (int n = 0; n < 4; ++n) F.b[n] = S.b[nslot(wn0 + 32 * n + lr, q)];
   };
   auto mfma = [&](const Frag& F) {
 #pragma unroll
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(512, 1) void linear_nv_tile(
   for (int f = 0; f < 1; ++f) {
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-      const int c = n0 + 32 * n + lr;
+      const int c = n0 + wn0 + 32 * n + lr;
       if (c >= D) continue;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
