@@ -125,37 +125,29 @@ __global__ __launch_bounds__(512, 1) void linear_nv_tile(
   // ---- staging roles: half h of column scol and (waves 0-3) of row srow
   const uint32_t h = tid & 1;
   const bool a_role = w < 4;                           // uniform per wave
-  const int srow[1] = {(tid >> 1) & 127}, scol = tid >> 1;
-  uint32_t ar[1];
-  {
-    const int gr = m0 + srow[0];
-    ar[0] = gr < rows ? (uint32_t)gather_row(row_index, gr, act_rows) : 0u;
-  }
-  const int gc = n0 + scol;
+  const int srow = (tid >> 1) & 127, scol = tid >> 1;
+  const int gr = m0 + srow, gc = n0 + scol;
+  const uint32_t ar = gr < rows ? (uint32_t)gather_row(row_index, gr, act_rows) : 0u;
   const uint32_t wc = gc < D ? (uint32_t)gc : 0u;
 
-  struct LdA {
+  struct Ld {
     uint2 bc;            // backbone: compacted codes of the half's 4 groups
     uint32_t bm, bsc;    // backbone metadata (16 bits), scale byte
     uint4 rc;            // residual codes (16 B)
     uint32_t rsc;        // residual: two scale bytes
-  };
-  struct Ld {
-    LdA a[1];
     uint4 wcd;           // weight codes (16 B)
     uint32_t wsc;        // weight scale byte
   };
   auto load = [&](int s, Ld& L) {
     const uint32_t ss = (uint32_t)min(s, KS - 1);      // past the end: reload the last step (unused)
     if (a_role) {
-      const int j = 0;
-      const auto c = __builtin_amdgcn_raw_buffer_load_b64(r_bc, ar[j] * kA + 16u * ss + 8u * h, 0, 0);
-      L.a[j].bc = make_uint2(c[0], c[1]);
-      L.a[j].bm = __builtin_amdgcn_raw_buffer_load_b16(r_bm, ar[j] * kM + 4u * ss + 2u * h, 0, 0);
-      L.a[j].bsc = __builtin_amdgcn_raw_buffer_load_b8(r_bs, ar[j] * kS32 + 2u * ss + h, 0, 0);
-      const auto r = __builtin_amdgcn_raw_buffer_load_b128(r_rc, ar[j] * kR + 32u * ss + 16u * h, 0, 0);
-      L.a[j].rc = make_uint4(r[0], r[1], r[2], r[3]);
-      L.a[j].rsc = __builtin_amdgcn_raw_buffer_load_b16(r_rs, ar[j] * kS16 + 4u * ss + 2u * h, 0, 0);
+      const auto c = __builtin_amdgcn_raw_buffer_load_b64(r_bc, ar * kA + 16u * ss + 8u * h, 0, 0);
+      L.bc = make_uint2(c[0], c[1]);
+      L.bm = __builtin_amdgcn_raw_buffer_load_b16(r_bm, ar * kM + 4u * ss + 2u * h, 0, 0);
+      L.bsc = __builtin_amdgcn_raw_buffer_load_b8(r_bs, ar * kS32 + 2u * ss + h, 0, 0);
+      const auto r = __builtin_amdgcn_raw_buffer_load_b128(r_rc, ar * kR + 32u * ss + 16u * h, 0, 0);
+      L.rc = make_uint4(r[0], r[1], r[2], r[3]);
+      L.rsc = __builtin_amdgcn_raw_buffer_load_b16(r_rs, ar * kS16 + 4u * ss + 2u * h, 0, 0);
     }
     const auto b = __builtin_amdgcn_raw_buffer_load_b128(r_w, wc * kR + 32u * ss + 16u * h, 0, 0);
     L.wcd = make_uint4(b[0], b[1], b[2], b[3]);
@@ -164,19 +156,17 @@ __global__ __launch_bounds__(512, 1) void linear_nv_tile(
   auto store = [&](const Ld& L, NvStage& S) {
     const int q0 = 4 * (int)h;                         // the half's first 16-byte chunk
     if (a_role) {
-      const int j = 0;
-      const LdA& A = L.a[j];
-      const uint4 e = expand4(A.bc.x, A.bc.y, A.bm);
-      const v2h dec = dec_h2(A.bsc & 0xFFu);
-      S.a_sp[nslot(srow[j], q0 + 0)] = dequant8_f16(e.x, dec);
-      S.a_sp[nslot(srow[j], q0 + 1)] = dequant8_f16(e.y, dec);
-      S.a_sp[nslot(srow[j], q0 + 2)] = dequant8_f16(e.z, dec);
-      S.a_sp[nslot(srow[j], q0 + 3)] = dequant8_f16(e.w, dec);
-      const v2h d0 = dec_h2(A.rsc & 0xFFu), d1 = dec_h2((A.rsc >> 8) & 0xFFu);
-      S.a_dn[nslot(srow[j], q0 + 0)] = dequant8_f16(A.rc.x, d0);
-      S.a_dn[nslot(srow[j], q0 + 1)] = dequant8_f16(A.rc.y, d0);
-      S.a_dn[nslot(srow[j], q0 + 2)] = dequant8_f16(A.rc.z, d1);
-      S.a_dn[nslot(srow[j], q0 + 3)] = dequant8_f16(A.rc.w, d1);
+      const uint4 e = expand4(L.bc.x, L.bc.y, L.bm);
+      const v2h dec = dec_h2(L.bsc & 0xFFu);
+      S.a_sp[nslot(srow, q0 + 0)] = dequant8_f16(e.x, dec);
+      S.a_sp[nslot(srow, q0 + 1)] = dequant8_f16(e.y, dec);
+      S.a_sp[nslot(srow, q0 + 2)] = dequant8_f16(e.z, dec);
+      S.a_sp[nslot(srow, q0 + 3)] = dequant8_f16(e.w, dec);
+      const v2h d0 = dec_h2(L.rsc & 0xFFu), d1 = dec_h2((L.rsc >> 8) & 0xFFu);
+      S.a_dn[nslot(srow, q0 + 0)] = dequant8_f16(L.rc.x, d0);
+      S.a_dn[nslot(srow, q0 + 1)] = dequant8_f16(L.rc.y, d0);
+      S.a_dn[nslot(srow, q0 + 2)] = dequant8_f16(L.rc.z, d1);
+      S.a_dn[nslot(srow, q0 + 3)] = dequant8_f16(L.rc.w, d1);
     }
     const v2h db = dec_h2(L.wsc & 0xFFu);
     S.b[nslot(scol, q0 + 0)] = dequant8_f16(L.wcd.x, db);
@@ -185,41 +175,32 @@ __global__ __launch_bounds__(512, 1) void linear_nv_tile(
     S.b[nslot(scol, q0 + 3)] = dequant8_f16(L.wcd.w, db);
   };
 
-  // ---- MFMA fragments and accumulators
+  // ---- MFMA fragments and accumulators: rows wm0 + lr, columns wn0 + 32 n + lr
   const int wm0 = (w & 3) * 32, wn0 = (w >> 2) * 128;
   const int kh = l >> 5, lr = l & 31;
-  v16f acc_sp[1][4], acc_dn[1][4];
+  v16f acc_sp[4], acc_dn[4];
 #pragma unroll
-  for (int f = 0; f < 1; ++f)
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      acc_sp[f][n] = (v16f){};
-      acc_dn[f][n] = (v16f){};
-    }
+  for (int n = 0; n < 4; ++n) {
+    acc_sp[n] = (v16f){};
+    acc_dn[n] = (v16f){};
+  }
   struct Frag {
-    uint4 sp[1], dn[1], b[4];   // [f or n] of one 16-wide K slice
+    uint4 sp, dn, b[4];   // one 16-wide K slice
   };
   auto read = [&](const NvStage& S, int ks, Frag& F) {
     const int q = 2 * ks + kh;                         // chunk: K-values 8 q .. 8 q + 7
-#pragma unroll
-    for (int f = 0; f < 1; ++f) {
-      F.sp[f] = S.a_sp[nslot(wm0 + 32 * f + lr, q)];
-      F.dn[f] = S.a_dn[nslot(wm0 + 32 * f + lr, q)];
-    }
+    F.sp = S.a_sp[nslot(wm0 + lr, q)];
+    F.dn = S.a_dn[nslot(wm0 + lr, q)];
 #pragma unroll
     for (int n = 0; n < 4; ++n) F.b[n] = S.b[nslot(wn0 + 32 * n + lr, q)];
   };
   auto mfma = [&](const Frag& F) {
 #pragma unroll
-    for (int f = 0; f < 1; ++f)
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        acc_sp[f][n] = mfma_f16(F.sp[f], F.b[n], acc_sp[f][n]);
-        acc_dn[f][n] = mfma_f16(F.dn[f], F.b[n], acc_dn[f][n]);
-      }
+    for (int n = 0; n < 4; ++n) {
+      acc_sp[n] = mfma_f16(F.sp, F.b[n], acc_sp[n]);
+      acc_dn[n] = mfma_f16(F.dn, F.b[n], acc_dn[n]);
+    }
   };
-  // one step: fragments of the four K slices of stage S, then (behind the
-  // first slice's reads) the staging of the next step into N
   auto step = [&](const NvStage& S, const Ld& Lnext, NvStage& N) {
     Frag fr[2];
     read(S, 0, fr[0]);
@@ -251,16 +232,13 @@ __global__ __launch_bounds__(512, 1) void linear_nv_tile(
   // ---- epilogue: Y = s_w * (s_sp * acc_sp + s_dn * acc_dn)
   const float s_sp = a_ts[0], s_dn = a_ts[1], s_w = w_ts[0];
 #pragma unroll
-  for (int f = 0; f < 1; ++f) {
+  for (int n = 0; n < 4; ++n) {
+    const int c = n0 + wn0 + 32 * n + lr;
+    if (c >= D) continue;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int c = n0 + wn0 + 32 * n + lr;
-      if (c >= D) continue;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = m0 + wm0 + 32 * f + 8 * (i >> 2) + 4 * kh + (i & 3);
-        if (r < rows) Y[(int64_t)r * ldy + c] = s_w * (s_sp * acc_sp[f][n][i] + s_dn * acc_dn[f][n][i]);
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int r = m0 + wm0 + 8 * (i >> 2) + 4 * kh + (i & 3);
+      if (r < rows) Y[(int64_t)r * ldy + c] = s_w * (s_sp * acc_sp[n][i] + s_dn * acc_dn[n][i]);
     }
   }
 }
