@@ -338,7 +338,8 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const float* __restric
 // NVFP4 (emulated): phase 1 = RMSNorm + amax(y); phase 2 = mask, backbone
 // (E4M3 per 32 logical positions under s_sp), amax(R); phase 3 = residual
 // (E4M3 per 16 under s_dn).  Phases 2 and 3 recompute y from X with the
-// 1/rms saved by phase 1.
+// 1/rms saved by phase 1; phase 3 reads back the backbone phase 2 stored
+// (kept pairs, block scale, kept codes) to form R.
 // ============================================================================
 namespace {
 
@@ -477,15 +478,32 @@ __global__ __launch_bounds__(256) void prepare_nv_phase23(const void* __restrict
     float y[8];
     rr.get(c, y);
     if (ok) normalize(y, inv, gamma, 8 * (int64_t)g);
-    float gmax;
-    const uint32_t km = group_mask(y, gmax);
-    const uint32_t nib = mask_to_nibble(km);
-    // backbone block (32 logical positions) E4M3 scale under s_sp
-    const float bamax = quad_max(gmax);
-    const uint32_t sc_b = e4m3_encode(__fdiv_rn(__fdiv_rn(bamax, 6.0f), s_sp));
+    uint32_t km, nib, sc_b, bw;                         // kept pairs, metadata, block scale, pair codes
+    if constexpr (PHASE == 3) {
+      // the backbone phase 2 stored: metadata nibble, block scale and the two
+      // kept pair bytes (dropped pairs' codes stay zero; R does not use them)
+      uint32_t kb = 0u;
+      nib = 4u;
+      sc_b = 0u;
+      if (ok) {
+        const uint32_t mb = bb_meta[r * (K >> 4) + (g >> 1)];
+        nib = (g & 1) ? mb >> 4 : mb & 15u;
+        sc_b = bb_scale[r * (K >> 5) + (g >> 2)];
+        kb = *reinterpret_cast<const uint16_t*>(bb_codes + r * (K >> 2) + 2 * (int64_t)g);
+      }
+      const uint32_t i0 = nib & 3u, i1 = nib >> 2;
+      km = (1u << i0) | (1u << i1);
+      bw = ((kb & 0xFFu) << (8u * i0)) | ((kb >> 8) << (8u * i1));
+    } else {
+      float gmax;
+      km = group_mask(y, gmax);
+      nib = mask_to_nibble(km);
+      // backbone block (32 logical positions) E4M3 scale under s_sp
+      const float bamax = quad_max(gmax);
+      sc_b = e4m3_encode(__fdiv_rn(__fdiv_rn(bamax, 6.0f), s_sp));
+      bw = nv_codes8(y, __fmul_rn(e4m3_decode(sc_b), s_sp));
+    }
     const float dec_b = e4m3_decode(sc_b);
-    const float d_b = __fmul_rn(dec_b, s_sp);
-    const uint32_t bw = nv_codes8(y, d_b);
     float R[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
