@@ -146,6 +146,11 @@ sharq_status sharq_pack_weight(const void *W, int32_t dtype, int32_t K, int32_t 
  * R = y - X~_sp (exact in fp32) and its quantization.
  * X: (device) T x K of `dtype`, row t at X + t * ldx (ldx >= K).
  * gamma: (device) K fp32 RMSNorm weights, or NULL for no normalization (y = x).
+ * Input domain of the RMSNorm: every x_k * x_k and the row's sum of squares
+ * must be finite in fp32 (a single |x| above about 1.8e19 already overflows).
+ * Outside it the sum is +inf, 1/rms is 0 and the row is prepared as signed
+ * zeros (deterministic, identical to the fp32 order above; not a supported
+ * use).  Non-finite inputs give unspecified codes.
  * out: (host) struct describing (device) outputs sized by sharq_act_sizes.
  * workspace: (device) sharq_act_sizes()[6] bytes (NVFP4 tensor amax
  * partials; MXFP4 needs 0 and may pass NULL).

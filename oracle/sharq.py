@@ -87,12 +87,19 @@ def pairwise_sum_f32(a: np.ndarray) -> np.ndarray:
 
 
 def rmsnorm(x: np.ndarray, gamma, eps: float) -> np.ndarray:
-    """y = (x * inv_rms) * gamma in fp32; gamma None means no normalization."""
+    """y = (x * inv_rms) * gamma in fp32; gamma None means no normalization.
+
+    Input domain: every x_k * x_k and the row's sum of squares must be finite
+    in fp32 (one value of magnitude above about 1.8e19 already overflows).
+    Outside it S = +inf, inv = 1 / inf = 0 and the row comes out as signed
+    zeros; this is what fp32 arithmetic in the stated order gives, and it is
+    the documented behaviour of the library, not a supported use."""
     x = np.asarray(x, dtype=F32)
     if gamma is None:
         return x.copy()
     K = x.shape[-1]
-    S = pairwise_sum_f32(x * x)
+    with np.errstate(over="ignore"):
+        S = pairwise_sum_f32(x * x)
     ms = S / F32(K)
     r = np.sqrt(ms + F32(eps))
     inv = F32(1.0) / r
