@@ -194,15 +194,32 @@ sharq_status sharq_linear(const sharq_act *a, const sharq_weight *w, const int32
  * X, dtype, T, K, ldx, gamma, eps: as sharq_prepare; act: (host) MXFP4
  * activation buffers for T rows; w: (host) MXFP4 weight, n_groups == 1;
  * Y, ldy: as sharq_linear.
- * workspace: (device) >= 8 bytes, 16-byte aligned, all zero before the first
- * call; every call leaves it zero.  Calls that share a workspace must not
- * run concurrently.
+ * workspace: (device) >= 16 bytes, 16-byte aligned, all zero before the
+ * first call; the library keeps four uint32 words there across calls (a
+ * running count of prepared rows, a per-call base, a count of GEMM
+ * workgroups past their wait, a sticky error word).  Calls that share a
+ * workspace must not overlap: run them on one stream (or order them), and
+ * give each stream that calls concurrently its own workspace.
+ * Failure mode: a GEMM workgroup that waits for the prepared rows longer
+ * than a bound (about a second; a correct call waits microseconds) gives
+ * up, sets the sticky error word and writes NaN into its columns of Y; every
+ * later call on that workspace also writes NaN into Y until the caller
+ * clears the workspace.  The kernel always terminates.
+ * sharq_prepare_linear_status reports the word.
  * Errors: INVALID_ARGUMENT (also for NVFP4 or n_groups > 1),
  * UNSUPPORTED_SHAPE, FORMAT_MISMATCH, WORKSPACE_TOO_SMALL, HIP. */
 sharq_status sharq_prepare_linear(const void *X, int32_t dtype, int32_t T, int32_t K, int64_t ldx,
                                   const float *gamma, float eps, const sharq_act *act,
                                   const sharq_weight *w, float *Y, int64_t ldy, void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/* Status of a sharq_prepare_linear workspace: SHARQ_OK, or SHARQ_ERR_HIP when
+ * a single-launch decode on it gave up waiting (its Y holds NaN; see the
+ * failure mode above).  Unlike the other calls this one synchronizes: it
+ * copies the workspace's words to the host on `stream` and waits for them.
+ * workspace: (device) the workspace, >= 16 bytes, 16-byte aligned.
+ * Errors: WORKSPACE_TOO_SMALL, INVALID_ARGUMENT, HIP. */
+sharq_status sharq_prepare_linear_status(const void *workspace, size_t workspace_bytes, void *stream);
 
 /* ---- Plain baseline (the unfused pipeline the fused preparation replaces,
  * xllm-io paper review §5 kernel latency breakdown): RMSNorm, plain MXFP4

@@ -250,8 +250,8 @@ sharq_status sharq_prepare_linear(const void* X, int32_t dtype, int32_t T, int32
   if (w->n_groups != 1) return fail(SHARQ_ERR_INVALID_ARGUMENT, "sharq_prepare_linear is a plain linear (n_groups = 1)");
   if (sharq_status st = prepare_checks(X, dtype, T, K, ldx, gamma, eps, act, nullptr, 0)) return st;
   if (sharq_status st = linear_checks(act, w, nullptr, nullptr, T, Y, ldy)) return st;
-  if (!workspace || workspace_bytes < 8)
-    return fail(SHARQ_ERR_WORKSPACE_TOO_SMALL, "workspace needs 8 bytes, got %zu", workspace ? workspace_bytes : 0);
+  if (!workspace || workspace_bytes < 16)
+    return fail(SHARQ_ERR_WORKSPACE_TOO_SMALL, "workspace needs 16 bytes, got %zu", workspace ? workspace_bytes : 0);
   if (!aligned16(workspace)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == SHARQ_BF16;
@@ -267,6 +267,23 @@ sharq_status sharq_prepare_linear(const void* X, int32_t dtype, int32_t T, int32
   return from_hip(sharq::launch_linear_mx(act->bb_codes, act->bb_meta, act->bb_scale, act->res_codes, act->res_scale,
                                           nullptr, T, T, K, w->payload, w->scale_sp, w->D, 1, nullptr, Y, ldy, s),
                   "sharq_prepare_linear launch");
+}
+
+sharq_status sharq_prepare_linear_status(const void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || workspace_bytes < 16)
+    return fail(SHARQ_ERR_WORKSPACE_TOO_SMALL, "workspace needs 16 bytes, got %zu", workspace ? workspace_bytes : 0);
+  if (!aligned16(workspace)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  uint32_t words[4] = {0, 0, 0, 0};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (sharq_status st = from_hip(hipMemcpyAsync(words, workspace, sizeof(words), hipMemcpyDeviceToHost, s),
+                                 "sharq_prepare_linear_status copy"))
+    return st;
+  if (sharq_status st = from_hip(hipStreamSynchronize(s), "sharq_prepare_linear_status synchronize")) return st;
+  if (words[3] != 0)
+    return fail(SHARQ_ERR_HIP,
+                "a single-launch decode on this workspace gave up waiting for its prepared rows; its Y was "
+                "written as NaN (clear the workspace to zero before reusing it)");
+  return ok();
 }
 
 sharq_status sharq_rmsnorm(const void* X, int32_t dtype, int32_t T, int32_t K, int64_t ldx, const float* gamma,

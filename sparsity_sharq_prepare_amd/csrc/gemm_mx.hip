@@ -12,15 +12,20 @@
 // the low nibble), with that 32-block's scale byte; the result lane l holds
 // column (l & 15), rows 4 * (l >> 4) .. +3.
 //
-// Two kernels:
-//  - skinny (decode, T <= 64): weight streaming.  A 16-row MFMA tile holds the
+// Three kernels:
+//  - skinny (T <= 64): weight streaming.  A 16-row MFMA tile holds the
 //    backbone of 8 tokens in rows 0-7 and their residual in rows 8-15, so one
 //    MFMA applies a weight fragment to both paths; the epilogue adds row r and
 //    row r + 8 of the tile.  K is split over the waves of a workgroup and the
 //    partial tiles are summed in a fixed order through LDS.
-//  - tile (prefill and grouped MoE): 256-column tiles, 256 (or 128) rows, K
-//    steps of 128 staged through double-buffered LDS; the backbone is expanded
-//    from its compacted bytes while staging.
+//  - decode (T <= 8): the skinny scheme with the activation side staged once
+//    per workgroup in LDS in operand form, optionally fused with the
+//    preparation of the rows (single-launch decode).
+//  - tile8 (prefill and grouped MoE, more than 64 rows): 256 rows x 256 (or
+//    224) columns, eight waves, K steps of 128 staged by buffer->LDS DMA
+//    through a 3-deep ring (scales and metadata in a side ring of four-step
+//    groups); the compacted backbone is staged as is and expanded in
+//    registers right before its MFMAs.
 #include "common.h"
 #include "kernels.h"
 #include "prep_device.h"
@@ -220,19 +225,32 @@ __global__ __launch_bounds__(MT >= 8 ? 512 : 1024) void linear_mx_skinny(
 // also prepare one activation row each (RowPrep: the standalone prepare's
 // outputs, bit for bit): they load the row and gamma, then their weights,
 // quantize and store the row with write-through stores, wait until all of it
-// is done, and increment sync[0] at memory.  (A release that writes the L2
-// back costs microseconds; write-through stores need none.)  Workgroups go to
-// the 8 XCDs round robin, so all producers share XCD 0 and its L2.  Every GEMM workgroup issues its weight loads,
-// then waits (one lane, bounded polling) until sync[0] reaches rows, and only
-// then loads the prepared activations with ordinary loads: on XCD 0 they hit
-// the producers' L2, elsewhere the L2 holds no line of these buffers (caches
-// are invalidated at kernel start and nothing reads them before the wait), so
-// the first read fetches the written-back bytes and later ones hit.  The
-// weight stream overlaps the preparation.  Workgroups are dispatched in index
-// order on every XCD and the producers come first on XCD 0, so they are
-// resident before any waiting workgroup can hold their place.  The last GEMM
-// workgroup past the wait resets sync[0] and sync[1] to zero for the next
-// call.
+// is done, and increment the done counter at memory.  (A release that writes
+// the L2 back costs microseconds; write-through stores need none.)
+// Workgroups go to the 8 XCDs round robin, so all producers share XCD 0 and
+// its L2.  Every GEMM workgroup issues its weight loads, then waits (one lane,
+// bounded polling) until the done counter reaches this call's target, and
+// only then loads the prepared activations with ordinary loads: on XCD 0 they
+// hit the producers' L2, elsewhere the L2 holds no line of these buffers
+// (caches are invalidated at kernel start and nothing reads them before the
+// wait), so the first read fetches the written-back bytes and later ones hit.
+// The weight stream overlaps the preparation.  Workgroups are dispatched in
+// index order on every XCD and the producers come first on XCD 0, so they
+// are resident before any waiting workgroup can hold their place.
+//
+// Workspace words (uint32): sync[0] counts finished producer rows over all
+// calls (it is never reset, so an increment can only count for its own call
+// or an earlier one); sync[2] is this call's base, the value sync[0] holds
+// once every earlier call's producers are done, so the wait is for
+// sync[0] - sync[2] >= rows (modulo 2^32); sync[1] counts the GEMM
+// workgroups past the wait, and the last one sets sync[2] += rows and
+// sync[1] = 0 for the next call.  sync[3] is a sticky error word: a GEMM
+// workgroup whose wait gives up (kFusedSpinMax polls, about a second; a
+// correct call waits microseconds) sets it, and every GEMM workgroup that
+// finds it set writes NaN to its Y columns instead of computing them, so a
+// failed wait is never a silently wrong Y.  The caller clears a workspace
+// (all zero) before first use and after an error; sharq_prepare_linear_status
+// reads the word.
 constexpr int kDecodeMaxK = 16384;                   // staged operand + reduction fit in LDS
 constexpr uint32_t kFusedSpinMax = 1u << 20;         // polls before giving up (the kernel always ends)
 constexpr int kAuxWriteThrough = 16;                 // store cache policy sc1: written through to memory
@@ -243,7 +261,7 @@ struct FusedPrep {
   int64_t ldx;
   const float* gamma;          // RMSNorm weights or null (no normalization)
   float eps;
-  uint32_t* sync;              // [2] counters, zero between calls
+  uint32_t* sync;              // [4]: done rows, GEMM workgroups past the wait, base, sticky error
 };
 
 template <int NK, int CG, int J, bool FUSED, bool M24 = false>
@@ -393,18 +411,37 @@ __global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
       if (tid == 0) __hip_atomic_fetch_add(&fp.sync[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       if (bx >= n_gemm) return;                      // producer only (tiny D)
     }
+    __shared__ uint32_t failed;
     if (tid == 0) {
-      for (uint32_t it = 0; it < kFusedSpinMax; ++it) {
-        if (__hip_atomic_load(&fp.sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)rows) break;
-        __builtin_amdgcn_s_sleep(2);
+      const uint32_t base = __hip_atomic_load(&fp.sync[2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      uint32_t bad = __hip_atomic_load(&fp.sync[3], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (!bad) {
+        uint32_t it = 0;
+        for (; it < kFusedSpinMax; ++it) {
+          const uint32_t done = __hip_atomic_load(&fp.sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((int32_t)(done - base - (uint32_t)rows) >= 0) break;
+          __builtin_amdgcn_s_sleep(2);
+        }
+        if (it == kFusedSpinMax) {                   // gave up: never compute from unready activations
+          bad = 1u;
+          __hip_atomic_fetch_or(&fp.sync[3], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
+      failed = bad;
       const uint32_t n = __hip_atomic_fetch_add(&fp.sync[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (n + 1 == (uint32_t)n_gemm) {               // every GEMM workgroup is past the wait
         __hip_atomic_store(&fp.sync[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&fp.sync[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&fp.sync[2], base + (uint32_t)rows, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     __syncthreads();
+    if (failed) {                                    // uniform: NaN in this workgroup's outputs
+      for (int i = tid; i < 8 * 16 * CG; i += NT) {
+        const int t = i / (16 * CG), c = bx * 16 * CG + i % (16 * CG);
+        if (t < rows && c < D) Y[(int64_t)t * ldy + c] = __builtin_nanf("");
+      }
+      return;
+    }
     load_act();
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -720,11 +757,14 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
   const int4v r_b = make_rsrc(payload + (int64_t)grp * D * kR, (uint32_t)D * kR);
   const int4v r_sb = make_rsrc(wscale + (int64_t)grp * D * kS, (uint32_t)D * kS);
 
-  // activation row of tile row r (rows past the tile's end read row 0: their
-  // products reach only outputs that are never stored)
-  auto act_row = [&](int r) -> uint32_t {
+  // byte offset of tile row r's activation row at `bytes` per row; rows past
+  // the tile's end (the last row tile of the matrix or of an expert) get an
+  // offset past every buffer, so their DMAs load zeros without a memory
+  // request (their products reach only outputs that are never stored)
+  constexpr uint32_t kAbsent = 0x80000000u;
+  auto act_off = [&](int r, uint32_t bytes) -> uint32_t {
     const int gr = m0 + r;
-    return gr < row_end ? (uint32_t)gather_row(row_index, gr, act_rows) : 0u;
+    return gr < row_end ? (uint32_t)gather_row(row_index, gr, act_rows) * bytes : kAbsent;
   };
   auto w_row = [&](int c) -> uint32_t { return n0 + c < D ? (uint32_t)(n0 + c) : 0u; };
 
@@ -733,7 +773,7 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int sl = 64 * (w + 8 * j) + l, row = sl >> 2, q = (sl & 3) ^ swz(row);
-    o_dn[j] = act_row(row) * kR + 16 * q;
+    o_dn[j] = act_off(row, kR) + 16 * q;
     // staged columns past the tile's BNE are never read: an offset past the
     // buffer loads zeros without a memory request
     o_b[j] = row < BNE ? w_row(row) * kR + 16 * q : 0x80000000u;
@@ -741,14 +781,14 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
   uint32_t o_sp;
   {
     const int sl = 64 * w + l, row = sl >> 1, h = (sl & 1) ^ ((row >> 3) & 1);
-    o_sp = act_row(row) * kA + 16 * h;
+    o_sp = act_off(row, kA) + 16 * h;
   }
   // 4:8: 2 lanes x 16 B per row and side group; 2:4: 16 B per row and step,
   // waves w and w + 4 loading the same rows (same bytes to the same place)
-  const uint32_t o_mt = M24 ? act_row(64 * wq + l) * kM : act_row((64 * w + l) >> 1) * kM + 16 * (l & 1);
+  const uint32_t o_mt = M24 ? act_off(64 * wq + l, kM) : act_off((64 * w + l) >> 1, kM) + 16 * (l & 1);
   // waves 0-3: backbone scale rows and weight scale columns 64 wq + l;
   // waves 4-7: residual scale rows and the same weight columns again
-  const uint32_t o_sa = act_row(64 * wq + l) * kS;
+  const uint32_t o_sa = act_off(64 * wq + l, kS);
   const uint32_t o_sw = 64 * wq + l < BNE ? w_row(64 * wq + l) * kS : 0x80000000u;
   const int4v r_sa = w < 4 ? r_ssp : r_sdn;
 
@@ -775,6 +815,11 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
 
   const int wm0 = (w % WROWS) * WM, wn0 = (w / WROWS) * WNC;
   const int kh = l >> 5, lr = l & 31;
+  // a wave whose rows all lie past the tile's end (an expert's or the
+  // matrix's last row tile) issues its share of the DMAs and takes every
+  // barrier, but reads no fragments and issues no MFMAs, leaving its SIMD's
+  // matrix core to the other wave there (uniform per wave)
+  const bool live = m0 + wm0 < row_end;
   // per step: scales (both halves: op_sel picks the byte), metadata (low /
   // high 16 bits) and the compacted backbone (low / high 8 bytes) are read
   // once; per half-step only the weight and residual code fragments
@@ -865,15 +910,18 @@ __global__ __launch_bounds__(512, 1) void linear_mx_tile8(
       issue_main(min(s + 2, KS - 1), lds[(s + 2) % kNS]);
       // side group g+1 replaces group g-1, last read at step 4 g - 1
       if (p == 2) issue_side(min(g + 1, G - 1), side[(g + 1) & 1]);
-      const MainT& cur = lds[s % kNS];
-      read_step(cur, sd, p, sf);
-      read_half(cur, hf, j0);
-      mfma_half(sf, hf, j0);
-      read_half(cur, hf, j1);
-      mfma_half(sf, hf, j1);
+      if (live) {
+        const MainT& cur = lds[s % kNS];
+        read_step(cur, sd, p, sf);
+        read_half(cur, hf, j0);
+        mfma_half(sf, hf, j0);
+        read_half(cur, hf, j1);
+        mfma_half(sf, hf, j1);
+      }
     }
   }
   wait_vm_lgkm0<0>();                                  // no DMA may land after the tile ends
+  if (!live) return;
 
   // ---- epilogue: fp32 store of the accumulator tile
 #pragma unroll

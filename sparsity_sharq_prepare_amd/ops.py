@@ -157,18 +157,28 @@ def linear(act: PreparedAct, w: PackedWeight, group_offsets: Optional[torch.Tens
     return out
 
 
-# per-device zeroed 16-byte workspaces of prepare_linear (its counters are
-# left zero by every call); calls on one device are stream-ordered here
+# default prepare_linear workspaces (16 bytes, zero before first use), one
+# per (device, stream): calls that share a workspace must not overlap, and
+# calls on one stream never do
 _PL_WS: dict = {}
 
 
-def _prepare_linear_ws(device: torch.device) -> torch.Tensor:
-    key = (device.type, device.index if device.index is not None else torch.cuda.current_device())
+def _prepare_linear_ws(device: torch.device, stream=None) -> torch.Tensor:
+    dev = device.index if device.index is not None else torch.cuda.current_device()
+    key = (device.type, dev, _stream_ptr(stream))
     ws = _PL_WS.get(key)
     if ws is None:
         ws = torch.zeros(16, dtype=torch.uint8, device=device)
         _PL_WS[key] = ws
     return ws
+
+
+def prepare_linear_status(workspace: torch.Tensor, stream=None) -> None:
+    """Raise SharqError if a single-launch decode on ``workspace`` gave up
+    waiting for its prepared rows (its Y was written as NaN).  Synchronizes
+    the stream."""
+    _dev_check(workspace)
+    L.check(L.lib().sharq_prepare_linear_status(workspace.data_ptr(), workspace.numel(), _stream_ptr(stream)))
 
 
 def prepare_linear(X: torch.Tensor, gamma: Optional[torch.Tensor], w: PackedWeight, eps: float = 1e-6,
@@ -183,7 +193,7 @@ def prepare_linear(X: torch.Tensor, gamma: Optional[torch.Tensor], w: PackedWeig
     act = act or empty_act(w.fmt, T, K, X.device)
     if out is None:
         out = torch.empty((T, w.D), dtype=torch.float32, device=X.device)
-    ws = workspace if workspace is not None else _prepare_linear_ws(X.device)
+    ws = workspace if workspace is not None else _prepare_linear_ws(X.device, stream)
     L.check(L.lib().sharq_prepare_linear(X.data_ptr(), _dtype_code(X), T, K, X.stride(0), _ptr(gamma), eps,
                                          act.struct(), w.struct(), out.data_ptr(), out.stride(0), ws.data_ptr(),
                                          ws.numel(), _stream_ptr(stream)))

@@ -158,6 +158,11 @@ def test_prepare_linear_validation_errors():
     # workspace missing, too small, misaligned
     assert f(X, 1, 8, 256, 256, None, 1e-6, a, w, Y, 64, None, 0, None) == L.SHARQ_ERR_WORKSPACE_TOO_SMALL
     assert f(X, 1, 8, 256, 256, None, 1e-6, a, w, Y, 64, ws, 4, None) == L.SHARQ_ERR_WORKSPACE_TOO_SMALL
+    assert f(X, 1, 8, 256, 256, None, 1e-6, a, w, Y, 64, ws, 8, None) == L.SHARQ_ERR_WORKSPACE_TOO_SMALL
+    # the status query checks its workspace argument before any copy
+    assert lib.sharq_prepare_linear_status(None, 16, None) == L.SHARQ_ERR_WORKSPACE_TOO_SMALL
+    assert lib.sharq_prepare_linear_status(ws, 8, None) == L.SHARQ_ERR_WORKSPACE_TOO_SMALL
+    assert lib.sharq_prepare_linear_status(ws + 4, 16, None) == L.SHARQ_ERR_INVALID_ARGUMENT
     assert f(X, 1, 8, 256, 256, None, 1e-6, a, w, Y, 64, ws + 4, 16, None) == L.SHARQ_ERR_INVALID_ARGUMENT
     # activation / weight K differ; act describes other rows; K % 128 != 0
     assert f(X, 1, 8, 256, 256, None, 1e-6, a, _fake_weight(K=512), Y, 64, ws, 16, None) == \

@@ -400,8 +400,10 @@ def test_prepare_linear_shapes(T, K, D, dtype, gamma):
         assert torch.equal(getattr(act, k), getattr(act2, k)), k
         assert torch.equal(getattr(act3, k), getattr(act2, k)), k
     assert torch.equal(Y, Y2) and torch.equal(Y3, Y2)
-    ws = ops._prepare_linear_ws(X.device)
-    assert int(ws.view(torch.int32)[:2].abs().sum()) == 0
+    # workspace words: rows done (running), workgroups past the wait (0
+    # between calls), base (= rows done once every call has finished), sticky error
+    words = ops._prepare_linear_ws(X.device).view(torch.int32).cpu().tolist()
+    assert words[1] == 0 and words[3] == 0 and words[0] == words[2]
 
 
 @pytest.mark.parametrize("i", range(3), ids=DECODE_IDS)
@@ -435,7 +437,41 @@ def test_prepare_linear_sequence_and_own_workspace():
     torch.cuda.synchronize()
     for Y, Y2 in outs:
         assert torch.equal(Y, Y2)
-    assert int(ws.abs().sum()) == 0
+    words = ws.view(torch.int32).cpu().tolist()
+    assert words[1] == 0 and words[3] == 0 and words[0] == words[2] == 8 + 1 + 4 + 8
+    ops.prepare_linear_status(ws)
+
+
+def test_prepare_linear_wait_give_up_is_loud():
+    # a workspace whose base lies far ahead of its running count: the wait can
+    # never be satisfied, so every GEMM workgroup gives up after its bounded
+    # polling (the kernel ends normally), sets the sticky error word and writes
+    # NaN into Y; later calls on that workspace keep writing NaN; a cleared
+    # workspace works again
+    T, K, D = 4, 512, 96
+    case = synth.random_case(808, T, K, D)
+    X, g = dev_x(case), dev_gamma(case.gamma)
+    w = ops.pack_weight(dev_w(case.w, case.dtype))
+    ws = torch.zeros(4, dtype=torch.int32, device="cuda")
+    ws[2] = 0x40000000
+    wsb = ws.view(torch.uint8)
+    act, Y = ops.prepare_linear(X, g, w, workspace=wsb)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(Y).all())
+    compare_act(act, oracle_prepare(case))          # the producers still wrote their rows
+    from sparsity_sharq_prepare_amd import _lib
+    with pytest.raises(_lib.SharqError) as ei:
+        ops.prepare_linear_status(wsb)
+    assert ei.value.status == _lib.SHARQ_ERR_HIP
+    _, Y2 = ops.prepare_linear(X, g, w, workspace=wsb)   # sticky: NaN again, no wait
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(Y2).all())
+    ws.zero_()
+    _, Y3 = ops.prepare_linear(X, g, w, workspace=wsb)
+    Yref = ops.linear(ops.prepare(X, g, 1e-6), w)
+    torch.cuda.synchronize()
+    assert torch.equal(Y3, Yref)
+    ops.prepare_linear_status(wsb)
 
 
 def test_prepare_linear_graph_replay():
