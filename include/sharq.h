@@ -160,6 +160,20 @@ sharq_status sharq_prepare(const void *X, int32_t dtype, int32_t T, int32_t K, i
                            const float *gamma, float eps, const sharq_act *out,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* Allocation-free sharq_prepare, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same outputs as sharq_prepare, bit for bit, with
+ * the NVFP4 preparation's scratch taken from a static device array of the
+ * library (1 MiB per GPU, held until the process ends) instead of a caller
+ * workspace.  MXFP4 formats need no scratch.  Calls that overlap on one GPU
+ * share that array and race: order them (one stream, or events).  Nothing
+ * is allocated; the array's device address is looked up once per device.
+ * Arguments as sharq_prepare.  Errors: as sharq_prepare, and
+ * UNSUPPORTED_SHAPE when the NVFP4 scratch (4 T + 8 ceil(T / rows per
+ * workgroup) + 256 bytes, sharq_act_sizes()[6]) exceeds 1 MiB. */
+sharq_status sharq_prepare_no_alloc(const void *X, int32_t dtype, int32_t T, int32_t K, int64_t ldx,
+                                    const float *gamma, float eps, const sharq_act *out, void *stream);
+
 /* Dual-path FP4 GEMM (review §3.4-§3.5): Y^ = X~_sp W~ + R~ W~ with one
  * accumulator per output tile (the dense path accumulates into the sparse
  * path's tile); the backbone runs zero-filled through dense scaled MFMA

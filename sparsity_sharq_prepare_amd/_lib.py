@@ -28,7 +28,8 @@ SHARQ_BF16 = 1
 FORMATS = {"mxfp4": SHARQ_MXFP4, "nvfp4": SHARQ_NVFP4_EMU, "mxfp4_24": SHARQ_MXFP4_24}
 
 # every entry point include/sharq.h declares
-EXPORTS = ("sharq_weight_sizes", "sharq_act_sizes", "sharq_pack_weight", "sharq_prepare", "sharq_linear",
+EXPORTS = ("sharq_weight_sizes", "sharq_act_sizes", "sharq_pack_weight", "sharq_prepare", "sharq_prepare_no_alloc",
+           "sharq_linear",
            "sharq_prepare_linear", "sharq_prepare_linear_status", "sharq_rmsnorm", "sharq_quantize_mx", "sharq_linear_dense",
            "sharq_status_string", "sharq_last_error")
 
@@ -67,6 +68,8 @@ def lib() -> ctypes.CDLL:
                                         POINTER(SharqWeight), c_void_p, c_size_t, c_void_p]
         L.sharq_prepare.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_int64, c_void_p, c_float,
                                     POINTER(SharqAct), c_void_p, c_size_t, c_void_p]
+        L.sharq_prepare_no_alloc.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_int64, c_void_p, c_float,
+                                             POINTER(SharqAct), c_void_p]
         L.sharq_linear.argtypes = [POINTER(SharqAct), POINTER(SharqWeight), c_void_p, c_void_p, c_int32,
                                    c_void_p, c_int64, c_void_p]
         L.sharq_prepare_linear.argtypes = [c_void_p, c_int32, c_int32, c_int32, c_int64, c_void_p, c_float,
@@ -78,7 +81,8 @@ def lib() -> ctypes.CDLL:
         L.sharq_quantize_mx.argtypes = [c_void_p, c_int32, c_int32, c_int64, c_void_p, c_void_p, c_void_p]
         L.sharq_linear_dense.argtypes = [c_void_p, c_void_p, c_int32, POINTER(SharqWeight), c_void_p, c_int64,
                                          c_void_p]
-        for name in ("sharq_weight_sizes", "sharq_act_sizes", "sharq_pack_weight", "sharq_prepare", "sharq_linear",
+        for name in ("sharq_weight_sizes", "sharq_act_sizes", "sharq_pack_weight", "sharq_prepare",
+                     "sharq_prepare_no_alloc", "sharq_linear",
                      "sharq_prepare_linear", "sharq_prepare_linear_status", "sharq_rmsnorm", "sharq_quantize_mx", "sharq_linear_dense"):
             getattr(L, name).restype = c_int32
         L.sharq_status_string.argtypes = [c_int32]

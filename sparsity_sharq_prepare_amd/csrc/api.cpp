@@ -225,6 +225,24 @@ sharq_status sharq_prepare(const void* X, int32_t dtype, int32_t T, int32_t K, i
                   "sharq_prepare launch");
 }
 
+sharq_status sharq_prepare_no_alloc(const void* X, int32_t dtype, int32_t T, int32_t K, int64_t ldx,
+                                    const float* gamma, float eps, const sharq_act* out, void* stream) {
+  if (!out) return fail(SHARQ_ERR_INVALID_ARGUMENT, "X and out must not be NULL");
+  size_t sz[7];
+  if (sharq_status st = sharq_act_sizes(out->fmt, T, K, sz)) return st;
+  void* scratch = nullptr;
+  if (sz[6] > 0) {
+    if (sz[6] > sharq::scratch_max_bytes())
+      return fail(SHARQ_ERR_UNSUPPORTED_SHAPE,
+                  "T = %d needs %zu bytes of scratch; the allocation-free prepare holds %zu (use sharq_prepare "
+                  "with a workspace)",
+                  T, sz[6], sharq::scratch_max_bytes());
+    if (sharq_status st = from_hip(sharq::scratch_device_ptr(&scratch), "sharq_prepare_no_alloc scratch lookup"))
+      return st;
+  }
+  return sharq_prepare(X, dtype, T, K, ldx, gamma, eps, out, scratch, sz[6], stream);
+}
+
 sharq_status sharq_linear(const sharq_act* a, const sharq_weight* w, const int32_t* group_offsets,
                           const int32_t* row_index, int32_t total_rows, float* Y, int64_t ldy, void* stream) {
   if (sharq_status st = linear_checks(a, w, group_offsets, row_index, total_rows, Y, ldy)) return st;

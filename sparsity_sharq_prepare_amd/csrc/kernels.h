@@ -16,6 +16,10 @@ namespace sharq {
 // largest K the register-resident prepare kernels handle
 int prepare_max_k();
 size_t prepare_nv_workspace(int T, int K);
+// the file-scope scratch of the allocation-free prepare: its size, and the
+// current device's address of it (looked up once per device)
+size_t scratch_max_bytes();
+hipError_t scratch_device_ptr(void** out);
 size_t pack_nv_workspace(int K, int D, int n_groups);
 
 // m24: the 2:4 element-wise backbone (metadata K/8 bytes per row) instead of 4:8 in pairs

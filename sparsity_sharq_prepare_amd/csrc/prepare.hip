@@ -14,6 +14,9 @@
 // tree, a butterfly over the wave combines aligned 512-value blocks, waves of
 // the row combine in order through LDS, and the chunks are combined as a tree.
 // Every fp32 operation rounds to nearest even, without contraction.
+#include <mutex>
+#include <unordered_map>
+
 #include "common.h"
 #include "kernels.h"
 #include "prep_device.h"
@@ -645,6 +648,42 @@ PrepGeom prep_geometry_mx(int T, int K) {
 }  // namespace
 
 int prepare_max_k() { return 256 * 8 * 16; }
+
+// ---- static scratch of the allocation-free prepare (sharq_prepare_no_alloc)
+// The NVFP4 preparation needs prepare_nv_workspace(T, K) bytes of scratch
+// (per-row 1/rms and per-workgroup partial maxima).  Callers that cannot
+// allocate get it from this file-scope array instead: each GPU the library
+// runs on holds its own copy until the process ends.  Every block writes its
+// own entries before they are read, so nothing needs clearing between calls;
+// calls that overlap on one GPU share the array and race.
+constexpr size_t kScratchBytes = (size_t)1 << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+std::unordered_map<int, void*> g_scratch_ptr;   // device -> address of its copy of `scratch`
+}  // namespace
+
+size_t scratch_max_bytes() { return kScratchBytes; }
+
+// Device address of the current device's `scratch` (looked up once per
+// device; in host code the array's name is only a host-side stand-in).
+hipError_t scratch_device_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    it = g_scratch_ptr.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return hipSuccess;
+}
 
 size_t prepare_nv_workspace(int T, int K) {
   const PrepGeom g = prep_geometry(T, K);

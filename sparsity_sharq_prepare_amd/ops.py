@@ -140,6 +140,20 @@ def prepare(X: torch.Tensor, gamma: Optional[torch.Tensor], eps: float = 1e-6, f
     return out
 
 
+def prepare_no_alloc(X: torch.Tensor, gamma: Optional[torch.Tensor], eps: float, out: PreparedAct,
+                     stream=None) -> PreparedAct:
+    """sharq_prepare_no_alloc: the preparation into caller-provided outputs,
+    with the NVFP4 scratch in the library's static device array (no
+    workspace; calls that overlap on one GPU race)."""
+    _dev_check(X, gamma)
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be a 2-D tensor contiguous along K")
+    T, K = X.shape
+    L.check(L.lib().sharq_prepare_no_alloc(X.data_ptr(), _dtype_code(X), T, K, X.stride(0), _ptr(gamma), eps,
+                                           out.struct(), _stream_ptr(stream)))
+    return out
+
+
 def linear(act: PreparedAct, w: PackedWeight, group_offsets: Optional[torch.Tensor] = None,
            row_index: Optional[torch.Tensor] = None, total_rows: Optional[int] = None,
            out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:

@@ -176,6 +176,19 @@ def test_prepare_linear_validation_errors():
     assert f(X, 1, 8, 256, 256, None, 1e-6, a, w, Y, 32, ws, 16, None) == L.SHARQ_ERR_INVALID_ARGUMENT
 
 
+def test_prepare_no_alloc_validation_errors():
+    # the allocation-free prepare: the usual prepare checks, and NVFP4 shapes
+    # whose scratch exceeds the static 1 MiB rejected before any device work
+    lib = L.lib()
+    f = lib.sharq_prepare_no_alloc
+    X = 0x50000
+    assert f(X, 1, 8, 256, 256, None, ctypes.c_float(1e-6), None, None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert f(X, 7, 8, 256, 256, None, ctypes.c_float(1e-6), _fake_act(), None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert f(X, 1, 100000, 2048, 2048, None, ctypes.c_float(1e-6), _fake_act(fmt=1, T=100000, K=2048), None) == \
+        L.SHARQ_ERR_UNSUPPORTED_SHAPE
+    assert "scratch" in lib.sharq_last_error().decode()
+
+
 def test_plain_baseline_validation_errors():
     lib = L.lib()
     X, Y, c, s = 0x50000, 0x30000, 0x60000, 0x70000
