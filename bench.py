@@ -11,6 +11,11 @@ Inputs are resident in HBM before timing starts; the packed weights rotate
 through ``--copies`` distinct buffers (default 8, about 570 MB) so the 256 MB
 Infinity Cache cannot serve them between steps.
 
+The default line also carries a ``prefill`` sub-record: the 4096 x 4096 x
+14336 prefill linear's prepare and dual GEMM launch durations, their HBM and
+MFMA roofline fractions and the plain unfused breakdown (``--no-prefill``
+skips it).
+
 ``--workload prefill|nvfp4|moe`` measures the other shapes (4096 x 4096 x
 14336 prefill; emulated NVFP4 at T = 2048; grouped MoE up+down) for the
 profiles; they are not the headline line.
@@ -45,6 +50,8 @@ def parse():
                    help="backbone mask of the MXFP4 workloads: 4:8 in pairs, or 2:4 element-wise")
     p.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = enough for > 512 MB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="decode workload: skip the prefill (4096 x 4096 x 14336) sub-record")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="first run one plain device-to-device copy of MIB MiB (a reference dispatch of known "
@@ -335,11 +342,17 @@ def cpu_baseline(cases, workload, target_s):
     import numpy as np
     from oracle import sharq as O
     from sparsity_sharq_prepare_amd import synth
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
+    def blas_threads():
+        # threads of the BLAS the oracle's GEMMs run on (the prepare itself is
+        # single-threaded numpy); queried after a matmul has loaded the BLAS
+        try:
+            from threadpoolctl import threadpool_info
+            np.ones((2, 2)) @ np.ones((2, 2))
+            return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        except Exception:
+            return 1
+    cores = blas_threads()
+    host_cpus = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     if workload in ("decode", "prefill", "nvfp4"):
         items = []
         for c in cases:
@@ -357,8 +370,18 @@ def cpu_baseline(cases, workload, target_s):
             n += 1
         rows_desc = "all 8 rows" if workload == "decode" else "the first 64 rows"
         sample = f"{n} pass(es) of the workload's {len(items)} linear(s) on {rows_desc} (prepare + dual GEMM, weights pre-packed)"
+        # the prepare alone on one thread (it is elementwise numpy: no BLAS)
+        tp, n_el = 0.0, 0
+        while tp < min(3.0, target_s / 4):
+            for x, g, _, fmt, _ in items:
+                t0 = time.perf_counter()
+                O.prepare(x, g, 1e-6, fmt)
+                tp += time.perf_counter() - t0
+                n_el += x.size
         return {"value": flops / t / 1e12, "unit": "TFLOPS-eff", "cores": cores, "kind": "oracle", "sample": sample,
-                "seconds": round(t, 2)}
+                "seconds": round(t, 2), "host_cpus": host_cpus,
+                "prepare_single_thread": {"elements_per_s": round(n_el / tp, 1), "seconds": round(tp, 2),
+                                          "threads": 1}}
     # moe: a few experts of each projection
     flops, t = 0.0, 0.0
     n_exp = 0
@@ -377,7 +400,8 @@ def cpu_baseline(cases, workload, target_s):
             if t > target_s / 2 * (1 + (mc is cases[-1])):
                 break
     return {"value": flops / t / 1e12, "unit": "TFLOPS-eff", "cores": cores, "kind": "oracle",
-            "sample": f"{n_exp} experts' rows (prepare + dual GEMM, weights pre-packed)", "seconds": round(t, 2)}
+            "sample": f"{n_exp} experts' rows (prepare + dual GEMM, weights pre-packed)", "seconds": round(t, 2),
+            "host_cpus": host_cpus}
 
 
 # ----------------------------------------------------------------------------
@@ -455,6 +479,41 @@ def oracle_errors(cases, y_gpu, extra_gpu, workload):
 
 
 # ----------------------------------------------------------------------------
+def prefill_subrecord(mask: str = "4:8"):
+    """The 4096 x 4096 x 14336 prefill linear (MXFP4), measured beside the
+    decode headline: each kernel's average launch duration (as kernel_times),
+    its roofline fraction (prepare: HBM; dual GEMM: MXFP4 MFMA on the
+    algorithmic 3 T K D and on the issued 4 T K D) and the plain unfused
+    breakdown (review §5 kernel latency breakdown)."""
+    import torch
+    from sparsity_sharq_prepare_amd.profiling import SOURCES
+    jobs, _, _ = build_jobs("prefill", 0, mask)
+    R = len(jobs[0].weights)
+    prep_ms, gemm_ms, _ = kernel_times(jobs, R)
+    j, pm, gm = jobs[0], prep_ms[0], gemm_ms[0]
+    prep_gbs = j.prep_bytes() / (pm * 1e-3) / 1e9
+    alg = j.gemm_flops_alg() / (gm * 1e-3) / 1e12
+    issued = j.gemm_flops_issued() / (gm * 1e-3) / 1e12
+    out = {
+        "workload": "llama3.1-8b prefill linear 4096x4096x14336, MXFP4",
+        "prepare_us": round(pm * 1e3, 2), "prepare_GBs": round(prep_gbs, 1),
+        "prepare_frac_hbm": round(prep_gbs / HBM_PEAK_GBS, 4),
+        "dual_gemm_us": round(gm * 1e3, 2), "dual_gemm_TFLOPS_alg": round(alg, 1),
+        "dual_gemm_TFLOPS_issued": round(issued, 1),
+        "dual_gemm_frac_mfma_alg": round(alg / FP4_PEAK_TFLOPS, 4),
+        "dual_gemm_frac_mfma_issued": round(issued / FP4_PEAK_TFLOPS, 4),
+        "dual_gemm_traffic": read_traffic("linear_mx_tile_prefill", SOURCES["linear_mx_tile"]),
+        "step_us": round((pm + gm) * 1e3, 2),
+        "TFLOPS_eff": round(j.gemm_flops_nominal() / ((pm + gm) * 1e-3) / 1e12, 1),
+        "tokens_per_s": round(j.T / ((pm + gm) * 1e-3), 1),
+        "breakdown": plain_breakdown(jobs, prep_ms, gemm_ms, R)[j.name],
+    }
+    del jobs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -546,12 +605,23 @@ def main():
     }
     if args.workload == "prefill":
         out["breakdown"] = plain_breakdown(jobs, prep_ms, gemm_ms, len(jobs[0].weights))
+    if args.workload == "moe":
+        # the grouped GEMMs sit near the ridge: both fractions, per launch
+        for j, g in zip(jobs, gemm_ms):
+            k = kernels[j.name]
+            k["gemm_frac_hbm"] = round(k["gemm_GBs"] / HBM_PEAK_GBS, 4)
+            k["gemm_frac_mfma_alg"] = round(k["gemm_TFLOPS_alg"] / FP4_PEAK_TFLOPS, 4)
+            k["gemm_frac_mfma_issued"] = round(k["gemm_TFLOPS_issued"] / FP4_PEAK_TFLOPS, 4)
+        roofline["frac_hbm"] = round(sum(j.gemm_bytes() for j in jobs) / n / (gemm_total_ms / n * 1e-3) / 1e9
+                                     / HBM_PEAK_GBS, 4)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cases, args.workload, args.cpu_seconds)
         if args.workload != "moe":
             rows = [j.rows if args.workload == "decode" else 64 for j in jobs]
             y_gpu = [j.Y[:r].float().cpu().numpy() for j, r in zip(jobs, rows)]
             out["errors"] = oracle_errors(cases, y_gpu, gpu_error_outputs(jobs, rows), args.workload)
+    if args.workload == "decode" and not args.no_prefill:
+        out["prefill"] = prefill_subrecord(args.mask)
     print(json.dumps(out))
 
 

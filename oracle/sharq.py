@@ -568,6 +568,37 @@ def _dense_quantized(v: np.ndarray, fmt: str, f64: bool = False) -> np.ndarray:
     return nv_dequant_f64(c, sc, NV_RES_BLOCK, s) if f64 else nv_dequant_f32(c, sc, NV_RES_BLOCK, s)
 
 
+def decomposition_pieces(x: np.ndarray, gamma, fmt: str = "mxfp4", eps: float = 1e-6) -> dict:
+    """The quantized pieces of the review's Table 5 path combinations
+    (review §5.3) for the activation rows x: y = RMSNorm(x) and, each as
+    the exact fp64 values the GEMM multiplies,
+      sparse_first   X~_sp: the 4:8 in-pairs backbone of ``prepare``
+      sparse_second  Q_sp(M'(R) ⊙ R): the pair-top-2 rule applied again to
+                     R = y - X~_sp and quantized like a backbone
+      dense_residual Q_dn(R): SharQ's dense residual path
+      dense_first    Q(y): y quantized densely
+      dense_second   Q(y - Q(y)): the residual of the dense first path,
+                     quantized densely
+    plus the fp32 inputs of the second paths (R and y - Q(y), exact by
+    Sterbenz as for R) and, for MXFP4, the 2:4 element-wise backbone and its
+    dense residual.  Every residual is taken against the quantized first path
+    (review §3.3)."""
+    prep = prepare(x, gamma, eps, fmt)
+    y, R = prep["y"], prep["R"]
+    q1 = _dense_quantized(y, fmt)                       # fp32, the dense residual's reference
+    out = {"y": y, "prep": prep, "R": R, "y_minus_q": y - q1,
+           "sparse_first": _sparse_quantized(y, fmt, f64=True),
+           "sparse_second": _sparse_quantized(R, fmt, f64=True),
+           "dense_residual": _dense_quantized(R, fmt, f64=True),
+           "dense_first": _dense_quantized(y, fmt, f64=True),
+           "dense_second": _dense_quantized(y - q1, fmt, f64=True)}
+    if fmt == "mxfp4":                                  # the pages' MXFP4 pattern, 2:4 element-wise
+        sp24 = _sparse_quantized(y, fmt, mask="2:4")
+        out["sparse_first_24"] = _sparse_quantized(y, fmt, f64=True, mask="2:4")
+        out["dense_residual_24"] = _dense_quantized(y - sp24, fmt, f64=True)
+    return out
+
+
 def decomposition_study(x: np.ndarray, gamma, w: np.ndarray, fmt: str = "mxfp4", eps: float = 1e-6,
                         wp: dict = None) -> dict:
     """Operator-level analogue of the review's Table 5 (sparse / dense path
@@ -580,30 +611,23 @@ def decomposition_study(x: np.ndarray, gamma, w: np.ndarray, fmt: str = "mxfp4",
       sharq         X~_sp + Q_dn(R)          (sparse backbone, dense residual)
       plain         Q(y)                     (one dense FP4 path)
     and, for MXFP4, sparse_only_2:4 and sharq_2:4 with a 2:4 element-wise
-    backbone mask instead of 4:8 in pairs
-    where y = RMSNorm(x), X~_sp and R are those of ``prepare``, W~ is the
-    packed weight, M' is the pair-top-2 mask chosen on R, and each residual
-    is taken against the quantized first path (review §3.3).  Every
-    residual here is exact in fp32 (Sterbenz, as for R).  ``wp``: W already
+    backbone mask instead of 4:8 in pairs, built from the pieces of
+    ``decomposition_pieces``.  W~ is the packed weight.  ``wp``: W already
     packed (``pack_weight(w, fmt)``), to skip packing it again."""
-    prep = prepare(x, gamma, eps, fmt)
-    y = prep["y"]
+    pc = decomposition_pieces(x, gamma, fmt, eps)
+    y = pc["y"]
     W = weight_dequant(wp if wp is not None else pack_weight(w, fmt), "dn")
     ref = y.astype(np.float64) @ np.asarray(w, dtype=np.float64)
-    Xt_sp = _sparse_quantized(y, fmt, f64=True)        # exact values of the backbone
-    R = prep["R"]
-    q1 = _dense_quantized(y, fmt)                       # fp32, the residual's reference
     approx = {
-        "sparse_only": Xt_sp,
-        "sparse_sparse": Xt_sp + _sparse_quantized(R, fmt, f64=True),
-        "dense_dense": _dense_quantized(y, fmt, f64=True) + _dense_quantized(y - q1, fmt, f64=True),
-        "sharq": Xt_sp + _dense_quantized(R, fmt, f64=True),
+        "sparse_only": pc["sparse_first"],
+        "sparse_sparse": pc["sparse_first"] + pc["sparse_second"],
+        "dense_dense": pc["dense_first"] + pc["dense_second"],
+        "sharq": pc["sparse_first"] + pc["dense_residual"],
         "plain": plain_quantized(y, fmt),
     }
-    if fmt == "mxfp4":                                  # the pages' MXFP4 pattern, 2:4 element-wise
-        sp24 = _sparse_quantized(y, fmt, mask="2:4")
-        approx["sparse_only_2:4"] = _sparse_quantized(y, fmt, f64=True, mask="2:4")
-        approx["sharq_2:4"] = approx["sparse_only_2:4"] + _dense_quantized(y - sp24, fmt, f64=True)
+    if fmt == "mxfp4":
+        approx["sparse_only_2:4"] = pc["sparse_first_24"]
+        approx["sharq_2:4"] = pc["sparse_first_24"] + pc["dense_residual_24"]
     Wf = np.asarray(w, dtype=np.float64)
     return {"weights_fp4": {k: rel_frobenius(v @ W, ref) for k, v in approx.items()},
             "activation_only": {k: rel_frobenius(v @ Wf, ref) for k, v in approx.items()}}
