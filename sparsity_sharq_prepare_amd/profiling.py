@@ -24,6 +24,13 @@ ignores it once the kernel has changed.
         --title "..." --out profiles/<kernel>_<workload>_kernel_trace.txt --command "..."
 
 writes the per-kernel call count and average / min / max duration table.
+
+    python -m sparsity_sharq_prepare_amd.profiling counters \
+        --csv <rocprofv3 --pmc counter_collection.csv> --kernel linear_mx_tile \
+        --workload prefill --out profiles/linear_mx_tile_prefill_counters.txt --command "..."
+
+averages SQ / GRBM counters over the kernel's dispatches and derives the
+MFMA busy fraction and VALU instructions per unit of work.
 """
 from __future__ import annotations
 
@@ -120,9 +127,59 @@ def trace_main(argv):
     print(open(a.out).read())
 
 
+def counters_main(argv):
+    """Per-dispatch averages of SQ / GRBM counters for one kernel selection,
+    with the derived figures: MFMA busy cycles per MFMA instruction, the
+    MFMA busy fraction of the GPU-active cycles per SIMD (SQ_VALU_MFMA_BUSY_
+    CYCLES is summed over the SIMDs and GRBM_GUI_ACTIVE over the XCDs), and
+    VALU wave-instructions per unit of work (--units: e.g. groups of 8
+    K-values a dispatch prepares; a wave covers 64 of them per instruction)."""
+    ap = argparse.ArgumentParser(description="counter summary from a rocprofv3 --pmc run")
+    ap.add_argument("--csv", required=True, help="counter_collection.csv")
+    ap.add_argument("--kernel", required=True, choices=sorted(SOURCES))
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--command", default="")
+    ap.add_argument("--simds", type=int, default=1024)
+    ap.add_argument("--xcds", type=int, default=8)
+    ap.add_argument("--units", type=float, default=0.0, help="work units per dispatch (lane-level), for VALU per unit")
+    ap.add_argument("--unit-name", default="unit")
+    a = ap.parse_args(argv)
+    vals = defaultdict(lambda: defaultdict(float))
+    names = {}
+    with open(a.csv, newline="") as fh:
+        for r in csv.DictReader(fh):
+            vals[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+            names[r["Dispatch_Id"]] = r["Kernel_Name"]
+    sel = [d for d in vals if selects(a.kernel, names[d])]
+    if not sel:
+        raise SystemExit(f"{a.csv}: no dispatch of {a.kernel}")
+    counters = sorted({c for d in sel for c in vals[d]})
+    avg = {c: sum(vals[d][c] for d in sel) / len(sel) for c in counters}
+    with open(a.out, "w") as fh:
+        fh.write(f"# counters of {a.kernel} ({a.workload} workload), rocprofv3 --pmc, averaged over {len(sel)} dispatches\n")
+        if a.command:
+            fh.write(f"# command: {a.command}\n")
+        for c in counters:
+            fh.write(f"{c} = {avg[c]:.0f}\n")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "SQ_INSTS_MFMA" in avg and avg["SQ_INSTS_MFMA"] > 0:
+            fh.write(f"mfma_busy_cycles_per_instruction = {avg['SQ_VALU_MFMA_BUSY_CYCLES'] / avg['SQ_INSTS_MFMA']:.2f}\n")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and "GRBM_GUI_ACTIVE" in avg and avg["GRBM_GUI_ACTIVE"] > 0:
+            per_simd = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / a.simds
+            active = avg["GRBM_GUI_ACTIVE"] / a.xcds
+            fh.write(f"gpu_active_cycles = {active:.0f}\n")
+            fh.write(f"mfma_busy_fraction = {per_simd / active:.4f}\n")
+        if a.units > 0 and "SQ_INSTS_VALU" in avg:
+            fh.write(f"valu_wave_instructions_per_64_{a.unit_name}s = {avg['SQ_INSTS_VALU'] * 64.0 / a.units:.1f}\n")
+        fh.write(f"source_sha256 = {source_hash(SOURCES[a.kernel])}\n")
+    print(open(a.out).read())
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "trace":
         return trace_main(sys.argv[2:])
+    if len(sys.argv) > 1 and sys.argv[1] == "counters":
+        return counters_main(sys.argv[2:])
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--fetch", required=True)
     ap.add_argument("--write", required=True)
