@@ -50,6 +50,9 @@ def parse():
                    help="backbone mask of the MXFP4 workloads: 4:8 in pairs, or 2:4 element-wise")
     p.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0 = enough for > 512 MB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--tokens", type=int, default=8,
+                   help="decode workload: tokens per step (8: the headline; up to 16 runs the two-tile decode "
+                        "kernel and single-launch form)")
     p.add_argument("--no-prefill", action="store_true",
                    help="decode workload: skip the prefill (4096 x 4096 x 14336) sub-record")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -79,7 +82,7 @@ class Job:
         self.Y = torch.empty((self.rows, D), dtype=torch.float32, device=X.device)
         self.groups = weights[0].n_groups
         # decode linears: also timed as one launch (sharq_prepare_linear)
-        self.fused = fmt == "mxfp4" and self.groups == 1 and rows is None and T <= 8
+        self.fused = fmt == "mxfp4" and self.groups == 1 and rows is None and T <= 16
         self.step_fused = False          # the step uses it when it is the faster form
 
     # algorithmic work of one launch
@@ -117,7 +120,7 @@ def _dev(a, bf16=True):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def build_jobs(workload: str, copies: int, mask: str = "4:8"):
+def build_jobs(workload: str, copies: int, mask: str = "4:8", tokens: int = 8):
     import numpy as np
     import torch
     from sparsity_sharq_prepare_amd import ops, synth
@@ -143,7 +146,7 @@ def build_jobs(workload: str, copies: int, mask: str = "4:8"):
         trio_bytes = sum(K * D * 0.53125 for K, D in synth.DECODE_SHAPES)
         n = n_copies(trio_bytes)
         for i in range(3):
-            c = synth.decode_case(i)
+            c = synth.decode_case(i, T=tokens)
             W = _dev(c.w)
             jobs.append(Job(c.name, afmt, _dev(c.x), _dev(c.gamma, False), pack_copies(W, "mxfp4", n),
                             c.T, c.K, c.D))
@@ -368,7 +371,7 @@ def cpu_baseline(cases, workload, target_s):
                 t += time.perf_counter() - t0
                 flops += fl
             n += 1
-        rows_desc = "all 8 rows" if workload == "decode" else "the first 64 rows"
+        rows_desc = f"all {items[0][0].shape[0]} rows" if workload == "decode" else "the first 64 rows"
         sample = f"{n} pass(es) of the workload's {len(items)} linear(s) on {rows_desc} (prepare + dual GEMM, weights pre-packed)"
         # the prepare alone on one thread (it is elementwise numpy: no BLAS)
         tp, n_el = 0.0, 0
@@ -538,7 +541,10 @@ def main():
     if args.mask == "2:4" and args.workload == "nvfp4":
         print("the 2:4 backbone is an MXFP4 option", file=sys.stderr)
         sys.exit(2)
-    jobs, cases, pack_times = build_jobs(args.workload, args.copies, args.mask)
+    if args.tokens != 8 and args.workload != "decode":
+        print("--tokens applies to the decode workload", file=sys.stderr)
+        sys.exit(2)
+    jobs, cases, pack_times = build_jobs(args.workload, args.copies, args.mask, args.tokens)
     wall, n_steps, prep_ms, gemm_ms, fused_ms = timed(jobs, args.steps, args.warmup)
     ms_step = wall * 1e3 / n_steps
 
@@ -590,7 +596,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "mxfp4" if args.workload != "nvfp4" else "nvfp4-emu(fp16 mfma)",
         "data": "synthetic",
-        "config": {"workload": {"decode": "llama3.1-8b decode linears, T=8, (4096x4096, 4096x14336, 14336x4096), MXFP4",
+        "config": {"workload": {"decode": f"llama3.1-8b decode linears, T={args.tokens}, (4096x4096, 4096x14336, 14336x4096), MXFP4",
                                 "prefill": "llama3.1-8b prefill linear 4096x4096x14336, MXFP4",
                                 "nvfp4": "qwen2.5-7b linears T=2048 (3584x18944, 18944x3584), NVFP4 emulated",
                                 "moe": "qwen3-30b-a3b moe linears, 128 experts top-8, 4096 tokens, up 2048x768 + down 768x2048, MXFP4"}[args.workload],

@@ -198,8 +198,8 @@ sharq_status sharq_linear(const sharq_act *a, const sharq_weight *w, const int32
 /* Single-launch decode (review §3.5: preparation fused ahead of the dual-
  * path GEMM, here in the same kernel launch): sharq_prepare of the T rows
  * of X into act, then sharq_linear(act, w) into Y (plain linear: row t of Y
- * from activation row t, total_rows = T).  For T <= 8 and K <= 16384 one
- * kernel does both: its first T workgroups prepare one row each and signal
+ * from activation row t, total_rows = T).  For T <= 8 and K <= 16384, and
+ * for 9 <= T <= 16 and K <= 7168, one kernel does both: its first T workgroups prepare one row each and signal
  * through counters in `workspace`; the GEMM workgroups stream their weights
  * meanwhile and wait (bounded polling) before reading the activations.
  * Larger shapes run sharq_prepare's and sharq_linear's kernels one after the

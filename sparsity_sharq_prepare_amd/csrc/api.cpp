@@ -273,7 +273,7 @@ sharq_status sharq_prepare_linear(const void* X, int32_t dtype, int32_t T, int32
   if (!aligned16(workspace)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == SHARQ_BF16;
-  if (T <= 8 && K <= sharq::decode_max_k())
+  if (T <= 16 && K <= sharq::decode_max_k(T))
     return from_hip(sharq::launch_prepare_linear_mx(X, bf16, T, K, ldx, gamma, eps, act->bb_codes, act->bb_meta,
                                                     act->bb_scale, act->res_codes, act->res_scale, w->payload,
                                                     w->scale_sp, w->D, Y, ldy, static_cast<uint32_t*>(workspace), s),

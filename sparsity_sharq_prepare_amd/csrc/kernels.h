@@ -50,10 +50,10 @@ hipError_t launch_linear_mx(const uint8_t* bb_codes, const uint8_t* bb_meta, con
                             int act_rows, int K, const uint8_t* payload, const uint8_t* wscale, int D, int n_groups,
                             const int32_t* group_offsets, float* Y, int64_t ldy, hipStream_t s, bool m24 = false);
 
-// single-launch decode (T <= 8, K <= decode_max_k()): MXFP4 prepare of the T
-// rows and the plain dual-path linear on them in one kernel; sync: two
-// device counters, zero before the call and left zero
-int decode_max_k();
+// single-launch decode (T <= 16, K <= decode_max_k(T)): MXFP4 prepare of the
+// T rows and the plain dual-path linear on them in one kernel; sync: the
+// four workspace words of the counter protocol (zero before first use)
+int decode_max_k(int rows);
 hipError_t launch_prepare_linear_mx(const void* X, bool bf16, int T, int K, int64_t ldx, const float* gamma, float eps,
                                     uint8_t* bb_codes, uint8_t* bb_meta, uint8_t* bb_scale, uint8_t* res_codes,
                                     uint8_t* res_scale, const uint8_t* payload, const uint8_t* wscale, int D, float* Y,

@@ -165,6 +165,11 @@ LINEAR_SHAPES = [  # skinny (T <= 64) and tile paths, ragged rows and columns
     # decode path (<= 8 rows): uneven steps per wave, the largest staged K, and
     # a K beyond it (general skinny path)
     (5, 1152, 72), (7, 16384, 48), (2, 18944, 40),
+    # decode path with two MFMA tiles (9-16 rows): ragged rows, column
+    # groups, the largest staged K (7168); beyond it the one-tile kernel
+    # twice (rows 0-7 and the rest) up to K = 16384, then the skinny path
+    (16, 4096, 300), (9, 1152, 72), (12, 2048, 4100), (11, 7168, 64), (16, 7296, 40),
+    (9, 14336, 72), (10, 16512, 40),
     # degenerate widths: one output column, the smallest GEMM K
     (3, 256, 1), (70, 512, 1), (1, 128, 16),
 ]
@@ -180,12 +185,15 @@ def test_linear_shapes(T, K, D):
     assert_gemm_close(Y.cpu().numpy(), Yr, S)
 
 
-@pytest.mark.parametrize("T", [8, 200])
-def test_linear_row_gather(T):
-    case = synth.random_case(99 + T, T, 256, 96)
+@pytest.mark.parametrize("T,K,n", [(8, 256, 13), (200, 256, 205), (6, 256, 5), (12, 8192, 14)])
+def test_linear_row_gather(T, K, n):
+    # n gathered output rows: the two-tile decode kernel (13), the tile path
+    # (205), the one-tile decode kernel (5) and two one-tile launches (14
+    # rows at K = 8192, the second reading row_index from entry 8)
+    case = synth.random_case(99 + T, T, K, 96)
     act = ops.prepare(dev_x(case), dev_gamma(case.gamma), 1e-6)
     w = ops.pack_weight(dev_w(case.w, "bf16"))
-    rows = np.random.default_rng(T).integers(0, T, T + 5).astype(np.int32)
+    rows = np.random.default_rng(T).integers(0, T, n).astype(np.int32)
     Y = ops.linear(act, w, row_index=torch.from_numpy(rows).cuda())
     Yr, S = O.sharq_linear(oracle_prepare(case), O.pack_weight(case.w_f32()), rows=rows)
     assert_gemm_close(Y.cpu().numpy(), Yr, S)
@@ -370,13 +378,19 @@ def test_graph_replay_matches_eager():
 
 
 # ------------------------------------------------------------------ single-launch decode
-FUSED_SHAPES = [  # (T, K, D, dtype, gamma): one launch for T <= 8, K <= 16384 (every decode
-    # kernel geometry: 1..16 K-splits, 1..8 column groups, J = 4 and 8), else the two launches
+FUSED_SHAPES = [  # (T, K, D, dtype, gamma): one launch for T <= 8, K <= 16384 and for
+    # T <= 16, K <= 7168 (every decode kernel geometry: 1..16 K-splits, 1..8
+    # column groups, J = 4 and 8), else the two launches
     (1, 256, 64, "bf16", True), (8, 512, 200, "bf16", True), (5, 1152, 72, "bf16", True),
     (3, 384, 40, "f32", True), (8, 2048, 96, "bf16", False), (7, 16384, 48, "bf16", True),
     (2, 14336, 130, "f32", True), (6, 768, 8200, "bf16", True), (8, 4096, 4100, "bf16", True),
     (2, 256, 40000, "bf16", True),
-    (9, 512, 96, "bf16", True), (4, 16512, 64, "bf16", True),
+    (4, 16512, 64, "bf16", True),
+    # 9-16 rows: two MFMA tiles per step in one launch up to K = 7168
+    (9, 512, 96, "bf16", True), (16, 4096, 4100, "bf16", True), (12, 1152, 200, "f32", True),
+    (16, 7168, 130, "bf16", False), (13, 256, 40000, "bf16", True),
+    # 9-16 rows beyond K = 7168: the two launches
+    (16, 7296, 64, "bf16", True),
 ]
 
 
@@ -439,6 +453,16 @@ def test_prepare_linear_sequence_and_own_workspace():
         assert torch.equal(Y, Y2)
     words = ws.view(torch.int32).cpu().tolist()
     assert words[1] == 0 and words[3] == 0 and words[0] == words[2] == 8 + 1 + 4 + 8
+    # 16 rows (two MFMA tiles) on the same workspace: the base advances by 16
+    case = synth.random_case(599, 16, 1024, 320)
+    X, g = dev_x(case), dev_gamma(case.gamma)
+    w = ops.pack_weight(dev_w(case.w, case.dtype))
+    _, Y = ops.prepare_linear(X, g, w, workspace=ws)
+    Y2 = ops.linear(ops.prepare(X, g, 1e-6), w)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2)
+    words = ws.view(torch.int32).cpu().tolist()
+    assert words[1] == 0 and words[3] == 0 and words[0] == words[2] == 21 + 16
     ops.prepare_linear_status(ws)
 
 
