@@ -769,9 +769,9 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 1 : 2) void linear_mx_tile8(
     m0 = (band * kBand + in_band % band_m) * BM;
     n0 = (in_band / band_m) * BNE;
   } else {
-    // the lookup's LDS lives in the third ring stage, which the first DMA
-    // reaches only after the main loop's first barrier, when every thread has
-    // read the result
+    // the lookup's LDS lives in the last ring stage (the third of three, the
+    // second of two), which the first DMA reaches only after the main loop's
+    // first barrier, when every thread has read the result
     int* scan = reinterpret_cast<int*>(&lds[NS - 1].a_dn[0]);
     int e, start, cnt, b;
     if (!find_group_tile(blockIdx.x, n_groups, group_offsets, rows, BM, tiles_n, scan, scan + 256, e, start, cnt, b))

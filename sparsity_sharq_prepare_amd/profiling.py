@@ -38,6 +38,7 @@ import argparse
 import csv
 import hashlib
 import os
+import re
 import sys
 from collections import defaultdict
 
@@ -48,19 +49,17 @@ SOURCES = {
     "linear_nv_tile": ["gemm_nv.hip", "common.h"],
     "prepare_mx_kernel": ["prepare.hip", "common.h", "prep_device.h"],
 }
-# dispatch names a kernel's counters are averaged over (all substrings must
-# match): the decode step's GEMM is the two-launch form on the 4:8 backbone
-# (linear_mx_decode<NK, CG, J, FUSED = false, M24 = false>)
+# dispatch names a kernel's counters are averaged over (the pattern must
+# match the name as the profiler prints it): the decode step's GEMM is the
+# two-launch form on the 4:8 backbone with one MFMA tile (up to 8 rows:
+# linear_mx_decode<NK, CG, J, FUSED = false, M24 = false, MT = 1>); the tile
+# GEMM counts its dual-GEMM instances, not the plain baseline's dense tile
+# (linear_mx_tile8<BM, BNE, DENSE = true, ...>)
 MATCH = {
-    "linear_mx_decode": ("linear_mx_decode<", ", false, false>"),
-    "linear_mx_tile": ("linear_mx_tile",),
-    "linear_nv_tile": ("linear_nv_tile",),
-    "prepare_mx_kernel": ("prepare_mx_kernel",),
-}
-# ... and none of these: the plain baseline's dense tile
-# (linear_mx_tile8<8, BNE, DENSE = true, ...>)
-EXCLUDE = {
-    "linear_mx_tile": ("linear_mx_tile8<8, 224, true,", "linear_mx_tile8<8, 256, true,"),
+    "linear_mx_decode": r"linear_mx_decode<\d+, \d+, \d+, false, false, 1>",
+    "linear_mx_tile": r"linear_mx_tile8<\d+, \d+, false,",
+    "linear_nv_tile": r"linear_nv_tile",
+    "prepare_mx_kernel": r"prepare_mx_kernel<",
 }
 
 
@@ -88,7 +87,7 @@ def per_dispatch(path: str, counter: str) -> dict:
 
 def selects(kernel: str, name: str) -> bool:
     """Whether dispatch `name` (as the profiler prints it) counts for `kernel`."""
-    return all(m in name for m in MATCH[kernel]) and not any(x in name for x in EXCLUDE.get(kernel, ()))
+    return re.search(MATCH[kernel], name) is not None
 
 
 def kernel_bytes(path: str, counter: str, kernel: str, copy_bytes: int):
