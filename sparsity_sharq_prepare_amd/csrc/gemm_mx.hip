@@ -751,36 +751,23 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 1 : 2) void linear_mx_tile8(
   // 64 wb .. (waves w and w + 4 load the same bytes when NW = 8)
   const int wq = w % (NW / 2), wb = w & 3;
 
-  // ---- tile -> (first row, first column). Tiles are ordered in bands of
-  // kBand row tiles that sweep all column tiles (row fastest inside a band),
-  // and each XCD takes one contiguous stretch of that order: the workgroups
-  // that run together on one XCD then share a few activation and weight
-  // tiles through its L2 instead of all 16 row tiles of the activations
-  // (measured at 4096 x 4096 x 14336: 269 -> 243 us)
+  // ---- tile order. Tiles are ordered in bands of kBand row tiles that
+  // sweep all column tiles (row fastest inside a band), and each XCD takes
+  // one contiguous stretch of that order: the workgroups that run together on
+  // one XCD then share a few activation and weight tiles through its L2
+  // instead of all 16 row tiles of the activations (measured at 4096 x 4096
+  // x 14336: 269 -> 243 us).  Grouped tiles are numbered expert by expert
+  // (each expert's ceil(rows_e / BM) x tiles_n tiles, row tiles outer), so an
+  // XCD's stretch covers a few experts.
   const int tiles_n = (D + BNE - 1) / BNE;
-  int grp = 0, m0, n0, row_end = rows;
-  if constexpr (!GROUPED) {
+  constexpr int kBand = 4;
+  auto band_tile = [&](int t, int& m0, int& n0) {
     const int tiles_m = (rows + BM - 1) / BM;
-    const int nt = tiles_m * tiles_n;
-    const int bi = xcd_tile(blockIdx.x, nt);
-    constexpr int kBand = 4;
-    const int band = bi / (kBand * tiles_n), band_m = min(kBand, tiles_m - band * kBand);
-    const int in_band = bi - band * kBand * tiles_n;
+    const int band = t / (kBand * tiles_n), band_m = min(kBand, tiles_m - band * kBand);
+    const int in_band = t - band * kBand * tiles_n;
     m0 = (band * kBand + in_band % band_m) * BM;
     n0 = (in_band / band_m) * BNE;
-  } else {
-    // the lookup's LDS lives in the last ring stage (the third of three, the
-    // second of two), which the first DMA reaches only after the main loop's
-    // first barrier, when every thread has read the result
-    int* scan = reinterpret_cast<int*>(&lds[NS - 1].a_dn[0]);
-    int e, start, cnt, b;
-    if (!find_group_tile(blockIdx.x, n_groups, group_offsets, rows, BM, tiles_n, scan, scan + 256, e, start, cnt, b))
-      return;                                           // surplus workgroup (uniform)
-    grp = e;
-    m0 = start + (b / tiles_n) * BM;
-    n0 = (b % tiles_n) * BNE;
-    row_end = start + cnt;
-  }
+  };
 
   // K % 128 == 0: KS steps of 128, side groups of 4 steps (the last one may
   // be partial; its rows' side bytes past the step count are loaded but not
@@ -792,77 +779,93 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 1 : 2) void linear_mx_tile8(
   const int4v r_mt = make_rsrc(bb_meta, (uint32_t)act_rows * kM);
   const int4v r_ssp = make_rsrc(bb_scale, (uint32_t)act_rows * kS);
   const int4v r_sdn = make_rsrc(res_scale, (uint32_t)act_rows * kS);
-  const int4v r_b = make_rsrc(payload + (int64_t)grp * D * kR, (uint32_t)D * kR);
-  const int4v r_sb = make_rsrc(wscale + (int64_t)grp * D * kS, (uint32_t)D * kS);
-
-  // byte offset of tile row r's activation row at `bytes` per row; rows past
-  // the tile's end (the last row tile of the matrix or of an expert) get an
-  // offset past every buffer, so their DMAs load zeros without a memory
-  // request (their products reach only outputs that are never stored)
-  constexpr uint32_t kAbsent = 0x80000000u;
-  auto act_off = [&](int r, uint32_t bytes) -> uint32_t {
-    const int gr = m0 + r;
-    return gr < row_end ? (uint32_t)gather_row(row_index, gr, act_rows) * bytes : kAbsent;
-  };
-  auto w_row = [&](int c) -> uint32_t { return n0 + c < D ? (uint32_t)(n0 + c) : 0u; };
-
-  // ---- per-lane DMA byte offsets at step / group 0
-  uint32_t o_dn[2], o_b[WB];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int sl = 64 * (w + NW * j) + l, row = sl >> 2, q = (sl & 3) ^ swz(row);
-    o_dn[j] = act_off(row, kR) + 16 * q;
-  }
-#pragma unroll
-  for (int j = 0; j < WB; ++j) {
-    const int sl = 64 * (w + NW * j) + l, col = sl >> 2, q = (sl & 3) ^ swz(col);
-    // staged columns past the tile's BNE are never read: an offset past the
-    // buffer loads zeros without a memory request
-    o_b[j] = col < BNE ? w_row(col) * kR + 16 * q : 0x80000000u;
-  }
-  uint32_t o_sp;
-  {
-    const int sl = 64 * w + l, row = sl >> 1, h = (sl & 1) ^ ((row >> 3) & 1);
-    o_sp = act_off(row, kA) + 16 * h;
-  }
-  // 4:8: 2 lanes x 16 B per row and side group; 2:4: 16 B per row and step,
-  // waves w and w + NW / 2 loading the same rows (same bytes to the same place)
-  const uint32_t o_mt = M24 ? act_off(64 * wq + l, kM) : act_off((64 * w + l) >> 1, kM) + 16 * (l & 1);
-  // the first half of the waves: backbone scale rows 64 wq + l; the second
-  // half: residual scale rows (the plain baseline: its scales, twice)
-  const uint32_t o_sa = act_off(64 * wq + l, kS);
-  const uint32_t o_sw = 64 * wb + l < BNE ? w_row(64 * wb + l) * kS : 0x80000000u;
   const bool first_half = w < NW / 2;                  // uniform
   const int4v r_sa = first_half ? r_ssp : r_sdn;
 
-  auto issue_main = [&](int s, MainT& st) {
+  // ---- one tile: rows m0 .. row_end - 1 (at most BM of them), columns
+  // n0 .., the weight descriptors of its expert, and every lane's DMA byte
+  // offsets at step / group 0.  Rows past the tile's end (the last row tile
+  // of the matrix or of an expert) get an offset past every buffer, so their
+  // DMAs load zeros without a memory request (their products reach only
+  // outputs that are never stored).
+  constexpr uint32_t kAbsent = 0x80000000u;
+  struct TileRows {            // activation rows the lane's DMAs read (or kAbsent)
+    uint32_t dn[2], sp, sa;    // residual rows; backbone (and 4:8 metadata) row; scale (and 2:4 metadata) row
+  };
+  struct TileOff {
+    int m0, n0, row_end;
+    int4v r_b, r_sb;
+    uint32_t dn[2], b[WB], sp, mt, sa, sw;
+  };
+  // gathered rows: row_index loads when rows are gathered
+  auto tile_rows = [&](int m0, int row_end, TileRows& tr) {
+    auto g = [&](int r) -> uint32_t {
+      const int gr = m0 + r;
+      return gr < row_end ? (uint32_t)gather_row(row_index, gr, act_rows) : kAbsent;
+    };
+#pragma unroll
+    for (int j = 0; j < 2; ++j) tr.dn[j] = g((64 * (w + NW * j) + l) >> 2);
+    tr.sp = g((64 * w + l) >> 1);
+    tr.sa = g(64 * wq + l);
+  };
+  auto tile_off = [&](int grp, int m0, int n0, int row_end, const TileRows& tr, TileOff& o) {
+    auto off = [&](uint32_t row, uint32_t bytes) -> uint32_t { return row == kAbsent ? kAbsent : row * bytes; };
+    auto w_row = [&](int c) -> uint32_t { return n0 + c < D ? (uint32_t)(n0 + c) : 0u; };
+    o.m0 = m0;
+    o.n0 = n0;
+    o.row_end = row_end;
+    o.r_b = make_rsrc(payload + (int64_t)grp * D * kR, (uint32_t)D * kR);
+    o.r_sb = make_rsrc(wscale + (int64_t)grp * D * kS, (uint32_t)D * kS);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int sl = 64 * (w + NW * j) + l, row = sl >> 2, q = (sl & 3) ^ swz(row);
+      o.dn[j] = off(tr.dn[j], kR) + 16 * q;
+    }
+#pragma unroll
+    for (int j = 0; j < WB; ++j) {
+      const int sl = 64 * (w + NW * j) + l, col = sl >> 2, q = (sl & 3) ^ swz(col);
+      // staged columns past the tile's BNE are never read: an offset past
+      // the buffer loads zeros without a memory request
+      o.b[j] = col < BNE ? w_row(col) * kR + 16 * q : kAbsent;
+    }
+    {
+      const int sl = 64 * w + l, row = sl >> 1, h = (sl & 1) ^ ((row >> 3) & 1);
+      o.sp = off(tr.sp, kA) + 16 * h;
+    }
+    // 4:8: 2 lanes x 16 B per row and side group; 2:4: 16 B per row and
+    // step, waves w and w + NW / 2 loading the same rows (same bytes to the
+    // same place)
+    o.mt = M24 ? off(tr.sa, kM) : off(tr.sp, kM) + 16 * (l & 1);
+    // the first half of the waves: backbone scale rows 64 wq + l; the
+    // second half: residual scale rows (the plain baseline: its scales,
+    // twice)
+    o.sa = off(tr.sa, kS);
+    o.sw = 64 * wb + l < BNE ? w_row(64 * wb + l) * kS : kAbsent;
+  };
+
+  auto issue_main = [&](int s, MainT& st, const TileOff& o) {
     const uint32_t s64 = 64u * s, s32 = 32u * s;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) dma16(r_dn, o_dn[j], s64, lds_addr(&st.a_dn[64 * (w + NW * j)]));
+    for (int j = 0; j < 2; ++j) dma16(r_dn, o.dn[j], s64, lds_addr(&st.a_dn[64 * (w + NW * j)]));
 #pragma unroll
-    for (int j = 0; j < WB; ++j) dma16(r_b, o_b[j], s64, lds_addr(&st.b[64 * (w + NW * j)]));
-    if constexpr (!DENSE) dma16(r_sp, o_sp, s32, lds_addr(&st.a_sp[64 * w]));
-    if constexpr (M24) dma16(r_mt, o_mt, 16u * s, lds_addr(&st.meta[64 * wq]));
+    for (int j = 0; j < WB; ++j) dma16(o.r_b, o.b[j], s64, lds_addr(&st.b[64 * (w + NW * j)]));
+    if constexpr (!DENSE) dma16(r_sp, o.sp, s32, lds_addr(&st.a_sp[64 * w]));
+    if constexpr (M24) dma16(r_mt, o.mt, 16u * s, lds_addr(&st.meta[64 * wq]));
   };
-  auto issue_side = [&](int g, SideT& sd) {
+  auto issue_side = [&](int g, SideT& sd, const TileOff& o) {
     if constexpr (DENSE) {
-      dma16(r_sdn, o_sa, 16u * g, lds_addr(&sd.s_dn[64 * wq]));   // waves w and w + NW / 2: same bytes
+      dma16(r_sdn, o.sa, 16u * g, lds_addr(&sd.s_dn[64 * wq]));   // waves w and w + NW / 2: same bytes
     } else if constexpr (M24) {
-      dma16(r_sa, o_sa, 16u * g, lds_addr(first_half ? &sd.s_sp[64 * wq] : &sd.s_dn[64 * wq]));
+      dma16(r_sa, o.sa, 16u * g, lds_addr(first_half ? &sd.s_sp[64 * wq] : &sd.s_dn[64 * wq]));
     } else {
-      dma16(r_mt, o_mt, 32u * g, lds_addr(&sd.meta[64 * w]));
-      dma16(r_sa, o_sa, 16u * g, lds_addr(first_half ? &sd.s_sp[64 * wq] : &sd.s_dn[64 * wq]));
+      dma16(r_mt, o.mt, 32u * g, lds_addr(&sd.meta[64 * w]));
+      dma16(r_sa, o.sa, 16u * g, lds_addr(first_half ? &sd.s_sp[64 * wq] : &sd.s_dn[64 * wq]));
     }
-    dma16(r_sb, o_sw, 16u * g, lds_addr(&sd.s_b[64 * wb]));   // NW = 8: waves w and w + 4 load the same bytes
+    dma16(o.r_sb, o.sw, 16u * g, lds_addr(&sd.s_b[64 * wb]));   // NW = 8: waves w and w + 4 load the same bytes
   };
 
   const int wm0 = 32 * w, wn0 = 0;
   const int kh = l >> 5, lr = l & 31;
-  // a wave whose rows all lie past the tile's end (an expert's or the
-  // matrix's last row tile) issues its share of the DMAs and takes every
-  // barrier, but reads no fragments and issues no MFMAs, leaving its SIMD's
-  // matrix core to the other wave there (uniform per wave)
-  const bool live = m0 + wm0 < row_end;
   // per step: scales (both halves: op_sel picks the byte), metadata (low /
   // high 16 bits) and the compacted backbone (low / high 8 bytes) are read
   // once; per half-step only the weight and residual code fragments
@@ -906,10 +909,12 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 1 : 2) void linear_mx_tile8(
   };
 
   v16f acc[FM][FN];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int f = 0; f < FM; ++f)
+    for (int f = 0; f < FM; ++f)
 #pragma unroll
-    for (int n = 0; n < FN; ++n) acc[f][n] = (v16f){};
+      for (int n = 0; n < FN; ++n) acc[f][n] = (v16f){};
+  };
 
   auto mfma_half = [&](const StepFrag& S, const HalfFrag& H, auto jc) {
     constexpr int J = decltype(jc)::value;
@@ -931,20 +936,74 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 1 : 2) void linear_mx_tile8(
   };
   const std::integral_constant<int, 0> j0{};
   const std::integral_constant<int, 1> j1{};
-
   StepFrag sf;
   HalfFrag hf;
-  issue_main(0, lds[0]);
-  issue_side(0, side[0]);
-  if constexpr (NS == 3) issue_main(min(1, KS - 1), lds[1]);
-  for (int g = 0; g < G; ++g) {
-    const SideT& sd = side[g & 1];
+  auto compute_step = [&](const MainT& cur, const SideT& sd, int p) {
+    read_step(cur, sd, p, sf);
+    read_half(cur, hf, j0);
+    mfma_half(sf, hf, j0);
+    read_half(cur, hf, j1);
+    mfma_half(sf, hf, j1);
+  };
+
+  // ---- epilogue: fp32 store of the accumulator tile
+  auto epilogue = [&](const TileOff& o) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int s = 4 * g + p;
-      if constexpr (PARTIAL)
-        if (s >= KS) break;                               // partial last side group (uniform)
-      if constexpr (NS == 3) {
+    for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+      for (int n = 0; n < FN; ++n) {
+        const int c = o.n0 + wn0 + 32 * n + lr;
+        if (c >= D) continue;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = o.m0 + wm0 + 32 * fm + 8 * (i >> 2) + 4 * kh + (i & 3);
+          if (r < o.row_end) Y[(int64_t)r * ldy + c] = acc[fm][n][i];
+        }
+      }
+    }
+  };
+
+  if constexpr (NS == 3) {
+    // ---- 256-row tiles: one tile per workgroup
+    int grp = 0, m0, n0, row_end = rows;
+    if constexpr (!GROUPED) {
+      band_tile(xcd_tile(blockIdx.x, ((rows + BM - 1) / BM) * tiles_n), m0, n0);
+    } else {
+      // the lookup's LDS lives in the last ring stage, which the first DMA
+      // reaches only after the main loop's first barrier, when every thread
+      // has read the result
+      int* scan = reinterpret_cast<int*>(&lds[NS - 1].a_dn[0]);
+      int e, start, cnt, b;
+      if (!find_group_tile(blockIdx.x, n_groups, group_offsets, rows, BM, tiles_n, scan, scan + 256, e, start, cnt, b))
+        return;                                         // surplus workgroup (uniform)
+      grp = __builtin_amdgcn_readfirstlane(e);
+      start = __builtin_amdgcn_readfirstlane(start);
+      cnt = __builtin_amdgcn_readfirstlane(cnt);
+      b = __builtin_amdgcn_readfirstlane(b);
+      m0 = start + (b / tiles_n) * BM;
+      n0 = (b % tiles_n) * BNE;
+      row_end = start + cnt;
+    }
+    TileRows tr;
+    tile_rows(m0, row_end, tr);
+    TileOff o;
+    tile_off(grp, m0, n0, row_end, tr, o);
+    // a wave whose rows all lie past the tile's end (an expert's or the
+    // matrix's last row tile) issues its share of the DMAs and takes every
+    // barrier, but reads no fragments and issues no MFMAs, leaving its
+    // SIMD's matrix core to the other wave there (uniform per wave)
+    const bool live = m0 + wm0 < row_end;
+    zero_acc();
+    issue_main(0, lds[0], o);
+    issue_side(0, side[0], o);
+    issue_main(min(1, KS - 1), lds[1], o);
+    for (int g = 0; g < G; ++g) {
+      const SideT& sd = side[g & 1];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int s = 4 * g + p;
+        if constexpr (PARTIAL)
+          if (s >= KS) break;                             // partial last side group (uniform)
         // stage s (and at p = 0 side group g) landed; stage s+1 (and after
         // p = 2 side group g+1) may still be in flight.  After the barrier
         // every wave is past its reads of step s-1, whose buffer stage s+2
@@ -952,46 +1011,168 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 1 : 2) void linear_mx_tile8(
         if (p == 3) wait_vm_lgkm0<NMAIN + NSIDE>();
         else wait_vm_lgkm0<NMAIN>();
         __builtin_amdgcn_s_barrier();
-        issue_main(min(s + 2, KS - 1), lds[(s + 2) % NS]);
+        issue_main(min(s + 2, KS - 1), lds[(s + 2) % NS], o);
         // side group g+1 replaces group g-1, last read at step 4 g - 1
-        if (p == 2) issue_side(min(g + 1, G - 1), side[(g + 1) & 1]);
-      } else {
-        // two stages: stage s (and at p = 0 side group g) landed; only side
-        // group g+1, issued at p = 0 after stage s, may still be in flight
-        // at p = 1.  After the barrier every wave is past step s-1, whose
-        // buffer stage s+1 reuses, and at p = 0 past step 4 g - 1, the last
-        // reader of side group g-1, which group g+1 replaces.
-        if (p == 1) wait_vm_lgkm0<NSIDE>();
-        else wait_vm_lgkm0<0>();
-        __builtin_amdgcn_s_barrier();
-        issue_main(min(s + 1, KS - 1), lds[(s + 1) % NS]);
-        if (p == 0) issue_side(min(g + 1, G - 1), side[(g + 1) & 1]);
-      }
-      if (live) {
-        const MainT& cur = lds[s % NS];
-        read_step(cur, sd, p, sf);
-        read_half(cur, hf, j0);
-        mfma_half(sf, hf, j0);
-        read_half(cur, hf, j1);
-        mfma_half(sf, hf, j1);
+        if (p == 2) issue_side(min(g + 1, G - 1), side[(g + 1) & 1], o);
+        if (live) compute_step(lds[s % NS], sd, p);
       }
     }
-  }
-  wait_vm_lgkm0<0>();                                  // no DMA may land after the tile ends
-  if (!live) return;
-
-  // ---- epilogue: fp32 store of the accumulator tile
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-#pragma unroll
-    for (int n = 0; n < FN; ++n) {
-      const int c = n0 + wn0 + 32 * n + lr;
-      if (c >= D) continue;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = m0 + wm0 + 32 * fm + 8 * (i >> 2) + 4 * kh + (i & 3);
-        if (r < row_end) Y[(int64_t)r * ldy + c] = acc[fm][n][i];
+    wait_vm_lgkm0<0>();                                // no DMA may land after the tile ends
+    if (live) epilogue(o);
+  } else {
+    // ---- 128-row tiles, persistent: two workgroups per CU, each taking
+    // every J-th tile of its XCD's stretch.  During a tile's last step the
+    // next tile's first stage and side group are already in flight (into the
+    // ring slots that step no longer reads), and its gathered rows were
+    // loaded at the first step, so the lookup, the ring fill and the fp32
+    // epilogue of consecutive tiles overlap instead of following one another
+    // (the grid's workgroups stay resident, no relaunch per tile).
+    int total;
+    // grouped: inclusive tile prefix sums of experts 64 c + l in lane l (c <
+    // 4, at most 256 experts), built once through the LDS of ring stage 1,
+    // which the first DMA reaches only after the loop's first barrier
+    int tb_incl[4];
+    auto expert_rows = [&](int e, int& st, int& cnt) {
+      st = min(max(group_offsets[e], 0), rows);
+      cnt = min(max(group_offsets[e + 1], st), rows) - st;
+    };
+    if constexpr (GROUPED) {
+      int* scan = reinterpret_cast<int*>(&lds[1].a_dn[0]);
+      int te = 0;                                       // 256 threads: expert tid
+      if (tid < n_groups) {
+        int st, cnt;
+        expert_rows(tid, st, cnt);
+        te = ((cnt + BM - 1) / BM) * tiles_n;
       }
+      scan[tid] = te;
+      __syncthreads();
+      for (int d = 1; d < 256; d <<= 1) {               // inclusive Hillis-Steele scan
+        const int v = tid >= d ? scan[tid - d] : 0;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
+      }
+      total = __builtin_amdgcn_readfirstlane(scan[255]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) tb_incl[c] = scan[64 * c + l];
+    } else {
+      total = ((rows + BM - 1) / BM) * tiles_n;
+    }
+    // tile t -> expert, rows and columns (uniform)
+    auto tile_of = [&](int t, int& grp, int& m0, int& n0, int& row_end) {
+      if constexpr (GROUPED) {
+        // the first expert whose inclusive tile prefix exceeds t (experts
+        // with no tiles share their predecessor's prefix and are skipped)
+        int cc = 3, lane = 0;
+#pragma unroll
+        for (int c = 3; c >= 0; --c) {
+          const uint64_t m = __builtin_amdgcn_ballot_w64(t < tb_incl[c]);
+          if (m) {
+            cc = c;
+            lane = __builtin_ctzll(m);
+          }
+        }
+        int prev = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (c == cc && lane > 0) prev = __builtin_amdgcn_readlane(tb_incl[c], lane - 1);
+          if (c + 1 == cc && lane == 0) prev = __builtin_amdgcn_readlane(tb_incl[c], 63);
+        }
+        grp = 64 * cc + lane;
+        int st, cnt;
+        expert_rows(grp, st, cnt);                      // uniform address: scalar loads
+        const int b = t - prev;
+        m0 = st + (b / tiles_n) * BM;
+        n0 = (b % tiles_n) * BNE;
+        row_end = st + cnt;
+      } else {
+        band_tile(t, m0, n0);
+        grp = 0;
+        row_end = rows;
+      }
+    };
+    // this workgroup's tiles: lo + k for k = j, j + J, .. below len, where
+    // the tile order is cut into NX stretches, one per XCD (workgroup b runs
+    // on XCD b mod 8), and the J workgroups of stretch x interleave in it,
+    // so together they sweep it front to back
+    const int P = gridDim.x, NX = P < 8 ? P : 8, x = blockIdx.x % NX;
+    const int J = (P - x + NX - 1) / NX;                // workgroups of stretch x
+    const int q = total / NX, rr = total % NX;
+    const int lo = x * q + min(x, rr), len = q + (x < rr ? 1 : 0);
+    int k = blockIdx.x / NX;
+    if (k >= len) return;                               // surplus workgroup (uniform)
+
+    // the current tile (uniform) and its gathered rows; the per-lane DMA
+    // offsets are recomputed where needed rather than kept for two tiles
+    int cg, cm0, cn0, cre;
+    tile_of(lo + k, cg, cm0, cn0, cre);
+    TileRows ctr;
+    tile_rows(cm0, cre, ctr);
+    {
+      TileOff o0;
+      tile_off(cg, cm0, cn0, cre, ctr, o0);
+      issue_main(0, lds[0], o0);
+      issue_side(0, side[0], o0);
+    }
+    int sbase = 0, gbase = 0;                           // ring positions of the tile's step 0 / group 0
+    while (true) {
+      TileOff oc;
+      tile_off(cg, cm0, cn0, cre, ctr, oc);
+      k += J;
+      const bool has_next = k < len;                    // uniform
+      int ng = 0, nm0 = 0, nn0 = 0, nre = 0;
+      if (has_next) tile_of(lo + k, ng, nm0, nn0, nre);
+      TileRows ntr;
+      // as in the 256-row tile: a wave past the tile's end issues its DMAs
+      // and takes the barriers, but no fragment reads or MFMAs
+      const bool live = cm0 + wm0 < cre;
+      zero_acc();
+      for (int g = 0; g < G; ++g) {
+        const SideT& sd = side[(gbase + g) & 1];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int s = 4 * g + p;
+          if constexpr (PARTIAL)
+            if (s >= KS) break;                           // partial last side group (uniform)
+          const bool last = s == KS - 1;
+          // two stages: stage s (and at p = 0 side group g) landed.  Only
+          // side group g+1, issued at p = 0 after stage s, may still be in
+          // flight at p = 1; the last group issues none (the next tile's
+          // group 0 goes out with its stage 0 at the tile's last step).
+          // After the barrier every wave is past step s-1, whose ring slot
+          // stage s+1 reuses, and at p = 0 past step 4 g - 1, the last
+          // reader of the side slot group g+1 reuses.
+          if (p == 1 && g + 1 < G) wait_vm_lgkm0<NSIDE>();
+          else wait_vm_lgkm0<0>();
+          __builtin_amdgcn_s_barrier();
+          // the next tile's gathered rows: loaded here, first read at this
+          // tile's last step, after its wait for every load
+          if (s == 0 && has_next) tile_rows(nm0, nre, ntr);
+          if (!last) {
+            issue_main(s + 1, lds[(sbase + s + 1) & 1], oc);
+          } else if (has_next) {
+            // the next tile's stage 0 into the slot step s-1 used, and its
+            // group 0 into the slot of this tile's group G-2 (or, with one
+            // group per tile, the previous tile's last group)
+            TileOff on;
+            tile_off(ng, nm0, nn0, nre, ntr, on);
+            issue_main(0, lds[(sbase + s + 1) & 1], on);
+            issue_side(0, side[(gbase + G) & 1], on);
+          }
+          if (p == 0 && g + 1 < G) issue_side(g + 1, side[(gbase + g + 1) & 1], oc);
+          if (live) compute_step(lds[(sbase + s) & 1], sd, p);
+        }
+      }
+      if (!has_next) wait_vm_lgkm0<0>();               // no DMA may land after the workgroup ends
+      if (live) epilogue(oc);
+      if (!has_next) break;
+      sbase += KS;
+      gbase += G;
+      cg = ng;
+      cm0 = nm0;
+      cn0 = nn0;
+      cre = nre;
+      ctr = ntr;
     }
   }
 }
@@ -1093,6 +1274,10 @@ hipError_t launch_prepare_linear_mx(const void* X, bool bf16, int T, int K, int6
 }
 
 namespace {
+// rows of the plain (single-expert) tile: 256 (one workgroup per tile) or
+// 128 (a persistent grid, two workgroups per CU)
+constexpr int kPlainTileRows = 256;
+
 template <bool M24>
 hipError_t launch_linear_mx_impl(const uint8_t* bb_codes, const uint8_t* bb_meta, const uint8_t* bb_scale,
                                  const uint8_t* res_codes, const uint8_t* res_scale, const int32_t* row_index, int rows,
@@ -1148,20 +1333,25 @@ hipError_t launch_linear_mx_impl(const uint8_t* bb_codes, const uint8_t* bb_meta
   // group of four steps is partial
   if (K % 128 != 0) return hipErrorInvalidValue;
   const bool partial = K % 512 != 0;
+  const int ncu = num_cus_gemm();
   if (n_groups == 1) {
     // tile width 256 or 224: the one with fewer rounds x width over the CUs
     // (256 rows: at 4096 x 4096 x 14336 the 128-row tile, two workgroups
     // per CU, measured the same, 278.9 against 277.5-280.2 us, and stages
     // each weight column twice as often)
-    constexpr int PBM = 256;
+    constexpr int PBM = kPlainTileRows;
+    constexpr int slots = PBM == 256 ? 1 : 2;          // workgroups per CU
     const int tiles_m = (rows + PBM - 1) / PBM;
-    const int ncu = num_cus_gemm();
     const int t256 = tiles_m * ((D + 255) / 256), t224 = tiles_m * ((D + 223) / 224);
-    const bool narrow = (int64_t)((t224 + ncu - 1) / ncu) * 224 < (int64_t)((t256 + ncu - 1) / ncu) * 256;
+    const int ns = slots * ncu;
+    const bool narrow = (int64_t)((t224 + ns - 1) / ns) * 224 < (int64_t)((t256 + ns - 1) / ns) * 256;
+    const int tiles = narrow ? t224 : t256;
+    // 256 rows: one workgroup per tile; 128 rows: a persistent grid
+    const int grid = PBM == 256 ? tiles : std::min(tiles, ns);
 #define T8(BNE_, PARTIAL_)                                                                                            \
-  hipLaunchKernelGGL((linear_mx_tile8<PBM, BNE_, false, false, M24, PARTIAL_>), dim3(narrow ? t224 : t256), dim3(2 * PBM), 0, \
-                     s, bb_codes, bb_meta, bb_scale, res_codes, res_scale, row_index, rows, act_rows, K, payload,       \
-                     wscale, D, 1, nullptr, Y, ldy)
+  hipLaunchKernelGGL((linear_mx_tile8<PBM, BNE_, false, false, M24, PARTIAL_>), dim3(grid), dim3(2 * PBM), 0, s,      \
+                     bb_codes, bb_meta, bb_scale, res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale,  \
+                     D, 1, nullptr, Y, ldy)
     if (narrow) {
       if (partial) T8(224, true);
       else T8(224, false);
@@ -1170,14 +1360,29 @@ hipError_t launch_linear_mx_impl(const uint8_t* bb_codes, const uint8_t* bb_meta
       else T8(256, false);
     }
 #undef T8
-  } else {
+  } else if (n_groups <= 256) {
     // grouped: 128 x 256 tiles, two workgroups per CU: one workgroup's fp32
     // epilogue overlaps the other's MFMAs, and an expert's last row tile
     // wastes at most 127 rows.  Measured at the Qwen3-30B-A3B MoE shapes
     // (128 experts, top-8 of 4096 tokens): up 111.5 -> 90.3 us, down
-    // 142.8 -> 130.0 us against the 256-row tile.  A bound on the tile
-    // count; surplus workgroups return at once.
+    // 142.8 -> 130.0 us against the 256-row tile.  A persistent grid of two
+    // workgroups per CU (at most the bound on the tile count); the expert
+    // table of up to 256 experts sits in registers.
     constexpr int GBM = 128;
+    const int bound = ((rows + GBM - 1) / GBM + n_groups) * ((D + 255) / 256);
+    const int grid = std::min(bound, 2 * ncu);
+#define T8G(PARTIAL_)                                                                                                 \
+  hipLaunchKernelGGL((linear_mx_tile8<GBM, 256, false, true, M24, PARTIAL_>), dim3(grid), dim3(2 * GBM), 0, s, bb_codes, \
+                     bb_meta, bb_scale, res_codes, res_scale, row_index, rows, act_rows, K, payload, wscale, D, n_groups, \
+                     group_offsets, Y, ldy)
+    if (partial) T8G(true);
+    else T8G(false);
+#undef T8G
+  } else {
+    // more than 256 experts: 256 x 256 tiles, one workgroup per tile (a
+    // bound on the tile count; surplus workgroups return at once), each
+    // locating its expert by a workgroup prefix sum
+    constexpr int GBM = 256;
     const int bound = ((rows + GBM - 1) / GBM + n_groups) * ((D + 255) / 256);
 #define T8G(PARTIAL_)                                                                                                 \
   hipLaunchKernelGGL((linear_mx_tile8<GBM, 256, false, true, M24, PARTIAL_>), dim3(bound), dim3(2 * GBM), 0, s, bb_codes, \

@@ -319,6 +319,51 @@ def test_grouped_eight_wave_tile(gather, K):
     assert_gemm_close(Y.cpu().numpy(), Yr, S)
 
 
+@pytest.mark.parametrize("K", [128, 640, 1024])
+@pytest.mark.parametrize("gather", [False, True])
+def test_grouped_persistent_many_tiles(gather, K):
+    # 800 grouped tiles of 128 x 256, more than the persistent grid's
+    # workgroups (two per CU), so workgroups run several tiles back to back:
+    # experts of 0 to 6000 rows (empty ones first, in the middle and last),
+    # one step per tile (K = 128), a partial last group of four steps
+    # (K = 640) and two whole groups (K = 1024), rows expert-sorted or
+    # gathered from 3000 activations
+    rng = np.random.default_rng(K + 7 * gather)
+    sizes = [0, 4000, 37, 0, 6000, 2900, 4500, 255, 1, 2300, 0]
+    E, D = len(sizes), 1280
+    go = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    R = int(go[-1])
+    T = 3000 if gather else R
+    ri = rng.integers(0, T, R).astype(np.int32) if gather else None
+    case = synth.random_case(40 + K, T, K, 1)
+    W = synth.f32_to_bf16_bits(rng.standard_normal((E, K, D)).astype(np.float32) * 0.02)
+    act = ops.prepare(dev_x(case), dev_gamma(case.gamma), 1e-6)
+    w = ops.pack_weight(dev_w(W, "bf16"))
+    Y = ops.linear(act, w, group_offsets=torch.from_numpy(go).cuda(),
+                   row_index=None if ri is None else torch.from_numpy(ri).cuda(), total_rows=R)
+    ref = oracle_prepare(case)
+    wps = [O.pack_weight(synth.bf16_bits_to_f32(W[e])) for e in range(E)]
+    Yr, S = O.grouped_linear(ref, wps, go, ri)
+    assert_gemm_close(Y.cpu().numpy(), Yr, S)
+
+
+def test_grouped_more_than_256_experts():
+    # 300 experts: the 256-row tile that locates its expert by a workgroup
+    # prefix sum (the persistent tile's expert table holds 256)
+    rng = np.random.default_rng(300)
+    E, T, K, D = 300, 200, 256, 96
+    go, ri = synth.draw_routing(rng, T, E, 3)
+    case = synth.random_case(300, T, K, 1)
+    W = synth.f32_to_bf16_bits(rng.standard_normal((E, K, D)).astype(np.float32) * 0.02)
+    act = ops.prepare(dev_x(case), dev_gamma(case.gamma), 1e-6)
+    w = ops.pack_weight(dev_w(W, "bf16"))
+    Y = ops.linear(act, w, group_offsets=torch.from_numpy(go).cuda(), row_index=torch.from_numpy(ri).cuda())
+    ref = oracle_prepare(case)
+    wps = [O.pack_weight(synth.bf16_bits_to_f32(W[e])) for e in range(E)]
+    Yr, S = O.grouped_linear(ref, wps, go, ri)
+    assert_gemm_close(Y.cpu().numpy(), Yr, S)
+
+
 @pytest.mark.parametrize("proj", ["up", "down"])
 def test_grouped_moe_full_sampled(proj):
     mc = synth.moe_case(proj)
