@@ -270,6 +270,29 @@ sharq_status sharq_quantize_mx(const float *Y, int32_t T, int32_t K, int64_t ldy
 sharq_status sharq_linear_dense(const uint8_t *codes, const uint8_t *scales, int32_t T,
                                 const sharq_weight *w, float *Y, int64_t ldy, void *stream);
 
+/* ---- Tile timeline (tracing).  The library built with SHARQ_TIMELINE
+ * defined (`python -m sparsity_sharq_prepare_amd.build --timeline` writes
+ * libsharq_timeline.so beside libsharq.so) has the tile GEMM of
+ * sharq_linear (MXFP4, more than 64 rows) record, from wave 0 of each tile,
+ * s_memrealtime stamps (a 100 MHz clock): word 0 the tile's start, word 1
+ * after its first step's wait and barrier, word 2 after its last step,
+ * word 3 after its epilogue stores are issued; word 4 holds the XCC id (high
+ * half) and the hardware id register (low half), word 5 the workgroup
+ * index, words 6 and 7 are zero.  The persistent 128-row tile (grouped
+ * linears, at most 256 experts) writes record t for tile t of its tile
+ * order; the 256-row tile writes record b for workgroup b.  Each launch
+ * overwrites the records it writes, so read after the launch of interest.
+ * The normal build exports the same entry points: its record count is 0
+ * and clear / read return INVALID_ARGUMENT.
+ * sharq_timeline_records: (host) out, the number of 8-word records.
+ * sharq_timeline_clear: zeroes every record (synchronous, device-wide).
+ * sharq_timeline_read: copies the first `words` words to `host` (host
+ * memory, synchronous); words <= 8 * records.
+ * Errors: INVALID_ARGUMENT, HIP. */
+sharq_status sharq_timeline_records(size_t *records);
+sharq_status sharq_timeline_clear(void);
+sharq_status sharq_timeline_read(uint64_t *host, size_t words);
+
 /* Static string naming a status code. */
 const char *sharq_status_string(sharq_status s);
 

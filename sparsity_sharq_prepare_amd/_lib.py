@@ -10,7 +10,9 @@ import ctypes
 import os
 from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_void_p
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsharq.so")
+# SHARQ_LIBRARY selects another build of the same library (the tile-timeline
+# build, libsharq_timeline.so); by default the in-tree libsharq.so
+LIB_PATH = os.environ.get("SHARQ_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsharq.so")
 
 SHARQ_OK = 0
 SHARQ_ERR_INVALID_ARGUMENT = 1
@@ -31,6 +33,7 @@ FORMATS = {"mxfp4": SHARQ_MXFP4, "nvfp4": SHARQ_NVFP4_EMU, "mxfp4_24": SHARQ_MXF
 EXPORTS = ("sharq_weight_sizes", "sharq_act_sizes", "sharq_pack_weight", "sharq_prepare", "sharq_prepare_no_alloc",
            "sharq_linear",
            "sharq_prepare_linear", "sharq_prepare_linear_status", "sharq_rmsnorm", "sharq_quantize_mx", "sharq_linear_dense",
+           "sharq_timeline_records", "sharq_timeline_clear", "sharq_timeline_read",
            "sharq_status_string", "sharq_last_error")
 
 
@@ -84,6 +87,11 @@ def lib() -> ctypes.CDLL:
         for name in ("sharq_weight_sizes", "sharq_act_sizes", "sharq_pack_weight", "sharq_prepare",
                      "sharq_prepare_no_alloc", "sharq_linear",
                      "sharq_prepare_linear", "sharq_prepare_linear_status", "sharq_rmsnorm", "sharq_quantize_mx", "sharq_linear_dense"):
+            getattr(L, name).restype = c_int32
+        L.sharq_timeline_records.argtypes = [POINTER(c_size_t)]
+        L.sharq_timeline_clear.argtypes = []
+        L.sharq_timeline_read.argtypes = [c_void_p, c_size_t]
+        for name in ("sharq_timeline_records", "sharq_timeline_clear", "sharq_timeline_read"):
             getattr(L, name).restype = c_int32
         L.sharq_status_string.argtypes = [c_int32]
         L.sharq_status_string.restype = c_char_p

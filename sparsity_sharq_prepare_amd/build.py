@@ -1,8 +1,10 @@
 """Build libsharq.so (the HIP kernels + C ABI) in-tree for gfx950.
 
 ``python -m sparsity_sharq_prepare_amd.build`` compiles every source under
-``csrc/`` with hipcc and links ``sparsity_sharq_prepare_amd/libsharq.so``.
-Objects go to ``_build/`` at the repository root (not committed).
+``csrc/`` with hipcc and links ``sparsity_sharq_prepare_amd/libsharq.so``;
+with ``--timeline`` it links the tile-timeline (tracing) build
+``libsharq_timeline.so`` instead.  Objects go to ``_build/`` at the
+repository root (not committed).
 """
 from __future__ import annotations
 
@@ -40,38 +42,46 @@ SOURCES = ["prepare.hip", "pack.hip", "gemm_mx.hip", "gemm_nv.hip", "api.cpp"]
 EXTRA_FLAGS = {"prepare.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+# the tile-timeline build (tracing): the tile GEMM records per-tile stamps
+TIMELINE_OUT = os.path.join(PKG, "libsharq_timeline.so")
+TIMELINE_BUILD = os.path.join(ROOT, "_build", "timeline")
+TIMELINE_FLAGS = {"gemm_mx.hip": ["-DSHARQ_TIMELINE"]}
+
+
+def _compile(src: str, build_dir: str = BUILD, extra: dict = None) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-I", os.path.join(ROOT, "include"), "-c",
-           os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), *(extra or {}).get(src, []), *lang, "-I",
+           os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile all sources and link libsharq.so; returns its path."""
+def build(verbose: bool = False, timeline: bool = False) -> str:
+    """Compile all sources and link libsharq.so (with ``timeline``: the
+    tile-timeline build, libsharq_timeline.so); returns its path."""
     if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(BUILD, exist_ok=True)
+    build_dir, out, extra = (TIMELINE_BUILD, TIMELINE_OUT, TIMELINE_FLAGS) if timeline else (BUILD, OUT, None)
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, build_dir, extra), SOURCES))
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {OUT}")
-    return OUT
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":
     try:
-        build(verbose=True)
+        build(verbose=True, timeline="--timeline" in sys.argv[1:])
     except RuntimeError as e:
         print(e, file=sys.stderr)
         sys.exit(1)

@@ -145,6 +145,27 @@ const char* sharq_status_string(sharq_status s) {
 
 const char* sharq_last_error(void) { return g_last_error.c_str(); }
 
+sharq_status sharq_timeline_records(size_t* records) {
+  if (!records) return fail(SHARQ_ERR_INVALID_ARGUMENT, "records is NULL");
+  *records = sharq::timeline_built() ? sharq::timeline_records() : 0;
+  return ok();
+}
+
+sharq_status sharq_timeline_clear(void) {
+  if (!sharq::timeline_built())
+    return fail(SHARQ_ERR_INVALID_ARGUMENT, "this library is not the tile-timeline build (SHARQ_TIMELINE)");
+  return from_hip(sharq::timeline_clear(), "sharq_timeline_clear");
+}
+
+sharq_status sharq_timeline_read(uint64_t* host, size_t words) {
+  if (!sharq::timeline_built())
+    return fail(SHARQ_ERR_INVALID_ARGUMENT, "this library is not the tile-timeline build (SHARQ_TIMELINE)");
+  if (!host) return fail(SHARQ_ERR_INVALID_ARGUMENT, "host is NULL");
+  if (words > sharq::timeline_records() * 8)
+    return fail(SHARQ_ERR_INVALID_ARGUMENT, "words = %zu exceeds the %zu recorded", words, sharq::timeline_records() * 8);
+  return from_hip(sharq::timeline_read(host, words), "sharq_timeline_read");
+}
+
 sharq_status sharq_weight_sizes(int32_t fmt, int32_t K, int32_t D, int32_t n_groups, size_t bytes_out[5]) {
   if (!bytes_out) return fail(SHARQ_ERR_INVALID_ARGUMENT, "bytes_out is NULL");
   if (!valid_fmt(fmt)) return fail(SHARQ_ERR_INVALID_ARGUMENT, "unknown format %d", fmt);

@@ -657,6 +657,39 @@ SHARQ_DEV bool find_group_tile(int bid, int n_groups, const int32_t* __restrict_
 }
 
 // ============================================================================
+// tile timeline (tracing build only, SHARQ_TIMELINE): wave 0 of each tile
+// records s_memrealtime stamps (100 MHz) at the tile's start, after its first
+// step's wait and barrier, after its last step and after its epilogue stores
+// are issued, plus the issuing XCC and hardware ids and the workgroup.  The
+// persistent 128-row tile writes record t for tile t; the 256-row tile (one
+// tile per workgroup) writes record b for workgroup b.
+// ============================================================================
+constexpr int kTimelineRecords = 16384;
+#ifdef SHARQ_TIMELINE
+__device__ uint64_t g_timeline[kTimelineRecords * 8];
+#define SHARQ_TL(t, i, v)                                                     \
+  do {                                                                        \
+    if (threadIdx.x == 0 && (t) < kTimelineRecords) g_timeline[(t) * 8 + (i)] = (v); \
+  } while (0)
+#define SHARQ_TL_ID(t)                                                                                        \
+  do {                                                                                                        \
+    SHARQ_TL(t, 4, ((uint64_t)__builtin_amdgcn_s_getreg(kHwRegXccId) << 32) |                                \
+                       (uint32_t)__builtin_amdgcn_s_getreg(kHwRegHwId));                                      \
+    SHARQ_TL(t, 5, blockIdx.x);                                                                               \
+  } while (0)
+// s_getreg_b32 operands: all 32 bits of HW_REG_HW_ID (4) and HW_REG_XCC_ID (20)
+constexpr int kHwRegHwId = (31 << 11) | 4, kHwRegXccId = (31 << 11) | 20;
+#else
+#define SHARQ_TL(t, i, v) \
+  do {                    \
+  } while (0)
+#define SHARQ_TL_ID(t) \
+  do {                 \
+  } while (0)
+#endif
+#define SHARQ_TL_NOW() __builtin_amdgcn_s_memrealtime()
+
+// ============================================================================
 // tile kernel (more than 64 rows; plain and grouped; K % 128 == 0)
 // ============================================================================
 // Tile 256 x 256 (or 224 columns), eight waves, two per SIMD covering each
@@ -993,6 +1026,8 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 1 : 2) void linear_mx_tile8(
     // barrier, but reads no fragments and issues no MFMAs, leaving its
     // SIMD's matrix core to the other wave there (uniform per wave)
     const bool live = m0 + wm0 < row_end;
+    SHARQ_TL(blockIdx.x, 0, SHARQ_TL_NOW());
+    SHARQ_TL_ID(blockIdx.x);
     zero_acc();
     issue_main(0, lds[0], o);
     issue_side(0, side[0], o);
@@ -1011,14 +1046,17 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 1 : 2) void linear_mx_tile8(
         if (p == 3) wait_vm_lgkm0<NMAIN + NSIDE>();
         else wait_vm_lgkm0<NMAIN>();
         __builtin_amdgcn_s_barrier();
+        if (s == 0) SHARQ_TL(blockIdx.x, 1, SHARQ_TL_NOW());
         issue_main(min(s + 2, KS - 1), lds[(s + 2) % NS], o);
         // side group g+1 replaces group g-1, last read at step 4 g - 1
         if (p == 2) issue_side(min(g + 1, G - 1), side[(g + 1) & 1], o);
         if (live) compute_step(lds[s % NS], sd, p);
       }
     }
+    SHARQ_TL(blockIdx.x, 2, SHARQ_TL_NOW());
     wait_vm_lgkm0<0>();                                // no DMA may land after the tile ends
     if (live) epilogue(o);
+    SHARQ_TL(blockIdx.x, 3, SHARQ_TL_NOW());
   } else {
     // ---- 128-row tiles, persistent: two workgroups per CU, each taking
     // every J-th tile of its XCD's stretch.  During a tile's last step the
@@ -1126,6 +1164,9 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 1 : 2) void linear_mx_tile8(
       // as in the 256-row tile: a wave past the tile's end issues its DMAs
       // and takes the barriers, but no fragment reads or MFMAs
       const bool live = cm0 + wm0 < cre;
+      const int cur_t = lo + k - J;                     // this tile's index
+      SHARQ_TL(cur_t, 0, SHARQ_TL_NOW());
+      SHARQ_TL_ID(cur_t);
       zero_acc();
       for (int g = 0; g < G; ++g) {
         const SideT& sd = side[(gbase + g) & 1];
@@ -1147,6 +1188,7 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 1 : 2) void linear_mx_tile8(
           __builtin_amdgcn_s_barrier();
           // the next tile's gathered rows: loaded here, first read at this
           // tile's last step, after its wait for every load
+          if (s == 0) SHARQ_TL(cur_t, 1, SHARQ_TL_NOW());
           if (s == 0 && has_next) tile_rows(nm0, nre, ntr);
           if (!last) {
             issue_main(s + 1, lds[(sbase + s + 1) & 1], oc);
@@ -1163,8 +1205,10 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 1 : 2) void linear_mx_tile8(
           if (live) compute_step(lds[(sbase + s) & 1], sd, p);
         }
       }
+      SHARQ_TL(cur_t, 2, SHARQ_TL_NOW());
       if (!has_next) wait_vm_lgkm0<0>();               // no DMA may land after the workgroup ends
       if (live) epilogue(oc);
+      SHARQ_TL(cur_t, 3, SHARQ_TL_NOW());
       if (!has_next) break;
       sbase += KS;
       gbase += G;
@@ -1395,6 +1439,34 @@ hipError_t launch_linear_mx_impl(const uint8_t* bb_codes, const uint8_t* bb_meta
   return hipGetLastError();
 }
 }  // namespace
+
+// ---- tile timeline accessors (tracing build; elsewhere they report absence)
+bool timeline_built() {
+#ifdef SHARQ_TIMELINE
+  return true;
+#else
+  return false;
+#endif
+}
+size_t timeline_records() { return kTimelineRecords; }
+hipError_t timeline_clear() {
+#ifdef SHARQ_TIMELINE
+  static uint64_t zeros[kTimelineRecords * 8];
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_timeline), zeros, sizeof(zeros), 0, hipMemcpyHostToDevice);
+#else
+  return hipErrorNotSupported;
+#endif
+}
+hipError_t timeline_read(uint64_t* host, size_t words) {
+#ifdef SHARQ_TIMELINE
+  if (words > (size_t)kTimelineRecords * 8) words = (size_t)kTimelineRecords * 8;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_timeline), words * sizeof(uint64_t), 0, hipMemcpyDeviceToHost);
+#else
+  (void)host;
+  (void)words;
+  return hipErrorNotSupported;
+#endif
+}
 
 hipError_t launch_linear_mx(const uint8_t* bb_codes, const uint8_t* bb_meta, const uint8_t* bb_scale,
                             const uint8_t* res_codes, const uint8_t* res_scale, const int32_t* row_index, int rows,

@@ -21,6 +21,12 @@ size_t prepare_nv_workspace(int T, int K);
 size_t scratch_max_bytes();
 hipError_t scratch_device_ptr(void** out);
 size_t pack_nv_workspace(int K, int D, int n_groups);
+// tile timeline of the tracing build (SHARQ_TIMELINE): whether this build
+// records it, its record count (8 words each), and synchronous clear / read
+bool timeline_built();
+size_t timeline_records();
+hipError_t timeline_clear();
+hipError_t timeline_read(uint64_t* host, size_t words);
 
 // m24: the 2:4 element-wise backbone (metadata K/8 bytes per row) instead of 4:8 in pairs
 hipError_t launch_prepare_mx(const void* X, bool bf16, int T, int K, int64_t ldx, const float* gamma, float eps,

@@ -238,3 +238,18 @@ def test_prepare_k_limit():
     assert lib.sharq_prepare(0x50000, 1, 8, K, K, None, 1e-6, a, None, 0, None) == L.SHARQ_ERR_UNSUPPORTED_SHAPE
     assert "maximum" in lib.sharq_last_error().decode()
     assert lib.sharq_rmsnorm(0x50000, 1, 8, K, K, None, 1e-6, 0x30000, K, None) == L.SHARQ_ERR_UNSUPPORTED_SHAPE
+
+
+def test_timeline_entry_points_of_the_normal_build():
+    # the tile-timeline entry points exist in every build; outside the
+    # SHARQ_TIMELINE build they report no records and refuse clear / read
+    # (host-side answers: nothing touches the GPU)
+    lib = L.lib()
+    n = ctypes.c_size_t(7)
+    assert lib.sharq_timeline_records(ctypes.byref(n)) == L.SHARQ_OK
+    assert n.value == 0
+    assert lib.sharq_timeline_records(None) == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert lib.sharq_timeline_clear() == L.SHARQ_ERR_INVALID_ARGUMENT
+    assert "timeline" in lib.sharq_last_error().decode()
+    buf = (ctypes.c_uint64 * 8)()
+    assert lib.sharq_timeline_read(buf, 8) == L.SHARQ_ERR_INVALID_ARGUMENT
