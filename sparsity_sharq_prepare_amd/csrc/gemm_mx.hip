@@ -13,20 +13,22 @@
 // column (l & 15), rows 4 * (l >> 4) .. +3.
 //
 // Three kernels:
-//  - skinny (T <= 64): weight streaming.  A 16-row MFMA tile holds the
-//    backbone of 8 tokens in rows 0-7 and their residual in rows 8-15, so one
-//    MFMA applies a weight fragment to both paths; the epilogue adds row r and
-//    row r + 8 of the tile.  K is split over the waves of a workgroup and the
-//    partial tiles are summed in a fixed order through LDS.
-//  - decode (T <= 16): the skinny scheme with the activation side staged once
-//    per workgroup in LDS in operand form, optionally fused with the
-//    preparation of the rows (single-launch decode).
+//  - skinny (T <= 64 at K > 16384): weight streaming.  A 16-row MFMA tile
+//    holds the backbone of 8 tokens in rows 0-7 and their residual in rows
+//    8-15, so one MFMA applies a weight fragment to both paths; the epilogue
+//    adds row r and row r + 8 of the tile.  K is split over the waves of a
+//    workgroup and the partial tiles are summed in a fixed order through LDS.
+//  - decode (T <= 64, K <= 16384): the skinny scheme with the activation
+//    side staged once per workgroup in LDS in operand form, one or two
+//    16-row MFMA tiles (8 or 16 tokens) per launch, larger T in chunks of
+//    launches; optionally fused with the preparation of the rows
+//    (single-launch decode, T <= 16).
 //  - tile8 (prefill and grouped MoE, more than 64 rows): 256 rows x 256 (or
 //    224) columns, eight waves, K steps of 128 staged by buffer->LDS DMA
 //    through a 3-deep ring (scales and metadata in a side ring of four-step
 //    groups); the compacted backbone is staged as is and expanded in
 //    registers right before its MFMAs.  Grouped: 128-row tiles, four waves,
-//    a 2-deep ring, two workgroups per CU.
+//    a 2-deep ring, a persistent grid of two workgroups per CU.
 #include "common.h"
 #include "kernels.h"
 #include "prep_device.h"
@@ -1331,23 +1333,29 @@ hipError_t launch_linear_mx_impl(const uint8_t* bb_codes, const uint8_t* bb_meta
   if (n_groups == 1 && rows <= 8 && K <= kDecodeMaxK)
     return launch_decode<false, M24>(bb_codes, bb_meta, bb_scale, res_codes, res_scale, row_index, rows, act_rows, K, payload,
                                 wscale, D, Y, ldy, FusedPrep{}, s);
-  if (n_groups == 1 && rows <= 16 && K <= kDecodeMaxK16)
-    return launch_decode<false, M24, 2>(bb_codes, bb_meta, bb_scale, res_codes, res_scale, row_index, rows, act_rows, K,
-                                        payload, wscale, D, Y, ldy, FusedPrep{}, s);
-  if (n_groups == 1 && rows <= 16 && K <= kDecodeMaxK) {
-    // 9-16 rows beyond the two-tile kernel's K: the 8-row kernel twice, rows
-    // 0-7 and the rest (each streams the weight once; measured at 16 x 14336
-    // x 4096 faster than the skinny kernel, 2 x 9.8 against 30 us)
-    if (hipError_t e = launch_decode<false, M24>(bb_codes, bb_meta, bb_scale, res_codes, res_scale, row_index, 8,
-                                                 act_rows, K, payload, wscale, D, Y, ldy, FusedPrep{}, s))
-      return e;
-    if (row_index)                                   // gathered rows: the second call reads row_index[8 ..]
-      return launch_decode<false, M24>(bb_codes, bb_meta, bb_scale, res_codes, res_scale, row_index + 8, rows - 8,
-                                       act_rows, K, payload, wscale, D, Y + 8 * ldy, ldy, FusedPrep{}, s);
-    const int64_t r8 = 8;
-    return launch_decode<false, M24>(bb_codes + r8 * (K >> 2), bb_meta + r8 * (K >> (M24 ? 3 : 4)), bb_scale + r8 * (K >> 5),
-                                     res_codes + r8 * (K >> 1), res_scale + r8 * (K >> 5), nullptr, rows - 8,
-                                     act_rows - 8, K, payload, wscale, D, Y + 8 * ldy, ldy, FusedPrep{}, s);
+  if (n_groups == 1 && rows <= 64 && K <= kDecodeMaxK) {
+    // 9-64 rows: the decode kernel on chunks of 16 rows (two MFMA tiles,
+    // K <= 7168) or 8 rows (one tile, K <= 16384), one launch per chunk,
+    // each streaming the weight once.  Measured against the skinny kernel
+    // (Llama-3.1-8B decode shapes, 4096 x 4096 / 4096 x 14336 / 14336 x 4096):
+    // 16 rows 6.6 / 11.0 / 18.0 (two 8-row launches) against - / - / 30.0 us;
+    // the skinny kernel took 19.9 / 73.6 / 50.6 us at 32 rows and 32.4 /
+    // 108.5 / 93.5 us at 64.
+    const int chunk = K <= kDecodeMaxK16 ? 16 : 8;
+    for (int r0 = 0; r0 < rows; r0 += chunk) {
+      const int n = std::min(chunk, rows - r0);
+      const int64_t o = row_index ? 0 : r0;             // gathered rows: row_index[r0 ..] instead
+      const int32_t* ri = row_index ? row_index + r0 : nullptr;
+      const uint8_t *bc = bb_codes + o * (K >> 2), *bm = bb_meta + o * (K >> (M24 ? 3 : 4)),
+                    *bs = bb_scale + o * (K >> 5), *rc = res_codes + o * (K >> 1), *rs = res_scale + o * (K >> 5);
+      const int ar = act_rows - (int)o;
+      float* y = Y + (int64_t)r0 * ldy;
+      const hipError_t e =
+          n > 8 ? launch_decode<false, M24, 2>(bc, bm, bs, rc, rs, ri, n, ar, K, payload, wscale, D, y, ldy, FusedPrep{}, s)
+                : launch_decode<false, M24>(bc, bm, bs, rc, rs, ri, n, ar, K, payload, wscale, D, y, ldy, FusedPrep{}, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
   if (n_groups == 1 && rows <= 64) {
     const int KS = K / 128;

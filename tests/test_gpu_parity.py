@@ -156,7 +156,7 @@ def test_linear_tiny_config():
     assert_gemm_close(Y.cpu().numpy(), Yr, S)
 
 
-LINEAR_SHAPES = [  # skinny (T <= 64) and tile paths, ragged rows and columns
+LINEAR_SHAPES = [  # decode (T <= 64, in chunks), skinny and tile paths, ragged rows and columns
     (1, 512, 200), (8, 512, 200), (13, 256, 64), (64, 384, 130), (65, 512, 300), (300, 512, 520),
     (256, 1024, 256), (700, 128, 40),
     # K % 512 != 0 on the tile path: 3, 5 and 6 steps of 128 (a partial last
@@ -170,6 +170,11 @@ LINEAR_SHAPES = [  # skinny (T <= 64) and tile paths, ragged rows and columns
     # twice (rows 0-7 and the rest) up to K = 16384, then the skinny path
     (16, 4096, 300), (9, 1152, 72), (12, 2048, 4100), (11, 7168, 64), (16, 7296, 40),
     (9, 14336, 72), (10, 16512, 40),
+    # 17-64 rows: 16-row chunks (K <= 7168; a ragged last chunk of 1-8 rows
+    # on the one-tile kernel), 8-row chunks (K <= 16384), the skinny path
+    # beyond
+    (17, 512, 64), (32, 4096, 300), (40, 2048, 4100), (57, 1152, 200), (64, 7168, 48), (64, 7296, 40),
+    (33, 14336, 72), (40, 16512, 48), (64, 16512, 40),
     # degenerate widths: one output column, the smallest GEMM K
     (3, 256, 1), (70, 512, 1), (1, 128, 16),
 ]
@@ -185,11 +190,13 @@ def test_linear_shapes(T, K, D):
     assert_gemm_close(Y.cpu().numpy(), Yr, S)
 
 
-@pytest.mark.parametrize("T,K,n", [(8, 256, 13), (200, 256, 205), (6, 256, 5), (12, 8192, 14)])
+@pytest.mark.parametrize("T,K,n", [(8, 256, 13), (200, 256, 205), (6, 256, 5), (12, 8192, 14), (30, 1024, 50),
+                                   (20, 8192, 27)])
 def test_linear_row_gather(T, K, n):
     # n gathered output rows: the two-tile decode kernel (13), the tile path
-    # (205), the one-tile decode kernel (5) and two one-tile launches (14
-    # rows at K = 8192, the second reading row_index from entry 8)
+    # (205), the one-tile decode kernel (5), two one-tile launches (14 rows
+    # at K = 8192, the second reading row_index from entry 8), 16-row chunks
+    # (50 rows, the last chunk 2) and 8-row chunks (27 rows at K = 8192)
     case = synth.random_case(99 + T, T, K, 96)
     act = ops.prepare(dev_x(case), dev_gamma(case.gamma), 1e-6)
     w = ops.pack_weight(dev_w(case.w, "bf16"))
@@ -206,6 +213,21 @@ def test_linear_decode_full_sampled(i):
     ref = oracle_prepare(case)
     compare_act(act, ref)
     r, c = sample_pairs(case.T, case.D, 3000, seed=case.K)
+    Yr, S = O.sharq_linear_sampled(ref, O.pack_weight(case.w_f32()), r, c)
+    assert_gemm_close(Y.cpu().numpy()[r, c], Yr, S)
+
+
+@pytest.mark.parametrize("i", range(3), ids=DECODE_IDS)
+@pytest.mark.parametrize("T", [16, 40, 64])
+def test_linear_decode_batch_full_sampled(T, i):
+    # batched decode at the full Llama-3.1-8B shapes: 16 rows on the two-tile
+    # kernel (or two one-tile launches at K = 14336), 40 and 64 rows in
+    # chunks of launches
+    case = synth.decode_case(i, T=T)
+    act, w, Y = run_case(case)
+    ref = oracle_prepare(case)
+    compare_act(act, ref)
+    r, c = sample_pairs(case.T, case.D, 3000, seed=case.K + T)
     Yr, S = O.sharq_linear_sampled(ref, O.pack_weight(case.w_f32()), r, c)
     assert_gemm_close(Y.cpu().numpy()[r, c], Yr, S)
 
@@ -344,6 +366,23 @@ def test_grouped_persistent_many_tiles(gather, K):
     ref = oracle_prepare(case)
     wps = [O.pack_weight(synth.bf16_bits_to_f32(W[e])) for e in range(E)]
     Yr, S = O.grouped_linear(ref, wps, go, ri)
+    assert_gemm_close(Y.cpu().numpy(), Yr, S)
+
+
+def test_grouped_fewer_workgroups_than_xcds():
+    # two experts of 100 and 30 rows, one column tile: a grid of 3
+    # workgroups (the tile order is cut into 3 stretches, not 8)
+    rng = np.random.default_rng(3)
+    E, K, D = 2, 256, 96
+    go = np.array([0, 100, 130], dtype=np.int32)
+    case = synth.random_case(3, 130, K, 1)
+    W = synth.f32_to_bf16_bits(rng.standard_normal((E, K, D)).astype(np.float32) * 0.02)
+    act = ops.prepare(dev_x(case), dev_gamma(case.gamma), 1e-6)
+    w = ops.pack_weight(dev_w(W, "bf16"))
+    Y = ops.linear(act, w, group_offsets=torch.from_numpy(go).cuda())
+    ref = oracle_prepare(case)
+    wps = [O.pack_weight(synth.bf16_bits_to_f32(W[e])) for e in range(E)]
+    Yr, S = O.grouped_linear(ref, wps, go, None)
     assert_gemm_close(Y.cpu().numpy(), Yr, S)
 
 
