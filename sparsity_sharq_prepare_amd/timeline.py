@@ -65,6 +65,28 @@ def summarize(rec: np.ndarray) -> dict:
     return out
 
 
+def summarize_batch(rec: np.ndarray) -> dict:
+    """Phases of the batch kernel (17-64 rows), one record per workgroup:
+    words 0 start, 1 first chunk staged, 6 first chunk multiplied, 7 second
+    chunk staged, 2 last chunk multiplied, 3 stored."""
+    rec = rec[rec[:, 0] > 0].astype(np.int64)
+    us = 1e6 / CLOCK_HZ
+    ph = {"first chunk loaded and staged": rec[:, 1] - rec[:, 0],
+          "first chunk multiplied": rec[:, 6] - rec[:, 1],
+          "second chunk staged": rec[:, 7] - rec[:, 6],
+          "remaining chunks": rec[:, 2] - rec[:, 7],
+          "reduction and stores": rec[:, 3] - rec[:, 2]}
+    t0 = rec[:, 0].min()
+    return {"records": int(len(rec)), "workgroups": int(len(rec)), "span_us": float((rec[:, 3].max() - t0) * us),
+            "phases_us": {k: {"mean": float(v.mean() * us), "p10": float(np.percentile(v, 10) * us),
+                              "p50": float(np.median(v) * us), "p90": float(np.percentile(v, 90) * us)}
+                          for k, v in ph.items()},
+            "tiles_per_workgroup": {1: int(len(rec))},
+            "workgroup_end_us": {"p10": float(np.percentile((rec[:, 3] - t0) * us, 10)),
+                                 "p50": float(np.median((rec[:, 3] - t0) * us)),
+                                 "max": float((rec[:, 3].max() - t0) * us)}}
+
+
 def format_summary(name: str, s: dict, event_us: float) -> list:
     lines = [f"{name}: launch {event_us:.1f} us (HIP events); {s['records']} tile records, "
              f"{s['workgroups']} workgroups; first start to last epilogue {s['span_us']:.1f} us"]
@@ -96,6 +118,13 @@ def _jobs(workload: str):
             Y = ops.linear(act, w, group_offsets=go, row_index=ri, total_rows=mc.total_rows)
             jobs.append((mc.name, lambda act=act, w=w, go=go, ri=ri, Y=Y, n=mc.total_rows:
                          ops.linear(act, w, group_offsets=go, row_index=ri, total_rows=n, out=Y)))
+    elif workload == "batch":
+        for i, T in ((1, 32), (2, 64)):               # 4096 x 14336 at 32 rows, 14336 x 4096 at 64
+            c = synth.decode_case(i, T=T)
+            w = ops.pack_weight(bf16(c.w))
+            act = ops.prepare(bf16(c.x), torch.from_numpy(c.gamma).cuda(), 1e-6)
+            Y = ops.linear(act, w)
+            jobs.append((f"{c.name}_T{T}", lambda act=act, w=w, Y=Y: ops.linear(act, w, out=Y)))
     elif workload == "prefill":
         c = synth.prefill_case()
         w = ops.pack_weight(bf16(c.w))
@@ -109,7 +138,7 @@ def _jobs(workload: str):
 
 def main(argv=None) -> int:
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    p.add_argument("--workload", default="moe", choices=["moe", "prefill"])
+    p.add_argument("--workload", default="moe", choices=["moe", "prefill", "batch"])
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--out", default=None, help="write the summary here as well")
     a = p.parse_args(argv)
@@ -124,7 +153,8 @@ def main(argv=None) -> int:
         raise SystemExit(f"{L.LIB_PATH} is not the tile-timeline build: "
                          "run `python -m sparsity_sharq_prepare_amd.build --timeline`")
     buf = np.zeros(n.value * 8, dtype=np.uint64)
-    lines = [f"# tile timeline of linear_mx_tile8 ({a.workload} workload), s_memrealtime stamps of the "
+    kernel = "linear_mx_batch" if a.workload == "batch" else "linear_mx_tile8"
+    lines = [f"# timeline of {kernel} ({a.workload} workload), s_memrealtime stamps of the "
              f"SHARQ_TIMELINE build",
              f"# command: python -m sparsity_sharq_prepare_amd.build --timeline && "
              f"python -m sparsity_sharq_prepare_amd.timeline --workload {a.workload}"
@@ -140,7 +170,8 @@ def main(argv=None) -> int:
         e1.record()
         torch.cuda.synchronize()
         L.check(lib.sharq_timeline_read(buf.ctypes.data_as(ctypes.c_void_p), ctypes.c_size_t(buf.size)))
-        lines += format_summary(name, summarize(buf.reshape(-1, 8)), e0.elapsed_time(e1) * 1e3)
+        summ = summarize_batch if a.workload == "batch" else summarize
+        lines += format_summary(name, summ(buf.reshape(-1, 8)), e0.elapsed_time(e1) * 1e3)
     text = "\n".join(lines) + "\n"
     sys.stdout.write(text)
     if a.out:

@@ -170,11 +170,12 @@ LINEAR_SHAPES = [  # decode (T <= 64, in chunks), skinny and tile paths, ragged 
     # twice (rows 0-7 and the rest) up to K = 16384, then the skinny path
     (16, 4096, 300), (9, 1152, 72), (12, 2048, 4100), (11, 7168, 64), (16, 7296, 40),
     (9, 14336, 72), (10, 16512, 40),
-    # 17-64 rows: 16-row chunks (K <= 7168; a ragged last chunk of 1-8 rows
-    # on the one-tile kernel), 8-row chunks (K <= 16384), the skinny path
-    # beyond
+    # 17-64 rows: the batch kernel (32 or 64 MFMA rows; column groups of 1,
+    # 2 and 4; partial last K chunks; K beyond the decode kernel's), and
+    # 17-32 rows over wide outputs at K <= 7168 on 16-row decode launches
     (17, 512, 64), (32, 4096, 300), (40, 2048, 4100), (57, 1152, 200), (64, 7168, 48), (64, 7296, 40),
-    (33, 14336, 72), (40, 16512, 48), (64, 16512, 40),
+    (33, 14336, 72), (40, 16512, 48), (64, 16512, 40), (24, 640, 13000), (64, 384, 8200), (48, 18944, 130),
+    (40, 1024, 13000), (20, 7296, 12800),
     # degenerate widths: one output column, the smallest GEMM K
     (3, 256, 1), (70, 512, 1), (1, 128, 16),
 ]
@@ -797,8 +798,10 @@ def test_prepare_24_edge_rows():
     compare_act(act, O.prepare(x, g, 1e-6, "mxfp4", mask="2:4"))
 
 
-M24_LINEAR = [  # decode (<= 8 rows), skinny (<= 64), eight-wave tile (> 64 rows, any K % 128), ragged
+M24_LINEAR = [  # decode (<= 16 rows; 17-64 in chunks of launches up to K = 16384), skinny (<= 64 rows
+    # beyond), eight-wave tile (> 64 rows, any K % 128), ragged
     (1, 512, 200), (8, 512, 200), (5, 1152, 72), (7, 16384, 48), (13, 256, 64), (64, 384, 130),
+    (40, 2048, 300), (33, 8192, 72), (20, 16512, 40),
     (65, 512, 300), (300, 512, 520), (700, 128, 40), (256, 1024, 256), (70, 512, 1),
     (100, 384, 72), (333, 768, 250),
 ]
