@@ -70,6 +70,8 @@ def summarize_batch(rec: np.ndarray) -> dict:
     words 0 start, 1 first chunk staged, 6 first chunk multiplied, 7 second
     chunk staged, 2 last chunk multiplied, 3 stored."""
     rec = rec[rec[:, 0] > 0].astype(np.int64)
+    if len(rec) == 0:
+        raise ValueError("no records: the launch did not run the batch kernel")
     us = 1e6 / CLOCK_HZ
     ph = {"first chunk loaded and staged": rec[:, 1] - rec[:, 0],
           "first chunk multiplied": rec[:, 6] - rec[:, 1],
@@ -119,7 +121,7 @@ def _jobs(workload: str):
             jobs.append((mc.name, lambda act=act, w=w, go=go, ri=ri, Y=Y, n=mc.total_rows:
                          ops.linear(act, w, group_offsets=go, row_index=ri, total_rows=n, out=Y)))
     elif workload == "batch":
-        for i, T in ((1, 32), (2, 64)):               # 4096 x 14336 at 32 rows, 14336 x 4096 at 64
+        for i, T in ((1, 40), (2, 64)):               # 4096 x 14336 at 40 rows, 14336 x 4096 at 64
             c = synth.decode_case(i, T=T)
             w = ops.pack_weight(bf16(c.w))
             act = ops.prepare(bf16(c.x), torch.from_numpy(c.gamma).cuda(), 1e-6)
