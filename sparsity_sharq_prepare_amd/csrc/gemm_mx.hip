@@ -668,15 +668,18 @@ SHARQ_DEV bool find_group_tile(int bid, int n_groups, const int32_t* __restrict_
 // step's wait and barrier, after its last step and after its epilogue stores
 // are issued, plus the issuing XCC and hardware ids and the workgroup.  The
 // persistent 128-row tile writes record t for tile t; the 256-row tile (one
-// tile per workgroup) writes record b for workgroup b.
+// tile per workgroup) writes record b for workgroup b.  The batch kernel
+// writes record b for workgroup b, its staging phases from the first thread
+// of its first staging wave.
 // ============================================================================
 constexpr int kTimelineRecords = 16384;
 #ifdef SHARQ_TIMELINE
 __device__ uint64_t g_timeline[kTimelineRecords * 8];
-#define SHARQ_TL(t, i, v)                                                     \
-  do {                                                                        \
-    if (threadIdx.x == 0 && (t) < kTimelineRecords) g_timeline[(t) * 8 + (i)] = (v); \
+#define SHARQ_TL_BY(th, t, i, v)                                                        \
+  do {                                                                                  \
+    if (threadIdx.x == (th) && (t) < kTimelineRecords) g_timeline[(t) * 8 + (i)] = (v); \
   } while (0)
+#define SHARQ_TL(t, i, v) SHARQ_TL_BY(0, t, i, v)
 #define SHARQ_TL_ID(t)                                                                                        \
   do {                                                                                                        \
     SHARQ_TL(t, 4, ((uint64_t)__builtin_amdgcn_s_getreg(kHwRegXccId) << 32) |                                \
@@ -686,6 +689,9 @@ __device__ uint64_t g_timeline[kTimelineRecords * 8];
 // s_getreg_b32 operands: all 32 bits of HW_REG_HW_ID (4) and HW_REG_XCC_ID (20)
 constexpr int kHwRegHwId = (31 << 11) | 4, kHwRegXccId = (31 << 11) | 20;
 #else
+#define SHARQ_TL_BY(th, t, i, v) \
+  do {                           \
+  } while (0)
 #define SHARQ_TL(t, i, v) \
   do {                    \
   } while (0)
@@ -700,24 +706,31 @@ constexpr int kHwRegHwId = (31 << 11) | 4, kHwRegXccId = (31 << 11) | 20;
 // activation operand staged in chunks of K, so the weight is read once for
 // all rows at any K
 // ============================================================================
-// grid.x = ceil(D / (16 CG)); NW = CG NK waves.  K is processed in chunks of
-// KC = NK JC steps of 128: the chunk's activation pieces (coalesced 16-byte
-// pieces of the token rows, as in the decode kernel) go to registers while
-// the previous chunk is multiplied, then into one of two LDS stages in
-// operand form (backbone expanded).  Wave (cg, kw) multiplies steps
-// kw JC .. kw JC + JC - 1 of every chunk for the 16 columns of column group
-// cg, with weights loaded two chunks ahead; the NK partial tiles of a column
-// group are summed in a fixed order through LDS at the end.  MT MFMA tiles of
-// 16 rows (tile m: the backbone of tokens 8 m .. 8 m + 7 in rows 0-7, their
-// residual in rows 8-15) share each weight fragment.  Every slot of a stage
-// is written each chunk (absent tokens and blocks past K as zeros), so a
-// product never meets a stale byte.
+// grid.x = ceil(D / (16 CG)); CG NK = 4 compute waves and 4 staging waves.  K is
+// processed in chunks of KC = NK JC steps of 128, through two LDS stages
+// holding the chunk's activation operand (backbone expanded) and scales.
+//  - Staging waves load a chunk's pieces (coalesced 16-byte pieces of the
+//    token rows, as in the decode kernel) two chunks ahead into registers and
+//    write them to a stage in operand form.
+//  - Compute wave (cg, kw) multiplies steps kw JC .. kw JC + JC - 1 of every
+//    chunk for the 16 columns of column group cg, with its weights loaded
+//    two chunks ahead.
+// A wave's loads complete in order, so splitting the two streams over
+// different waves lets each run ahead without waiting for the other.  MT
+// MFMA tiles of 16 rows (tile m: the backbone of tokens 8 m .. 8 m + 7 in
+// rows 0-7, their residual in rows 8-15) share each weight fragment; the NK
+// partial tiles of a column group are summed in a fixed order through LDS at
+// the end.  Every slot of a stage is written each chunk (absent tokens and
+// blocks past K as zeros), so a product never meets a stale byte.
+constexpr int kBatchStagingWaves = 4;
 template <int MT, int CG, int NK, int JC>
-__global__ __launch_bounds__(CG * NK * 64) void linear_mx_batch(
+__global__ __launch_bounds__((CG * NK + kBatchStagingWaves) * 64) void linear_mx_batch(
     const uint8_t* bb_codes, const uint8_t* bb_meta, const uint8_t* bb_scale, const uint8_t* res_codes,
     const uint8_t* res_scale, const int32_t* __restrict__ row_index, int rows, int act_rows, int K,
     const uint8_t* __restrict__ payload, const uint8_t* __restrict__ wscale, int D, float* __restrict__ Y, int64_t ldy) {
-  constexpr int NW = CG * NK, NT = NW * 64;
+  constexpr int NCW = CG * NK;                          // compute waves
+  static_assert(NCW == 4, "four compute waves");
+  constexpr int NST = kBatchStagingWaves * 64;          // staging threads
   constexpr int NR = 16 * MT;                          // MFMA rows per step
   constexpr int KC = NK * JC;                          // steps per chunk
   constexpr int BC = 4 * KC;                           // 32-value blocks per chunk
@@ -727,15 +740,12 @@ __global__ __launch_bounds__(CG * NK * 64) void linear_mx_batch(
   // piece's store, consecutive blocks of one row, is contiguous
   constexpr int BCP = BC + 1;
   static_assert((SP / 4) % 2 == 1, "scale pitch");
+  constexpr int WD = 2;                                // weight chunks in flight per compute wave
   constexpr uint32_t kOut = 0x80000000u;             // offset past every buffer here: reads zero
-  // residual pieces: 8 MT token slots x BC blocks; backbone pieces: 8 MT x
-  // BC / 2 block pairs; scale pieces: NR rows x BC / 16
-  constexpr int NRES = 8 * MT * BC, NBB = 8 * MT * BC / 2, NSC = NR * (BC / 16);
-  constexpr int RPT = (NRES + NT - 1) / NT, BPT = (NBB + NT - 1) / NT, SPT = (NSC + NT - 1) / NT;
   extern __shared__ uint4 dsm[];
   uint4* const a_st = dsm;                                                       // [2][NR][BCP]
   uint8_t* const s_st = reinterpret_cast<uint8_t*>(dsm + 2 * NR * BCP);          // [2][NR][SP]
-  float* const red = reinterpret_cast<float*>(dsm);                              // after the last chunk: [NW][MT][64][4]
+  float* const red = reinterpret_cast<float*>(dsm);                              // after the last chunk: [NCW][MT][64][4]
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int KB = K >> 5, KS = K >> 7, NC = (KS + KC - 1) / KC;
@@ -743,157 +753,202 @@ __global__ __launch_bounds__(CG * NK * 64) void linear_mx_batch(
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0,
                                              __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
   };
-  const int an = __builtin_amdgcn_readfirstlane(act_rows);
-  const __amdgpu_buffer_rsrc_t r_rc = rsrc(res_codes, (int64_t)an * (K >> 1));
-  const __amdgpu_buffer_rsrc_t r_rs = rsrc(res_scale, (int64_t)an * (K >> 5));
-  const __amdgpu_buffer_rsrc_t r_bc = rsrc(bb_codes, (int64_t)an * (K >> 2));
-  const __amdgpu_buffer_rsrc_t r_bm = rsrc(bb_meta, (int64_t)an * (K >> 4));
-  const __amdgpu_buffer_rsrc_t r_bs = rsrc(bb_scale, (int64_t)an * (K >> 5));
-
-  // per-thread piece coordinates (chunk independent): token slot and block
-  // within the chunk; the activation row of a token slot (or none)
-  auto act_row = [&](int t) -> uint32_t {
-    return t < rows ? (uint32_t)gather_row(row_index, t, act_rows) : kOut;
-  };
-  uint32_t res_row[RPT], bb_row[BPT], sc_row[SPT];
-#pragma unroll
-  for (int j = 0; j < RPT; ++j) {
-    const int i = tid + NT * j, t = i / BC;
-    res_row[j] = i < NRES ? act_row(t) : kOut;
-  }
-#pragma unroll
-  for (int j = 0; j < BPT; ++j) {
-    const int i = tid + NT * j, t = i / (BC / 2);
-    bb_row[j] = i < NBB ? act_row(t) : kOut;
-  }
-#pragma unroll
-  for (int j = 0; j < SPT; ++j) {
-    const int i = tid + NT * j, r = i / (BC / 16), t = 8 * (r >> 4) + (r & 7);
-    sc_row[j] = i < NSC ? act_row(t) : kOut;
-  }
-  uint4 rv[RPT], bv[BPT], sv[SPT];
-  uint32_t mv[BPT];
-  // chunk c's pieces into registers (blocks past K read zero)
-  auto load_chunk = [&](int c) {
-    const int b0 = c * BC;                             // first block of the chunk
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      const int i = tid + NT * j, kb = b0 + i % BC;
-      const uint32_t off = res_row[j] != kOut && kb < KB ? res_row[j] * (uint32_t)(K >> 1) + 16u * kb : kOut;
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(r_rc, off, 0, 0);
-      rv[j] = make_uint4(v[0], v[1], v[2], v[3]);
-    }
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-      const int i = tid + NT * j, kp = (b0 >> 1) + i % (BC / 2);
-      const bool ok = bb_row[j] != kOut && 2 * kp < KB;
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(r_bc, ok ? bb_row[j] * (uint32_t)(K >> 2) + 16u * kp : kOut, 0, 0);
-      bv[j] = make_uint4(v[0], v[1], v[2], v[3]);
-      mv[j] = __builtin_amdgcn_raw_buffer_load_b32(r_bm, ok ? bb_row[j] * (uint32_t)(K >> 4) + 4u * kp : kOut, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < SPT; ++j) {
-      const int i = tid + NT * j, r = i / (BC / 16), p = i % (BC / 16), kb = b0 + 16 * p;
-      // bytes past the row's K / 32 are the next row's scales (or zero past
-      // the buffer): finite, and met only by zero weights
-      const uint32_t off = sc_row[j] != kOut && kb < KB ? sc_row[j] * (uint32_t)(K >> 5) + kb : kOut;
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128((r & 8) == 0 ? r_bs : r_rs, off, 0, 0);
-      sv[j] = make_uint4(v[0], v[1], v[2], v[3]);
-    }
-  };
-  // the registers of a chunk into LDS stage st, in operand form
-  auto store_chunk = [&](int st) {
-    uint4* const a = a_st + st * NR * BCP;
-    uint8_t* const sc = s_st + st * NR * SP;
-#pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      const int i = tid + NT * j, t = i / BC, kb = i % BC;
-      if (i < NRES) a[(16 * (t >> 3) + 8 + (t & 7)) * BCP + kb] = rv[j];
-    }
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-      const int i = tid + NT * j, t = i / (BC / 2), kp = i % (BC / 2), tr = 16 * (t >> 3) + (t & 7);
-      if (i < NBB) {
-        a[tr * BCP + 2 * kp] = expand4_fast(bv[j].x, bv[j].y, mv[j] & 0xFFFFu);
-        a[tr * BCP + 2 * kp + 1] = expand4_fast(bv[j].z, bv[j].w, mv[j] >> 16);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < SPT; ++j) {
-      const int i = tid + NT * j, r = i / (BC / 16), p = i % (BC / 16);
-      if (i < NSC) {
-        // 4-byte stores: SP is a multiple of 4, not of 16
-        uint32_t* dst = reinterpret_cast<uint32_t*>(sc + r * SP + 16 * p);
-        dst[0] = sv[j].x; dst[1] = sv[j].y; dst[2] = sv[j].z; dst[3] = sv[j].w;
-      }
-    }
-  };
-
-  // ---- weights of this wave's steps, two chunks ahead
-  const int cg = w % CG, kw = w / CG;
+  const int cg = w % CG, kw = w / CG;                  // compute waves
   const int col = (blockIdx.x * CG + cg) * 16 + (l & 15);
   const int kq = l >> 4;
-  const __amdgpu_buffer_rsrc_t r_w = rsrc(payload, (int64_t)D * (K >> 1));
-  const __amdgpu_buffer_rsrc_t r_ws = rsrc(wscale, (int64_t)D * (K >> 5));
-  const uint32_t o_w = col < D ? (uint32_t)col * (uint32_t)(K >> 1) + 16u * kq : kOut;
-  const uint32_t o_ws = col < D ? (uint32_t)col * (uint32_t)(K >> 5) : kOut;
-  uint4 wv[2][JC];
-  uint32_t wsd[2][JC];                                 // dword: the 4 block scales of the step (byte kq)
-  auto load_w = [&](int c, int b) {
-#pragma unroll
-    for (int j = 0; j < JC; ++j) {
-      const int s = c * KC + kw * JC + j;
-      const uint32_t out = s < KS ? 0u : kOut;
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(r_w, (o_w + 64u * (uint32_t)s) | out, 0, 0);
-      wv[b][j] = make_uint4(v[0], v[1], v[2], v[3]);
-      wsd[b][j] = __builtin_amdgcn_raw_buffer_load_b32(r_ws, (o_ws + 4u * (uint32_t)s) | out, 0, 0);
-    }
-  };
-
   v4f acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = (v4f){0.f, 0.f, 0.f, 0.f};
   SHARQ_TL(blockIdx.x, 0, SHARQ_TL_NOW());
   SHARQ_TL_ID(blockIdx.x);
-  load_chunk(0);
-  load_w(0, 0);
-  if (NC > 1) load_w(1, 1);
-  store_chunk(0);
-  SHARQ_TL(blockIdx.x, 1, SHARQ_TL_NOW());
-  for (int c = 0; c < NC; ++c) {
-    if (c + 1 < NC) load_chunk(c + 1);
-    // stage c % 2 is written; every wave is past chunk c - 1, which read
-    // the stage chunk c + 1 goes to
-    __syncthreads();
-    const uint4* const a = a_st + (c & 1) * NR * BCP;
-    const uint8_t* const sc = s_st + (c & 1) * NR * SP;
-    const int b = c & 1;
+
+  if (w >= NCW) {
+    // ---- staging waves.  Residual pieces: 8 MT token slots x BC blocks;
+    // backbone pieces: 8 MT x BC / 2 block pairs; scale pieces: NR rows x
+    // BC / 16.  Two register sets: chunk k's pieces in set k & 1.
+    constexpr int NRES = 8 * MT * BC, NBB = 8 * MT * BC / 2, NSC = NR * (BC / 16);
+    constexpr int RPT = (NRES + NST - 1) / NST, BPT = (NBB + NST - 1) / NST, SPT = (NSC + NST - 1) / NST;
+    const int ts = tid - NCW * 64;
+    const int an = __builtin_amdgcn_readfirstlane(act_rows);
+    const __amdgpu_buffer_rsrc_t r_rc = rsrc(res_codes, (int64_t)an * (K >> 1));
+    const __amdgpu_buffer_rsrc_t r_rs = rsrc(res_scale, (int64_t)an * (K >> 5));
+    const __amdgpu_buffer_rsrc_t r_bc = rsrc(bb_codes, (int64_t)an * (K >> 2));
+    const __amdgpu_buffer_rsrc_t r_bm = rsrc(bb_meta, (int64_t)an * (K >> 4));
+    const __amdgpu_buffer_rsrc_t r_bs = rsrc(bb_scale, (int64_t)an * (K >> 5));
+    // the activation row of each of this thread's pieces (or none)
+    auto act_row = [&](int t) -> uint32_t {
+      return t < rows ? (uint32_t)gather_row(row_index, t, act_rows) : kOut;
+    };
+    uint32_t res_row[RPT], bb_row[BPT], sc_row[SPT];
 #pragma unroll
-    for (int j = 0; j < JC; ++j) {
-      const int sl = kw * JC + j;                      // step within the chunk
+    for (int j = 0; j < RPT; ++j) {
+      const int i = ts + NST * j;
+      res_row[j] = i < NRES ? act_row(i / BC) : kOut;
+    }
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const int r = 16 * m + (l & 15);
-        acc[m] = mfma_fp4(a[r * BCP + 4 * sl + kq], wv[b][j], acc[m], sc[r * SP + 4 * sl + kq],
-                          (wsd[b][j] >> (8 * kq)) & 0xFFu);
+    for (int j = 0; j < BPT; ++j) {
+      const int i = ts + NST * j;
+      bb_row[j] = i < NBB ? act_row(i / (BC / 2)) : kOut;
+    }
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      const int i = ts + NST * j, r = i / (BC / 16);
+      sc_row[j] = i < NSC ? act_row(8 * (r >> 4) + (r & 7)) : kOut;
+    }
+    uint4 rv[2][RPT], bv[2][BPT], sv[2][SPT];
+    uint32_t mv[2][BPT];
+    // chunk c's pieces into register set q (blocks past K read zero); the
+    // set index is a compile-time constant (the loop below is unrolled by
+    // two), so the sets stay in registers
+    auto load_chunk = [&](int c, auto qc) {
+      constexpr int q = decltype(qc)::value;
+      const int b0 = c * BC;                           // first block of the chunk
+#pragma unroll
+      for (int j = 0; j < RPT; ++j) {
+        const int i = ts + NST * j, kb = b0 + i % BC;
+        const uint32_t off = res_row[j] != kOut && kb < KB ? res_row[j] * (uint32_t)(K >> 1) + 16u * kb : kOut;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r_rc, off, 0, 0);
+        rv[q][j] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) {
+        const int i = ts + NST * j, kp = (b0 >> 1) + i % (BC / 2);
+        const bool ok = bb_row[j] != kOut && 2 * kp < KB;
+        const auto v =
+            __builtin_amdgcn_raw_buffer_load_b128(r_bc, ok ? bb_row[j] * (uint32_t)(K >> 2) + 16u * kp : kOut, 0, 0);
+        bv[q][j] = make_uint4(v[0], v[1], v[2], v[3]);
+        mv[q][j] = __builtin_amdgcn_raw_buffer_load_b32(r_bm, ok ? bb_row[j] * (uint32_t)(K >> 4) + 4u * kp : kOut, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < SPT; ++j) {
+        const int i = ts + NST * j, r = i / (BC / 16), p = i % (BC / 16), kb = b0 + 16 * p;
+        // bytes past the row's K / 32 are the next row's scales (or zero
+        // past the buffer): finite, and met only by zero weights
+        const uint32_t off = sc_row[j] != kOut && kb < KB ? sc_row[j] * (uint32_t)(K >> 5) + kb : kOut;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128((r & 8) == 0 ? r_bs : r_rs, off, 0, 0);
+        sv[q][j] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+    };
+    // register set q into LDS stage q (chunk k uses set and stage k & 1)
+    auto store_chunk = [&](auto qc) {
+      constexpr int q = decltype(qc)::value;
+      uint4* const a = a_st + q * NR * BCP;
+      uint8_t* const sc = s_st + q * NR * SP;
+#pragma unroll
+      for (int j = 0; j < RPT; ++j) {
+        const int i = ts + NST * j, t = i / BC, kb = i % BC;
+        if (i < NRES) a[(16 * (t >> 3) + 8 + (t & 7)) * BCP + kb] = rv[q][j];
+      }
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) {
+        const int i = ts + NST * j, t = i / (BC / 2), kp = i % (BC / 2), tr = 16 * (t >> 3) + (t & 7);
+        if (i < NBB) {
+          a[tr * BCP + 2 * kp] = expand4_fast(bv[q][j].x, bv[q][j].y, mv[q][j] & 0xFFFFu);
+          a[tr * BCP + 2 * kp + 1] = expand4_fast(bv[q][j].z, bv[q][j].w, mv[q][j] >> 16);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < SPT; ++j) {
+        const int i = ts + NST * j, r = i / (BC / 16), p = i % (BC / 16);
+        if (i < NSC) {
+          // 4-byte stores: SP is a multiple of 4, not of 16
+          uint32_t* dst = reinterpret_cast<uint32_t*>(sc + r * SP + 16 * p);
+          dst[0] = sv[q][j].x; dst[1] = sv[q][j].y; dst[2] = sv[q][j].z; dst[3] = sv[q][j].w;
+        }
+      }
+    };
+    const std::integral_constant<int, 0> q0{};
+    const std::integral_constant<int, 1> q1{};
+    load_chunk(0, q0);
+    if (NC > 1) load_chunk(1, q1);
+    store_chunk(q0);
+    SHARQ_TL_BY(NCW * 64, blockIdx.x, 1, SHARQ_TL_NOW());
+    if (NC > 2) load_chunk(2, q0);
+    for (int c0 = 0; c0 < NC; c0 += 2) {
+      // chunk c = c0 + u: every compute wave is past chunk c - 1, which read
+      // the stage chunk c + 1 goes to; chunk c + 1 is in set (c + 1) & 1
+      __syncthreads();
+      if (c0 + 1 < NC) {
+        store_chunk(q1);
+        if (c0 == 0) SHARQ_TL_BY(NCW * 64, blockIdx.x, 7, SHARQ_TL_NOW());
+        if (c0 + 3 < NC) load_chunk(c0 + 3, q1);
+      }
+      if (c0 + 1 >= NC) break;
+      __syncthreads();
+      if (c0 + 2 < NC) {
+        store_chunk(q0);
+        if (c0 + 4 < NC) load_chunk(c0 + 4, q0);
       }
     }
-    if (c == 0) SHARQ_TL(blockIdx.x, 6, SHARQ_TL_NOW());
-    if (c + 2 < NC) load_w(c + 2, b);
-    if (c + 1 < NC) store_chunk((c + 1) & 1);
-    if (c == 0) SHARQ_TL(blockIdx.x, 7, SHARQ_TL_NOW());
+  } else {
+    // ---- compute waves: weights of this wave's steps, WD chunks ahead
+    const __amdgpu_buffer_rsrc_t r_w = rsrc(payload, (int64_t)D * (K >> 1));
+    const __amdgpu_buffer_rsrc_t r_ws = rsrc(wscale, (int64_t)D * (K >> 5));
+    const uint32_t o_w = col < D ? (uint32_t)col * (uint32_t)(K >> 1) + 16u * kq : kOut;
+    const uint32_t o_ws = col < D ? (uint32_t)col * (uint32_t)(K >> 5) : kOut;
+    uint4 wv[WD][JC];
+    uint32_t wsd[WD][JC];                              // dword: the 4 block scales of the step (byte kq)
+    auto load_w = [&](int c, auto bc) {                // slot b: a compile-time constant
+      constexpr int b = decltype(bc)::value;
+#pragma unroll
+      for (int j = 0; j < JC; ++j) {
+        const int s = c * KC + kw * JC + j;
+        const uint32_t out = s < KS ? 0u : kOut;
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(r_w, (o_w + 64u * (uint32_t)s) | out, 0, 0);
+        wv[b][j] = make_uint4(v[0], v[1], v[2], v[3]);
+        wsd[b][j] = __builtin_amdgcn_raw_buffer_load_b32(r_ws, (o_ws + 4u * (uint32_t)s) | out, 0, 0);
+      }
+    };
+    // chunk c = c0 + b uses weight slot b and stage c & 1 (WD even), both
+    // compile-time constants in the unrolled body
+    auto chunk = [&](int c, auto bc) {
+      constexpr int b = decltype(bc)::value;
+      // stage c & 1 is written
+      __syncthreads();
+      const uint4* const a = a_st + (b & 1) * NR * BCP;
+      const uint8_t* const sc = s_st + (b & 1) * NR * SP;
+#pragma unroll
+      for (int j = 0; j < JC; ++j) {
+        const int sl = kw * JC + j;                    // step within the chunk
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const int r = 16 * m + (l & 15);
+          acc[m] = mfma_fp4(a[r * BCP + 4 * sl + kq], wv[b][j], acc[m], sc[r * SP + 4 * sl + kq],
+                            (wsd[b][j] >> (8 * kq)) & 0xFFu);
+        }
+        // one step's operand reads at a time: hoisting a whole chunk's reads
+        // ahead of its MFMAs would not fit the registers
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (c == 0) SHARQ_TL(blockIdx.x, 6, SHARQ_TL_NOW());
+      // unconditional (steps past K read zero): a branch here lets the
+      // compiler sink the chunk's MFMAs below the new loads, which then
+      // need a second copy of the slot's registers and spill
+      load_w(c + WD, bc);
+    };
+    const std::integral_constant<int, 0> b0{};
+    const std::integral_constant<int, 1> b1{};
+    load_w(0, b0);
+    if (NC > 1) load_w(1, b1);
+    for (int c0 = 0; c0 < NC; c0 += WD) {
+      chunk(c0, b0);
+      if (c0 + 1 >= NC) break;
+      chunk(c0 + 1, b1);
+    }
   }
   SHARQ_TL(blockIdx.x, 2, SHARQ_TL_NOW());
-  __syncthreads();                                     // every wave is past its last reads of the stages
+  __syncthreads();                                     // every wave is past its last use of the stages
 
   // ---- fixed-order reduction over the K-splits; backbone row + residual row
+  if (w < NCW) {
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    float* p = red + ((w * MT + m) * 64 + l) * 4;
-    p[0] = acc[m][0]; p[1] = acc[m][1]; p[2] = acc[m][2]; p[3] = acc[m][3];
+    for (int m = 0; m < MT; ++m) {
+      float* p = red + ((w * MT + m) * 64 + l) * 4;
+      p[0] = acc[m][0]; p[1] = acc[m][1]; p[2] = acc[m][2]; p[3] = acc[m][3];
+    }
   }
   __syncthreads();
-  if (kw == 0 && l < 32) {
+  if (w < NCW && kw == 0 && l < 32) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
 #pragma unroll
@@ -1535,26 +1590,26 @@ hipError_t launch_batch(const uint8_t* bb_codes, const uint8_t* bb_meta, const u
                         const uint8_t* res_codes, const uint8_t* res_scale, const int32_t* row_index, int rows,
                         int act_rows, int K, const uint8_t* payload, const uint8_t* wscale, int D, float* Y, int64_t ldy,
                         hipStream_t s) {
+  // column groups as in the decode kernel; four compute waves (NK = 4 / CG
+  // K-splits) and four staging waves.  Steps per compute wave and chunk JC
+  // from a sweep over the Llama-3.1-8B decode shapes at 17-64 rows (JC = 8,
+  // and weights four chunks ahead instead of two, measured slower): 4, or 2
+  // for MT = 8 below four column groups
   int CG = 1;
   while (CG < 4 && (D + 32 * CG - 1) / (32 * CG) >= 200) CG *= 2;
-  // eight waves (sixteen would leave 128 VGPRs per wave, too few for the
-  // staged pieces, two chunks of weights and MT accumulators); steps per
-  // chunk and wave JC: at most 2 (MT = 8) or 4 (MT = 4), which bounds the
-  // weight registers, so wide column groups take short chunks
-  const int NK = 8 / CG, NW = CG * NK;
-  const int JC = (MT == 8 ? 2 : 4) / (CG == 1 ? 2 : 1);
+  const int NK = 4 / CG, JC = (MT == 8 && CG < 4) ? 2 : 4;
   const int KC = NK * JC, BC = 4 * KC, SP = BC + 4, NR = 16 * MT;
-  const size_t stage = (size_t)2 * NR * (BC + 1) * 16 + (size_t)2 * NR * SP, red = (size_t)NW * MT * 64 * 4 * sizeof(float);
+  const size_t stage = (size_t)2 * NR * (BC + 1) * 16 + (size_t)2 * NR * SP, red = (size_t)4 * MT * 64 * 4 * sizeof(float);
   const size_t lds = std::max(stage, red);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  dim3 grid((D + 16 * CG - 1) / (16 * CG)), block(64 * NW);
+  dim3 grid((D + 16 * CG - 1) / (16 * CG)), block(64 * (4 + kBatchStagingWaves));
 #define L(CG_, NK_, JC_)                                                                                                 \
   hipLaunchKernelGGL((linear_mx_batch<MT, CG_, NK_, JC_>), grid, block, lds, s, bb_codes, bb_meta, bb_scale, res_codes, \
                      res_scale, row_index, rows, act_rows, K, payload, wscale, D, Y, ldy)
   switch (CG) {
-    case 4: L(4, 2, MT == 8 ? 2 : 4); break;
-    case 2: L(2, 4, MT == 8 ? 2 : 4); break;
-    default: L(1, 8, MT == 8 ? 1 : 2); break;
+    case 4: L(4, 1, 4); break;
+    case 2: L(2, 2, MT == 8 ? 2 : 4); break;
+    default: L(1, 4, MT == 8 ? 2 : 4); break;
   }
 #undef L
   return hipGetLastError();
@@ -1592,14 +1647,11 @@ hipError_t launch_linear_mx_impl(const uint8_t* bb_codes, const uint8_t* bb_meta
     return launch_decode<false, M24>(bb_codes, bb_meta, bb_scale, res_codes, res_scale, row_index, rows, act_rows, K, payload,
                                 wscale, D, Y, ldy, FusedPrep{}, s);
   // 17-64 rows: the batch kernel, the weight read once for all rows (the
-  // chunks of decode launches below read it once per chunk), except 17-32
-  // rows over wide outputs (four column groups), where two 16-row decode
-  // launches measured faster.  Llama-3.1-8B decode shapes 4096 x 4096 /
-  // 4096 x 14336 / 14336 x 4096: batch kernel 11.8 / 26.0 / 27.0 us at 32
-  // rows and 16.8 / 28.2 / 37.9 us at 64; decode launches 12.4 / 20.1 / 34.1
-  // and 24.1 / 39.0 / 67.2 us
-  const bool wide = (D + 63) / 64 >= 200;               // the batch kernel's four column groups
-  if (n_groups == 1 && rows > 16 && rows <= 64 && !M24 && !(rows <= 32 && wide && K <= kDecodeMaxK16)) {
+  // chunks of decode launches below read it once per chunk).  Llama-3.1-8B
+  // decode shapes 4096 x 4096 / 4096 x 14336 / 14336 x 4096: batch kernel
+  // 9.2 / 16.2 / 19.9 us at 32 rows and 13.2 / 21.4 / 30.5 us at 64; decode
+  // launches 12.4 / 20.1 / 34.1 and 24.1 / 39.0 / 67.2 us
+  if (n_groups == 1 && rows > 16 && rows <= 64 && !M24) {
     return rows <= 32 ? launch_batch<4>(bb_codes, bb_meta, bb_scale, res_codes, res_scale, row_index, rows, act_rows, K,
                                         payload, wscale, D, Y, ldy, s)
                       : launch_batch<8>(bb_codes, bb_meta, bb_scale, res_codes, res_scale, row_index, rows, act_rows, K,

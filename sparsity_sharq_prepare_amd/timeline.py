@@ -66,18 +66,19 @@ def summarize(rec: np.ndarray) -> dict:
 
 
 def summarize_batch(rec: np.ndarray) -> dict:
-    """Phases of the batch kernel (17-64 rows), one record per workgroup:
-    words 0 start, 1 first chunk staged, 6 first chunk multiplied, 7 second
-    chunk staged, 2 last chunk multiplied, 3 stored."""
+    """Events of the batch kernel (17-64 rows), one record per workgroup,
+    each as time after the workgroup's start (word 0): staging waves' words
+    1 (first chunk staged) and 7 (second chunk staged), compute waves'
+    words 6 (first chunk multiplied) and 2 (last chunk multiplied), and word
+    3 (results stored).  The two kinds of wave run concurrently, so events
+    are reported from the start rather than as consecutive phases."""
     rec = rec[rec[:, 0] > 0].astype(np.int64)
     if len(rec) == 0:
         raise ValueError("no records: the launch did not run the batch kernel")
     us = 1e6 / CLOCK_HZ
-    ph = {"first chunk loaded and staged": rec[:, 1] - rec[:, 0],
-          "first chunk multiplied": rec[:, 6] - rec[:, 1],
-          "second chunk staged": rec[:, 7] - rec[:, 6],
-          "remaining chunks": rec[:, 2] - rec[:, 7],
-          "reduction and stores": rec[:, 3] - rec[:, 2]}
+    ev = {"first chunk staged": 1, "second chunk staged": 7, "first chunk multiplied": 6,
+          "last chunk multiplied": 2, "stored": 3}
+    ph = {k: rec[:, i] - rec[:, 0] for k, i in ev.items()}
     t0 = rec[:, 0].min()
     return {"records": int(len(rec)), "workgroups": int(len(rec)), "span_us": float((rec[:, 3].max() - t0) * us),
             "phases_us": {k: {"mean": float(v.mean() * us), "p10": float(np.percentile(v, 10) * us),
