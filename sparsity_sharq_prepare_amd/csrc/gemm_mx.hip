@@ -19,14 +19,15 @@
 //    paths; the epilogue adds row r and row r + 8 of the tile.  K is split
 //    over the waves of a workgroup and the partial tiles are summed in a
 //    fixed order through LDS.
-//  - decode (T <= 16, K <= 16384): the skinny scheme with the activation
-//    side staged once per workgroup in LDS in operand form, one or two
-//    16-row MFMA tiles (8 or 16 tokens) per launch (some 17-64-row cases in
-//    chunks of launches); optionally fused with the preparation of the rows
-//    (single-launch decode).
-//  - batch (4:8 backbone, 17-64 rows): the decode scheme with the activation
-//    operand staged in double-buffered chunks of K, so the weight is read
-//    once for all rows at any K.
+//  - decode (T <= 8 at K <= 16384, 9-16 rows at K <= 7168): the skinny
+//    scheme with the activation side staged once per workgroup in LDS in
+//    operand form, one or two 16-row MFMA tiles (8 or 16 tokens) per launch
+//    (2:4 backbones at 9-64 rows in chunks of launches); optionally fused
+//    with the preparation of the rows (single-launch decode).
+//  - batch (4:8 backbone, 17-64 rows, and 9-16 rows at K > 7168): the
+//    decode scheme with the activation operand staged in double-buffered
+//    chunks of K by staging waves beside the waves that load weights and
+//    multiply, so the weight is read once for all rows at any K.
 //  - tile8 (prefill and grouped MoE, more than 64 rows): 256 rows x 256 (or
 //    224) columns, eight waves, K steps of 128 staged by buffer->LDS DMA
 //    through a 3-deep ring (scales and metadata in a side ring of four-step
@@ -1651,6 +1652,9 @@ hipError_t launch_linear_mx_impl(const uint8_t* bb_codes, const uint8_t* bb_meta
   // decode shapes 4096 x 4096 / 4096 x 14336 / 14336 x 4096: batch kernel
   // 9.2 / 16.2 / 19.9 us at 32 rows and 13.2 / 21.4 / 30.5 us at 64; decode
   // launches 12.4 / 20.1 / 34.1 and 24.1 / 39.0 / 67.2 us
+  if (n_groups == 1 && rows > 8 && rows <= 16 && K > kDecodeMaxK16 && !M24)
+    return launch_batch<2>(bb_codes, bb_meta, bb_scale, res_codes, res_scale, row_index, rows, act_rows, K, payload,
+                           wscale, D, Y, ldy, s);
   if (n_groups == 1 && rows > 16 && rows <= 64 && !M24) {
     return rows <= 32 ? launch_batch<4>(bb_codes, bb_meta, bb_scale, res_codes, res_scale, row_index, rows, act_rows, K,
                                         payload, wscale, D, Y, ldy, s)

@@ -166,13 +166,14 @@ LINEAR_SHAPES = [  # decode (T <= 64, in chunks), skinny and tile paths, ragged 
     # a K beyond it (general skinny path)
     (5, 1152, 72), (7, 16384, 48), (2, 18944, 40),
     # decode path with two MFMA tiles (9-16 rows): ragged rows, column
-    # groups, the largest staged K (7168); beyond it the one-tile kernel
-    # twice (rows 0-7 and the rest) up to K = 16384, then the skinny path
+    # groups, the largest staged K (7168); beyond it the batch kernel with
+    # two MFMA tiles (column groups of 1, 2 and 4, K past the decode
+    # kernel's)
     (16, 4096, 300), (9, 1152, 72), (12, 2048, 4100), (11, 7168, 64), (16, 7296, 40),
-    (9, 14336, 72), (10, 16512, 40),
+    (9, 14336, 72), (10, 16512, 40), (13, 8192, 6500), (16, 14336, 13000),
     # 17-64 rows: the batch kernel (32 or 64 MFMA rows; column groups of 1,
-    # 2 and 4; partial last K chunks; K beyond the decode kernel's), and
-    # 17-32 rows over wide outputs at K <= 7168 on 16-row decode launches
+    # 2 and 4; partial last K chunks; K beyond the decode kernel's; wide
+    # outputs)
     (17, 512, 64), (32, 4096, 300), (40, 2048, 4100), (57, 1152, 200), (64, 7168, 48), (64, 7296, 40),
     (33, 14336, 72), (40, 16512, 48), (64, 16512, 40), (24, 640, 13000), (64, 384, 8200), (48, 18944, 130),
     (40, 1024, 13000), (20, 7296, 12800),
