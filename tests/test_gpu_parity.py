@@ -156,7 +156,7 @@ def test_linear_tiny_config():
     assert_gemm_close(Y.cpu().numpy(), Yr, S)
 
 
-LINEAR_SHAPES = [  # decode (T <= 64, in chunks), skinny and tile paths, ragged rows and columns
+LINEAR_SHAPES = [  # decode (T <= 16), batch (9-64 rows), skinny and tile paths, ragged rows and columns
     (1, 512, 200), (8, 512, 200), (13, 256, 64), (64, 384, 130), (65, 512, 300), (300, 512, 520),
     (256, 1024, 256), (700, 128, 40),
     # K % 512 != 0 on the tile path: 3, 5 and 6 steps of 128 (a partial last
@@ -196,9 +196,9 @@ def test_linear_shapes(T, K, D):
                                    (20, 8192, 27)])
 def test_linear_row_gather(T, K, n):
     # n gathered output rows: the two-tile decode kernel (13), the tile path
-    # (205), the one-tile decode kernel (5), two one-tile launches (14 rows
-    # at K = 8192, the second reading row_index from entry 8), 16-row chunks
-    # (50 rows, the last chunk 2) and 8-row chunks (27 rows at K = 8192)
+    # (205), the one-tile decode kernel (5), and the batch kernel with two
+    # (14 rows at K = 8192), eight (50 rows) and four (27 rows at K = 8192)
+    # MFMA tiles
     case = synth.random_case(99 + T, T, K, 96)
     act = ops.prepare(dev_x(case), dev_gamma(case.gamma), 1e-6)
     w = ops.pack_weight(dev_w(case.w, "bf16"))
@@ -223,8 +223,8 @@ def test_linear_decode_full_sampled(i):
 @pytest.mark.parametrize("T", [16, 40, 64])
 def test_linear_decode_batch_full_sampled(T, i):
     # batched decode at the full Llama-3.1-8B shapes: 16 rows on the two-tile
-    # kernel (or two one-tile launches at K = 14336), 40 and 64 rows in
-    # chunks of launches
+    # decode kernel (the two-tile batch kernel at K = 14336), 40 and 64 rows
+    # on the batch kernel (one and four column groups)
     case = synth.decode_case(i, T=T)
     act, w, Y = run_case(case)
     ref = oracle_prepare(case)
