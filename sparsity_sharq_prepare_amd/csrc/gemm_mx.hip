@@ -703,9 +703,9 @@ constexpr int kHwRegHwId = (31 << 11) | 4, kHwRegXccId = (31 << 11) | 20;
 #define SHARQ_TL_NOW() __builtin_amdgcn_s_memrealtime()
 
 // ============================================================================
-// batch kernel (17-64 rows, 4:8 backbone): the decode scheme with the
-// activation operand staged in chunks of K, so the weight is read once for
-// all rows at any K
+// batch kernel (4:8 backbone; 17-64 rows, and 9-16 rows at K > 7168): the
+// decode scheme with the activation operand staged in chunks of K, so the
+// weight is read once for all rows at any K
 // ============================================================================
 // grid.x = ceil(D / (16 CG)); CG NK = 4 compute waves and 4 staging waves.  K is
 // processed in chunks of KC = NK JC steps of 128, through two LDS stages
@@ -1583,9 +1583,9 @@ hipError_t launch_decode(const uint8_t* bb_codes, const uint8_t* bb_meta, const 
 }
 }  // namespace
 
-// 17-64 rows (4:8 backbone): the batch kernel, MT = 4 (32 rows) or 8 (64
-// rows) MFMA tiles; column groups as in the decode kernel (the widest with at
-// least 200 workgroups), K chunks split over the waves of a column group
+// the batch kernel (4:8 backbone) with MT = 2 (16 rows), 4 (32) or 8 (64)
+// MFMA tiles; column groups as in the decode kernel (the widest with at least
+// 200 workgroups), K chunks split over the compute waves of a column group
 template <int MT>
 hipError_t launch_batch(const uint8_t* bb_codes, const uint8_t* bb_meta, const uint8_t* bb_scale,
                         const uint8_t* res_codes, const uint8_t* res_scale, const int32_t* row_index, int rows,

@@ -63,11 +63,22 @@ MATCH = {
 }
 
 
+_COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
+def code_text(src: str) -> str:
+    """A source file's code without comments and whitespace: what the
+    compiler sees, so an edit to comments alone leaves it unchanged."""
+    return re.sub(r"\s+", "", _COMMENT.sub(" ", src))
+
+
 def source_hash(files) -> str:
+    """Hash of the code (comments and whitespace dropped) of a kernel's
+    source files; a summary whose hash differs was taken on other code."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "sparsity_sharq_prepare_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "sparsity_sharq_prepare_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -30,3 +30,15 @@ def test_other_kernels():
     assert selects("linear_nv_tile", "sharq::linear_nv_tile" + SIG)
     assert selects("prepare_mx_kernel", "void sharq::prepare_mx_kernel<64, 8, true, true, false>" + SIG)
     assert not selects("prepare_mx_kernel", "void sharq::prepare_nv_phase1<256, 16, true>" + SIG)
+
+
+def test_source_hash_ignores_comments_and_whitespace():
+    from sparsity_sharq_prepare_amd.profiling import code_text
+    a = "int f(int x) {  // doubles x\n  return 2 * x; /* no overflow\n check */ }\n"
+    b = "int f(int x) {\n\treturn 2*x;\n}"
+    c = "int f(int x) { return 3 * x; }"
+    assert code_text(a) == code_text(b)
+    assert code_text(a) != code_text(c)
+    # a '//' inside a string literal would also start a comment here; the
+    # kernel sources have no such literal
+    assert code_text("a = 1; // x\nb = 2;") == "a=1;b=2;"
