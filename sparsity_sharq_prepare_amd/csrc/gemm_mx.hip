@@ -1261,6 +1261,65 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 1 : 2) void linear_mx_tile8(
     read_half(cur, hf, j1);
     mfma_half(sf, hf, j1);
   };
+  // 256-row tiles, 4:8 at 224 columns and plain: a side group's scale and
+  // metadata bytes are read once per group of four steps, each 16-byte
+  // record (a column's or row's four steps) with one conflict-free 16-byte
+  // read, instead of a 2- or 4-byte read per step (2- and 4-way bank
+  // conflicts).  Of a record's dword p (step p) the lane needs bytes 2 kh
+  // and 2 kh + 1; steps 2 q and 2 q + 1 are packed into one dword (low and
+  // high half), so a step's two scale bytes sit in bytes 0 and 1 after a
+  // shift, where the MFMA's op_sel picks them as before.  4:8 metadata: the
+  // lane's dword of each step, from the row's two 16-byte halves.  2:4
+  // tiles and 256-wide 4:8 tiles keep the per-step reads (the held bytes
+  // would not fit their registers).
+  constexpr bool kGroupSide = !M24 && (DENSE || FN <= 7);
+  struct GroupFrag {
+    uint32_t bs[FN][2], ssp[FM][2], sdn[FM][2], mt[FM][4];
+  };
+  auto read_group = [&](const SideT& sd, GroupFrag& Gf) {
+    const uint32_t sel = kh ? 0x07060302u : 0x05040100u;   // bytes 2 kh, 2 kh + 1 of two dwords
+#pragma unroll
+    for (int n = 0; n < FN; ++n) {
+      const uint4 v = sd.s_b[wn0 + 32 * n + lr];
+      Gf.bs[n][0] = __builtin_amdgcn_perm(v.y, v.x, sel);
+      Gf.bs[n][1] = __builtin_amdgcn_perm(v.w, v.z, sel);
+    }
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+      const int r = wm0 + 32 * f + lr;
+      if constexpr (!DENSE && !M24) {
+        const uint4 v = sd.s_sp[r];
+        Gf.ssp[f][0] = __builtin_amdgcn_perm(v.y, v.x, sel);
+        Gf.ssp[f][1] = __builtin_amdgcn_perm(v.w, v.z, sel);
+        const uint4 m0 = sd.meta[2 * r], m1 = sd.meta[2 * r + 1];
+        Gf.mt[f][0] = kh ? m0.y : m0.x;
+        Gf.mt[f][1] = kh ? m0.w : m0.z;
+        Gf.mt[f][2] = kh ? m1.y : m1.x;
+        Gf.mt[f][3] = kh ? m1.w : m1.z;
+      }
+      const uint4 v = sd.s_dn[r];
+      Gf.sdn[f][0] = __builtin_amdgcn_perm(v.y, v.x, sel);
+      Gf.sdn[f][1] = __builtin_amdgcn_perm(v.w, v.z, sel);
+    }
+  };
+  auto compute_step_g = [&](const MainT& cur, const GroupFrag& Gf, int p) {
+    const int q = p >> 1, sh = 16 * (p & 1);
+#pragma unroll
+    for (int n = 0; n < FN; ++n) sf.bs[n] = Gf.bs[n][q] >> sh;
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+      if constexpr (!DENSE) {
+        sf.sp[f] = cur.a_sp[slot_sp(wm0 + 32 * f + lr, kh)];
+        sf.mt[f] = Gf.mt[f][p];
+        sf.ssp[f] = Gf.ssp[f][q] >> sh;
+      }
+      sf.sdn[f] = Gf.sdn[f][q] >> sh;
+    }
+    read_half(cur, hf, j0);
+    mfma_half(sf, hf, j0);
+    read_half(cur, hf, j1);
+    mfma_half(sf, hf, j1);
+  };
 
   // ---- epilogue: fp32 store of the accumulator tile
   auto epilogue = [&](const TileOff& o) {
@@ -1317,6 +1376,7 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 1 : 2) void linear_mx_tile8(
     issue_main(min(1, KS - 1), lds[1], o);
     for (int g = 0; g < G; ++g) {
       const SideT& sd = side[g & 1];
+      [[maybe_unused]] GroupFrag gf;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const int s = 4 * g + p;
@@ -1333,7 +1393,12 @@ __global__ __launch_bounds__(2 * BM, BM == 256 ? 1 : 2) void linear_mx_tile8(
         issue_main(min(s + 2, KS - 1), lds[(s + 2) % NS], o);
         // side group g+1 replaces group g-1, last read at step 4 g - 1
         if (p == 2) issue_side(min(g + 1, G - 1), side[(g + 1) & 1], o);
-        if (live) compute_step(lds[s % NS], sd, p);
+        if constexpr (!kGroupSide) {
+          if (live) compute_step(lds[s % NS], sd, p);
+        } else if (live) {
+          if (p == 0) read_group(sd, gf);
+          compute_step_g(lds[s % NS], gf, p);
+        }
       }
     }
     SHARQ_TL(blockIdx.x, 2, SHARQ_TL_NOW());
