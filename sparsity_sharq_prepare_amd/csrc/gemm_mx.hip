@@ -711,8 +711,8 @@ constexpr int kHwRegHwId = (31 << 11) | 4, kHwRegXccId = (31 << 11) | 20;
 // processed in chunks of KC = NK JC steps of 128, through two LDS stages
 // holding the chunk's activation operand (backbone expanded) and scales.
 //  - Staging waves load a chunk's pieces (coalesced 16-byte pieces of the
-//    token rows, as in the decode kernel) two chunks ahead into registers and
-//    write them to a stage in operand form.
+//    token rows, as in the decode kernel) three chunks ahead into registers
+//    and write them to a stage in operand form.
 //  - Compute wave (cg, kw) multiplies steps kw JC .. kw JC + JC - 1 of every
 //    chunk for the 16 columns of column group cg, with its weights loaded
 //    two chunks ahead.
@@ -796,11 +796,11 @@ __global__ __launch_bounds__((CG * NK + kBatchStagingWaves) * 64) void linear_mx
       const int i = ts + NST * j, r = i / (BC / 16);
       sc_row[j] = i < NSC ? act_row(8 * (r >> 4) + (r & 7)) : kOut;
     }
-    uint4 rv[2][RPT], bv[2][BPT], sv[2][SPT];
-    uint32_t mv[2][BPT];
-    // chunk c's pieces into register set q (blocks past K read zero); the
-    // set index is a compile-time constant (the loop below is unrolled by
-    // two), so the sets stay in registers
+    uint4 rv[3][RPT], bv[3][BPT], sv[3][SPT];
+    uint32_t mv[3][BPT];
+    // chunk c's pieces into register set q = c % 3 (blocks past K read
+    // zero); the set index is a compile-time constant (the loop below is
+    // unrolled by three), so the sets stay in registers
     auto load_chunk = [&](int c, auto qc) {
       constexpr int q = decltype(qc)::value;
       const int b0 = c * BC;                           // first block of the chunk
@@ -830,11 +830,11 @@ __global__ __launch_bounds__((CG * NK + kBatchStagingWaves) * 64) void linear_mx
         sv[q][j] = make_uint4(v[0], v[1], v[2], v[3]);
       }
     };
-    // register set q into LDS stage q (chunk k uses set and stage k & 1)
-    auto store_chunk = [&](auto qc) {
+    // register set q into LDS stage st (chunk c: set c % 3, stage c & 1)
+    auto store_chunk = [&](auto qc, int st) {
       constexpr int q = decltype(qc)::value;
-      uint4* const a = a_st + q * NR * BCP;
-      uint8_t* const sc = s_st + q * NR * SP;
+      uint4* const a = a_st + st * NR * BCP;
+      uint8_t* const sc = s_st + st * NR * SP;
 #pragma unroll
       for (int j = 0; j < RPT; ++j) {
         const int i = ts + NST * j, t = i / BC, kb = i % BC;
@@ -860,26 +860,31 @@ __global__ __launch_bounds__((CG * NK + kBatchStagingWaves) * 64) void linear_mx
     };
     const std::integral_constant<int, 0> q0{};
     const std::integral_constant<int, 1> q1{};
+    const std::integral_constant<int, 2> q2{};
     load_chunk(0, q0);
     if (NC > 1) load_chunk(1, q1);
-    store_chunk(q0);
+    if (NC > 2) load_chunk(2, q2);
+    store_chunk(q0, 0);
     SHARQ_TL_BY(NCW * 64, blockIdx.x, 1, SHARQ_TL_NOW());
-    if (NC > 2) load_chunk(2, q0);
-    for (int c0 = 0; c0 < NC; c0 += 2) {
-      // chunk c = c0 + u: every compute wave is past chunk c - 1, which read
-      // the stage chunk c + 1 goes to; chunk c + 1 is in set (c + 1) & 1
+    if (NC > 3) load_chunk(3, q0);                     // set 0 is free again
+    // the barrier of chunk c: every compute wave is past chunk c - 1, which
+    // read the stage chunk c + 1 goes to; chunk c + 1 is in set qn =
+    // (c + 1) % 3, which then takes chunk c + 4 (three chunks of loads in
+    // flight)
+    auto step = [&](int c, auto qn) {
       __syncthreads();
-      if (c0 + 1 < NC) {
-        store_chunk(q1);
-        if (c0 == 0) SHARQ_TL_BY(NCW * 64, blockIdx.x, 7, SHARQ_TL_NOW());
-        if (c0 + 3 < NC) load_chunk(c0 + 3, q1);
+      if (c + 1 < NC) {
+        store_chunk(qn, (c + 1) & 1);
+        if (c == 0) SHARQ_TL_BY(NCW * 64, blockIdx.x, 7, SHARQ_TL_NOW());
+        if (c + 4 < NC) load_chunk(c + 4, qn);
       }
+    };
+    for (int c0 = 0; c0 < NC; c0 += 3) {
+      step(c0, q1);
       if (c0 + 1 >= NC) break;
-      __syncthreads();
-      if (c0 + 2 < NC) {
-        store_chunk(q0);
-        if (c0 + 4 < NC) load_chunk(c0 + 4, q0);
-      }
+      step(c0 + 1, q2);
+      if (c0 + 2 >= NC) break;
+      step(c0 + 2, q0);
     }
   } else {
     // ---- compute waves: weights of this wave's steps, WD chunks ahead
