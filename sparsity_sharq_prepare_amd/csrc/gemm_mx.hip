@@ -400,20 +400,37 @@ __global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
   const uint32_t o_ws = col < D ? (uint32_t)col * (uint32_t)(K >> 5) : kOut;
   uint4 wv[J];
   uint32_t wsd[J];                                    // dword j: scales of step s0 + j (byte kq)
+  // steps [lo, hi) of this wave (lo, hi multiples of 4: one scale load per
+  // four steps)
+  auto load_weights = [&](auto lo_c, auto hi_c) {
+    constexpr int lo = decltype(lo_c)::value, hi = decltype(hi_c)::value;
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const uint32_t out = s0 + j < KS ? 0u : kOut;
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r_w, (o_w + 64u * (uint32_t)(s0 + j)) | out, 0, 0);
-    wv[j] = make_uint4(v[0], v[1], v[2], v[3]);
-  }
+    for (int j = lo; j < hi; ++j) {
+      const uint32_t out = s0 + j < KS ? 0u : kOut;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(r_w, (o_w + 64u * (uint32_t)(s0 + j)) | out, 0, 0);
+      wv[j] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
 #pragma unroll
-  for (int j = 0; j < J; j += 4) {
-    // 16 bytes = blocks 4 (s0 + j) .. 4 (s0 + j + 4) - 1; past the row's end
-    // only scales of zero-weight steps are affected
-    const uint32_t out = s0 + j < KS ? 0u : kOut;
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r_ws, (o_ws + 4u * (uint32_t)(s0 + j)) | out, 0, 0);
-    wsd[j] = v[0]; wsd[j + 1] = v[1]; wsd[j + 2] = v[2]; wsd[j + 3] = v[3];
-  }
+    for (int j = lo; j < hi; j += 4) {
+      // 16 bytes = blocks 4 (s0 + j) .. 4 (s0 + j + 4) - 1; past the row's
+      // end only scales of zero-weight steps are affected
+      const uint32_t out = s0 + j < KS ? 0u : kOut;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(r_ws, (o_ws + 4u * (uint32_t)(s0 + j)) | out, 0, 0);
+      wsd[j] = v[0]; wsd[j + 1] = v[1]; wsd[j + 2] = v[2]; wsd[j + 3] = v[3];
+    }
+  };
+  // fused: a wave's loads complete in order, so anything behind its weight
+  // loads also waits for them.  Producers load their weights only after
+  // their signal (its wait then covers their row stores alone) and wave 0,
+  // whose lane 0 polls the counter, after the poll and its activation
+  // loads; the other waves stream their weights from the start.  (Also
+  // holding back the second half of the other waves' weights until after
+  // their activation loads measured no better.)
+  const std::integral_constant<int, 0> c0{};
+  const std::integral_constant<int, J> cj{};
+  bool early_w = true;
+  if constexpr (FUSED) early_w = !producer && w != 0;   // uniform
+  if (early_w) load_weights(c0, cj);
   __builtin_amdgcn_sched_barrier(0);
 
   if constexpr (FUSED) {
@@ -461,6 +478,7 @@ __global__ __launch_bounds__(NK * CG * 64) void linear_mx_decode(
       return;
     }
     load_act();
+    if (!early_w) load_weights(c0, cj);
     __builtin_amdgcn_sched_barrier(0);
   }
 
