@@ -16,6 +16,7 @@
 // forms Y = s_w * (s_sp * acc_sp + s_dn * acc_dn).
 #include "common.h"
 #include "kernels.h"
+#include <type_traits>
 
 namespace sharq {
 
@@ -26,7 +27,7 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kNM = 128;                  // tile rows
-constexpr int kNN = 256;                  // tile columns
+constexpr int kNN = 256;                  // staged weight columns (the tile computes 256 or 224)
 constexpr int kKS = 64;                   // K per step: two halves of 32 (one backbone block, two residual blocks each)
 
 // 32x32x16 f16: lane l holds row / column (l & 31), K-values 8 (l >> 5) .. +7
@@ -79,17 +80,21 @@ SHARQ_DEV uint4 expand4(uint32_t c_lo, uint32_t c_hi, uint32_t meta16) {
 
 }  // namespace
 
-// Tile 128 x 256, eight waves (two per SIMD): wave w covers rows 32 (w & 3)
-// .. and columns 128 (w >> 2) .., with one accumulator per path (the two
-// paths have different tensor scales), 128 accumulator registers.  K
-// advances 64 per step.  (The activation side costs most of the staging
-// work and is staged once per column tile, so the wider tile stages it half
-// as often as 256 x 128 did.)
+// Tile 128 x 256 (or 224 columns), eight waves (two per SIMD): wave w covers
+// rows 32 (w & 3) .. and columns 128 (w >> 2) .., with one accumulator per
+// path (the two paths have different tensor scales), 128 accumulator
+// registers.  K advances 64 per step.  (The activation side costs most of the
+// staging work and is staged once per column tile, so the wider tile stages
+// it half as often as 256 x 128 did.)  BNE = 224: waves 4-7 compute three
+// 32-column accumulators per path instead of four and wave 7 stages no
+// weight columns (its 32 are past the tile), so a shape whose 256-wide tiles
+// fall short of a whole round over the CUs fills it instead (18944 x 3584 at
+// T = 2048: 224 tiles of 256 columns, 256 of 224).
 //
 // Staging (no DMA: operands are dequantized on the way).  A step's row of 64
 // values is split in two halves of 32 (one backbone scale block, two
 // residual ones); thread t stages half t & 1 of weight column t >> 1, and
-// threads below 256 also of tile row t >> 1 (waves 0-3, one on each SIMD),
+// threads 256 and up also of tile row (t >> 1) - 128 (waves 4-7, one on each SIMD),
 // so the two lanes of a row read adjacent bytes and one load instruction
 // covers 32 rows.  Per step a thread
 // loads its halves (raw buffer loads; rows and columns outside the tile read
@@ -97,6 +102,7 @@ SHARQ_DEV uint4 expand4(uint32_t c_lo, uint32_t c_hi, uint32_t meta16) {
 // dequantizes them to fp16 and writes 16-byte chunks to LDS.  Loads run two
 // steps ahead.  The two waves of a SIMD overlap one's staging with the
 // other's MFMAs (measured faster than interleaving them by schedule hints).
+template <int BNE>
 __global__ __launch_bounds__(512, 1) void linear_nv_tile(
     const uint8_t* __restrict__ bb_codes, const uint8_t* __restrict__ bb_meta, const uint8_t* __restrict__ bb_scale,
     const uint8_t* __restrict__ res_codes, const uint8_t* __restrict__ res_scale, const float* __restrict__ a_ts,
@@ -105,10 +111,11 @@ __global__ __launch_bounds__(512, 1) void linear_nv_tile(
   __shared__ NvStage st[2];
   const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tiles_m = (rows + kNM - 1) / kNM, tiles_n = (D + kNN - 1) / kNN;
+  static_assert(BNE == 256 || BNE == 224, "tile columns");
+  const int tiles_m = (rows + kNM - 1) / kNM, tiles_n = (D + BNE - 1) / BNE;
   const int nt = tiles_m * tiles_n;
   const int bi = xcd_tile(blockIdx.x, nt);                    // consecutive tiles on one XCD
-  const int m0 = (bi % tiles_m) * kNM, n0 = (bi / tiles_m) * kNN;
+  const int m0 = (bi % tiles_m) * kNM, n0 = (bi / tiles_m) * BNE;
   const int KS = K / kKS;
   const uint32_t kA = K >> 2, kM = K >> 4, kS32 = K >> 5, kS16 = K >> 4, kR = K >> 1;
 
@@ -122,9 +129,14 @@ __global__ __launch_bounds__(512, 1) void linear_nv_tile(
   const __amdgpu_buffer_rsrc_t r_rs = rsrc(res_scale, (int64_t)an * kS16);
   const __amdgpu_buffer_rsrc_t r_w = rsrc(payload, (int64_t)D * kR), r_ws = rsrc(wscale, (int64_t)D * kS32);
 
-  // ---- staging roles: half h of column scol and (waves 0-3) of row srow
+  // ---- staging roles: half h of column scol and (waves 4-7) of row srow
   const uint32_t h = tid & 1;
-  const bool a_role = w < 4;                           // uniform per wave
+  // activations: waves 4-7 (one on each SIMD), which at BNE = 224 also
+  // multiply the narrower half of the columns, so the waves that stage the
+  // most do the fewest MFMAs
+  const bool a_role = w >= 4;                          // uniform per wave
+  // weight columns past the tile's BNE (wave 7 at BNE = 224) are never read
+  const bool b_role = BNE == 256 || 64 * w < 2 * BNE;  // uniform per wave
   const int srow = (tid >> 1) & 127, scol = tid >> 1;
   const int gr = m0 + srow, gc = n0 + scol;
   const uint32_t ar = gr < rows ? (uint32_t)gather_row(row_index, gr, act_rows) : 0u;
@@ -149,9 +161,11 @@ __global__ __launch_bounds__(512, 1) void linear_nv_tile(
       L.rc = make_uint4(r[0], r[1], r[2], r[3]);
       L.rsc = __builtin_amdgcn_raw_buffer_load_b16(r_rs, ar * kS16 + 4u * ss + 2u * h, 0, 0);
     }
-    const auto b = __builtin_amdgcn_raw_buffer_load_b128(r_w, wc * kR + 32u * ss + 16u * h, 0, 0);
-    L.wcd = make_uint4(b[0], b[1], b[2], b[3]);
-    L.wsc = __builtin_amdgcn_raw_buffer_load_b8(r_ws, wc * kS32 + 2u * ss + h, 0, 0);
+    if (b_role) {
+      const auto b = __builtin_amdgcn_raw_buffer_load_b128(r_w, wc * kR + 32u * ss + 16u * h, 0, 0);
+      L.wcd = make_uint4(b[0], b[1], b[2], b[3]);
+      L.wsc = __builtin_amdgcn_raw_buffer_load_b8(r_ws, wc * kS32 + 2u * ss + h, 0, 0);
+    }
   };
   auto store = [&](const Ld& L, NvStage& S) {
     const int q0 = 4 * (int)h;                         // the half's first 16-byte chunk
@@ -168,79 +182,88 @@ __global__ __launch_bounds__(512, 1) void linear_nv_tile(
       S.a_dn[nslot(srow, q0 + 2)] = dequant8_f16(L.rc.z, d1);
       S.a_dn[nslot(srow, q0 + 3)] = dequant8_f16(L.rc.w, d1);
     }
-    const v2h db = dec_h2(L.wsc & 0xFFu);
-    S.b[nslot(scol, q0 + 0)] = dequant8_f16(L.wcd.x, db);
-    S.b[nslot(scol, q0 + 1)] = dequant8_f16(L.wcd.y, db);
-    S.b[nslot(scol, q0 + 2)] = dequant8_f16(L.wcd.z, db);
-    S.b[nslot(scol, q0 + 3)] = dequant8_f16(L.wcd.w, db);
+    if (b_role) {
+      const v2h db = dec_h2(L.wsc & 0xFFu);
+      S.b[nslot(scol, q0 + 0)] = dequant8_f16(L.wcd.x, db);
+      S.b[nslot(scol, q0 + 1)] = dequant8_f16(L.wcd.y, db);
+      S.b[nslot(scol, q0 + 2)] = dequant8_f16(L.wcd.z, db);
+      S.b[nslot(scol, q0 + 3)] = dequant8_f16(L.wcd.w, db);
+    }
   };
 
-  // ---- MFMA fragments and accumulators: rows wm0 + lr, columns wn0 + 32 n + lr
+  // ---- MFMA fragments and accumulators: rows wm0 + lr, columns wn0 + 32 n +
+  // lr for n < FN (FN = 4, or 3 for waves 4-7 of a 224-column tile); the two
+  // forms run the same loop, so every wave takes the same barriers
   const int wm0 = (w & 3) * 32, wn0 = (w >> 2) * 128;
   const int kh = l >> 5, lr = l & 31;
-  v16f acc_sp[4], acc_dn[4];
+  auto run = [&](auto fnc) {
+    constexpr int FN = decltype(fnc)::value;
+    v16f acc_sp[FN], acc_dn[FN];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    acc_sp[n] = (v16f){};
-    acc_dn[n] = (v16f){};
-  }
-  struct Frag {
-    uint4 sp, dn, b[4];   // one 16-wide K slice
-  };
-  auto read = [&](const NvStage& S, int ks, Frag& F) {
-    const int q = 2 * ks + kh;                         // chunk: K-values 8 q .. 8 q + 7
-    F.sp = S.a_sp[nslot(wm0 + lr, q)];
-    F.dn = S.a_dn[nslot(wm0 + lr, q)];
-#pragma unroll
-    for (int n = 0; n < 4; ++n) F.b[n] = S.b[nslot(wn0 + 32 * n + lr, q)];
-  };
-  auto mfma = [&](const Frag& F) {
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      acc_sp[n] = mfma_f16(F.sp, F.b[n], acc_sp[n]);
-      acc_dn[n] = mfma_f16(F.dn, F.b[n], acc_dn[n]);
+    for (int n = 0; n < FN; ++n) {
+      acc_sp[n] = (v16f){};
+      acc_dn[n] = (v16f){};
     }
-  };
-  auto step = [&](const NvStage& S, const Ld& Lnext, NvStage& N) {
-    Frag fr[2];
-    read(S, 0, fr[0]);
-    store(Lnext, N);
+    struct Frag {
+      uint4 sp, dn, b[FN];   // one 16-wide K slice
+    };
+    auto read = [&](const NvStage& S, int ks, Frag& F) {
+      const int q = 2 * ks + kh;                       // chunk: K-values 8 q .. 8 q + 7
+      F.sp = S.a_sp[nslot(wm0 + lr, q)];
+      F.dn = S.a_dn[nslot(wm0 + lr, q)];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks + 1 < 4) read(S, ks + 1, fr[(ks + 1) & 1]);
-      mfma(fr[ks & 1]);
-    }
-  };
+      for (int n = 0; n < FN; ++n) F.b[n] = S.b[nslot(wn0 + 32 * n + lr, q)];
+    };
+    auto mfma = [&](const Frag& F) {
+#pragma unroll
+      for (int n = 0; n < FN; ++n) {
+        acc_sp[n] = mfma_f16(F.sp, F.b[n], acc_sp[n]);
+        acc_dn[n] = mfma_f16(F.dn, F.b[n], acc_dn[n]);
+      }
+    };
+    auto step = [&](const NvStage& S, const Ld& Lnext, NvStage& N) {
+      Frag fr[2];
+      read(S, 0, fr[0]);
+      store(Lnext, N);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks + 1 < 4) read(S, ks + 1, fr[(ks + 1) & 1]);
+        mfma(fr[ks & 1]);
+      }
+    };
 
-  Ld l0, l1;
-  load(0, l0);
-  load(1, l1);
-  store(l0, st[0]);
-  __syncthreads();
-  // K % 128 == 0 (checked by the caller), so the number of steps is even
-  for (int s = 0; s < KS; s += 2) {
-    // step s: st[0] holds step s, st[1] receives step s+1
-    load(s + 2, l0);
-    step(st[0], l1, st[1]);
+    Ld l0, l1;
+    load(0, l0);
+    load(1, l1);
+    store(l0, st[0]);
     __syncthreads();
-    // step s+1
-    load(s + 3, l1);
-    step(st[1], l0, st[0]);
-    __syncthreads();
-  }
-
-  // ---- epilogue: Y = s_w * (s_sp * acc_sp + s_dn * acc_dn)
-  const float s_sp = a_ts[0], s_dn = a_ts[1], s_w = w_ts[0];
-#pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int c = n0 + wn0 + 32 * n + lr;
-    if (c >= D) continue;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = m0 + wm0 + 8 * (i >> 2) + 4 * kh + (i & 3);
-      if (r < rows) Y[(int64_t)r * ldy + c] = s_w * (s_sp * acc_sp[n][i] + s_dn * acc_dn[n][i]);
+    // K % 128 == 0 (checked by the caller), so the number of steps is even
+    for (int s = 0; s < KS; s += 2) {
+      // step s: st[0] holds step s, st[1] receives step s+1
+      load(s + 2, l0);
+      step(st[0], l1, st[1]);
+      __syncthreads();
+      // step s+1
+      load(s + 3, l1);
+      step(st[1], l0, st[0]);
+      __syncthreads();
     }
-  }
+
+    // ---- epilogue: Y = s_w * (s_sp * acc_sp + s_dn * acc_dn)
+    const float s_sp = a_ts[0], s_dn = a_ts[1], s_w = w_ts[0];
+#pragma unroll
+    for (int n = 0; n < FN; ++n) {
+      const int c = n0 + wn0 + 32 * n + lr;
+      if (c >= D) continue;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = m0 + wm0 + 8 * (i >> 2) + 4 * kh + (i & 3);
+        if (r < rows) Y[(int64_t)r * ldy + c] = s_w * (s_sp * acc_sp[n][i] + s_dn * acc_dn[n][i]);
+      }
+    }
+  };
+  if (BNE == 256 || w < 4) run(std::integral_constant<int, 4>{});
+  else run(std::integral_constant<int, (BNE - 128) / 32>{});
 }
 
 hipError_t launch_linear_nv(const uint8_t* bb_codes, const uint8_t* bb_meta, const uint8_t* bb_scale,
@@ -248,9 +271,21 @@ hipError_t launch_linear_nv(const uint8_t* bb_codes, const uint8_t* bb_meta, con
                             const int32_t* row_index, int rows, int act_rows, int K, const uint8_t* payload,
                             const uint8_t* wscale, const float* w_ts, int D, float* Y, int64_t ldy, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  const int nt = ((rows + kNM - 1) / kNM) * ((D + kNN - 1) / kNN);
-  hipLaunchKernelGGL(linear_nv_tile, dim3(nt), dim3(512), 0, s, bb_codes, bb_meta, bb_scale, res_codes, res_scale,
-                     a_ts, row_index, rows, act_rows, K, payload, wscale, w_ts, D, Y, ldy);
+  // tile width 256 or 224: the one with fewer rounds x width over the CUs
+  // (one workgroup per CU: 128 KB of LDS)
+  int ncu = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || ncu <= 0)
+    ncu = 256;
+  const int tiles_m = (rows + kNM - 1) / kNM;
+  const int t256 = tiles_m * ((D + 255) / 256), t224 = tiles_m * ((D + 223) / 224);
+  const bool narrow = (int64_t)((t224 + ncu - 1) / ncu) * 224 < (int64_t)((t256 + ncu - 1) / ncu) * 256;
+  if (narrow)
+    hipLaunchKernelGGL(linear_nv_tile<224>, dim3(t224), dim3(512), 0, s, bb_codes, bb_meta, bb_scale, res_codes,
+                       res_scale, a_ts, row_index, rows, act_rows, K, payload, wscale, w_ts, D, Y, ldy);
+  else
+    hipLaunchKernelGGL(linear_nv_tile<256>, dim3(t256), dim3(512), 0, s, bb_codes, bb_meta, bb_scale, res_codes,
+                       res_scale, a_ts, row_index, rows, act_rows, K, payload, wscale, w_ts, D, Y, ldy);
   return hipGetLastError();
 }
 

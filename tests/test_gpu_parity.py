@@ -294,6 +294,24 @@ def test_nvfp4_full_sampled(i):
     assert_gemm_close(Y.cpu().numpy()[r, c], Yr, S)
 
 
+@pytest.mark.parametrize("T,K,D", [(250, 512, 32700)])
+def test_nvfp4_tile_width_256_sampled(T, K, D):
+    # on 256 CUs: 256 tiles of 256 columns fill one round while 292 tiles of
+    # 224 would take two, so the 256-wide tile runs (ragged rows and columns);
+    # the small shapes above all take the 224-wide tile
+    case = synth.random_case(T + K + D + 7, T, K, D, fmt="nvfp4", spec=synth.QWEN_OUTLIERS)
+    act, w, Y = run_case(case)
+    ref = oracle_prepare(case)
+    compare_act(act, ref)
+    r, c = sample_pairs(case.T, case.D, 2000, seed=3)
+    cols = np.unique(c)
+    Wf = case.w_f32()
+    wsub = O.pack_weight(np.ascontiguousarray(Wf[:, cols]), "nvfp4", tensor_amax=np.abs(Wf).max())
+    compare_weight_cols(w, wsub, cols)
+    Yr, S = O.sharq_linear_sampled(ref, wsub, r, np.searchsorted(cols, c))
+    assert_gemm_close(Y.cpu().numpy()[r, c], Yr, S)
+
+
 def compare_weight_cols(w, ref, cols):
     torch.cuda.synchronize()
     idx = torch.from_numpy(cols).cuda()
